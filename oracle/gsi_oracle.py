@@ -1,0 +1,174 @@
+"""fp64 CPU oracle of the gated subspace linear map (test infrastructure).
+
+This module is the checker, not the product.  Only the test suite, the
+package smoke check and the CPU-baseline leg of the benchmark may import it;
+the HIP library never calls it and shares no code with it.
+
+Source: "Gated Subspace Inference for Transformer Acceleration" (S. J. Thomas,
+2026), technical summary as rendered by gist.science, cited below as GSI-TS.
+
+  * GSI-TS §2.1 (core decomposition): for a linear map W in R^{d_out x d}
+    and an orthonormal basis V_k in R^{d x k}, an activation splits exactly
+    into x = V_k V_k^T x + r, so y = W x = (W V_k)(V_k^T x) + W r = M g + W r
+    with the cached image M = W V_k and the coordinates g = V_k^T x.
+  * GSI-TS §2.2 (gated residual step): per token the residual ratio
+    rho = ||r|| / ||x|| is compared with a threshold eps; below it the
+    output is taken as M g (fast path), otherwise the full W x is computed
+    (slow path).  Theorem 4 there bounds the fast-path error of a token by
+    ||W||_2 * eps * ||x||.
+
+Everything is plain numpy float64 on inputs already upcast exactly from their
+storage dtype.  The residual r is formed explicitly.  No blocking, fusion or
+reordering beyond the definitions is done, so each function can be read
+against the pages.
+
+Readings where the pages are silent (each is listed in the design notes):
+  * tie rho == eps goes to the slow path (fast needs rho strictly below eps);
+  * ||x|| == 0 gives rho := 0, hence the fast path, whose output M g = 0
+    equals W x exactly;
+  * a NaN/Inf token makes rho NaN; "rho < eps" is then false, so the token
+    takes the slow path and W x carries the NaN as a dense layer would;
+  * the slow path returns W x (the §2.2 statement), not M g + W r (equal in
+    exact arithmetic, see the decomposition pin);
+  * eps <= 0 or eps > 1 is applied literally.
+
+Every function here is pinned by tests that check it against closed forms,
+special cases, identities, invariances or brute force (see tests/).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GATED, FORCE_FAST, FORCE_SLOW = 0, 1, 2
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def prepare(W, V) -> np.ndarray:
+    """Cached low-rank image M = W V_k (GSI-TS §2.1), shape [d_out][k]."""
+    return _f64(W) @ _f64(V)
+
+
+def project(V, x) -> np.ndarray:
+    """Subspace coordinates g = V_k^T x (GSI-TS §2.1), shape [k]."""
+    return _f64(V).T @ _f64(x)
+
+
+def residual(V, x, g) -> np.ndarray:
+    """Explicit residual r = x - V_k g (GSI-TS §2.1), shape [d]."""
+    return _f64(x) - _f64(V) @ _f64(g)
+
+
+def residual_ratio(x, r) -> float:
+    """rho = ||r|| / ||x|| (GSI-TS §2.2); 0 for x = 0, NaN for non-finite x."""
+    nx = float(np.linalg.norm(_f64(x)))
+    nr = float(np.linalg.norm(_f64(r)))
+    if not np.isfinite(nx) or not np.isfinite(nr):
+        return float("nan")
+    if nx == 0.0:
+        return 0.0
+    return nr / nx
+
+
+def takes_slow_path(rho: float, eps: float, mode: int = GATED) -> bool:
+    """Gate (GSI-TS §2.2): fast iff rho < eps, slow otherwise (ties slow)."""
+    if mode == FORCE_FAST:
+        return False
+    if mode == FORCE_SLOW:
+        return True
+    return not (rho < eps)
+
+
+def fast_output(M, g) -> np.ndarray:
+    """Fast path y = M g (GSI-TS §2.2)."""
+    return _f64(M) @ _f64(g)
+
+
+def slow_output(W, x) -> np.ndarray:
+    """Slow path y = W x (GSI-TS §2.2)."""
+    return _f64(W) @ _f64(x)
+
+
+def linear_token(W, V, M, x, eps: float, mode: int = GATED) -> dict:
+    """One token through the gated map: g, r, rho, slow flag and y."""
+    g = project(V, x)
+    r = residual(V, x, g)
+    rho = residual_ratio(x, r)
+    slow = takes_slow_path(rho, eps, mode)
+    y = slow_output(W, x) if slow else fast_output(M, g)
+    return {"g": g, "r": r, "rho": rho, "slow": slow, "y": y}
+
+
+def linear(W, V, M, X, eps: float, mode: int = GATED) -> dict:
+    """T tokens ([T][d]) through the gated map, one token at a time.
+
+    Returns stacked arrays: g [T][k], r [T][d], rho [T], slow [T] (bool),
+    y [T][d_out].
+    """
+    X = _f64(X)
+    outs = [linear_token(W, V, M, X[t], eps, mode) for t in range(X.shape[0])]
+    k = _f64(V).shape[1]
+    d_out = _f64(W).shape[0]
+    if not outs:
+        return {"g": np.zeros((0, k)), "r": np.zeros((0, X.shape[1])), "rho": np.zeros(0),
+                "slow": np.zeros(0, dtype=bool), "y": np.zeros((0, d_out))}
+    return {
+        "g": np.stack([o["g"] for o in outs]),
+        "r": np.stack([o["r"] for o in outs]),
+        "rho": np.array([o["rho"] for o in outs]),
+        "slow": np.array([o["slow"] for o in outs], dtype=bool),
+        "y": np.stack([o["y"] for o in outs]),
+    }
+
+
+def linear_rows(W_rows, V, x, eps: float, mode: int = GATED) -> dict:
+    """One token, outputs restricted to a subset of rows of W.
+
+    For maps too large to form M in full: the gate needs all of V_k and x,
+    while each sampled output row i uses only row i of W, i.e. row i of
+    M = W V_k.  Same definitions as linear_token, evaluated row by row.
+    """
+    g = project(V, x)
+    r = residual(V, x, g)
+    rho = residual_ratio(x, r)
+    slow = takes_slow_path(rho, eps, mode)
+    if slow:
+        y = slow_output(W_rows, x)
+    else:
+        y = fast_output(prepare(W_rows, V), g)
+    return {"g": g, "rho": rho, "slow": slow, "y": y}
+
+
+def stack(calls, mode: int = GATED) -> list:
+    """A sequence of independent gated calls (one per map of a decode step).
+
+    `calls` holds dicts with keys W, V, M, X, eps.  GSI-TS §3 applies the gate
+    to every linear map of the transformer; the calls here are independent,
+    so the sequence is evaluated one call after the other.
+    """
+    return [linear(c["W"], c["V"], c["M"], c["X"], c["eps"], mode) for c in calls]
+
+
+# ---- diagnostics (not compared against the GPU, used by pins) -------------
+
+def rho_from_norms(x, g) -> float:
+    """sqrt(max(0, 1 - ||g||^2/||x||^2)): equals rho when V_k is orthonormal."""
+    nx2 = float(np.dot(_f64(x), _f64(x)))
+    if nx2 == 0.0:
+        return 0.0
+    return float(np.sqrt(max(0.0, 1.0 - float(np.dot(_f64(g), _f64(g))) / nx2)))
+
+
+def spectral_norm(W) -> float:
+    """||W||_2 (largest singular value) via LAPACK SVD."""
+    return float(np.linalg.norm(_f64(W), 2))
+
+
+def theorem4_bound(W, x, rho: float) -> float:
+    """Fast-path error bound ||W||_2 * rho * ||x|| (GSI-TS §2.2, Theorem 4).
+
+    With rho < eps on the fast path this is below ||W||_2 * eps * ||x||.
+    """
+    return spectral_norm(W) * rho * float(np.linalg.norm(_f64(x)))

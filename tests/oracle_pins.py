@@ -1,0 +1,306 @@
+"""Pins of the fp64 oracle: checks against facts the oracle does not compute.
+
+Each pin takes an oracle module (the real one, or a copy with a planted
+mistake in tests/test_oracle_mutants.py) and raises AssertionError when the
+oracle disagrees with a closed form, a special case, an identity, an
+invariance or a brute-force computation.  References are to the technical
+summary of "Gated Subspace Inference for Transformer Acceleration"
+(S. J. Thomas, 2026), cited as GSI-TS.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from rank_gated_memory_amd import synth
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _orthonormal(rng, d, k):
+    q, r = np.linalg.qr(rng.standard_normal((d, k)))
+    return q * np.sign(np.diag(r))
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.allclose(a, b, rtol=rtol, atol=atol), f"{what}: max |diff| {np.max(np.abs(a - b))}"
+
+
+def pin_identity_basis(orc):
+    """V_k = first k columns of I: closed forms (GSI-TS §2.1, §2.2).
+
+    g = x[:k], r = (0, x[k:]), rho = ||x[k:]|| / ||x||, M = W[:, :k],
+    fast y = W[:, :k] x[:k], slow y = W x.
+    """
+    rng = _rng(11)
+    d, d_out, k = 12, 7, 4
+    W = rng.standard_normal((d_out, d))
+    V = np.eye(d)[:, :k]
+    X = rng.standard_normal((6, d))
+    X[:3, k:] *= 1e-3          # three tokens with a tiny residual -> fast
+    W_sq = rng.standard_normal((d, d))
+    _close(orc.prepare(W_sq, V), W_sq[:, :k], 1e-15, 0, "M of a square W")
+    M = orc.prepare(W, V)
+    _close(M, W[:, :k], 1e-15, 0, "M")
+    res = orc.linear(W, V, M, X, 0.05)
+    _close(res["g"], X[:, :k], 1e-15, 0, "g")
+    rho = np.array([np.sqrt(np.sum(x[k:] ** 2) / np.sum(x ** 2)) for x in X])
+    _close(res["rho"], rho, 1e-13, 0, "rho")
+    assert list(res["slow"]) == [False, False, False, True, True, True], res["slow"]
+    for t in range(6):
+        want = W @ X[t] if t >= 3 else W[:, :k] @ X[t, :k]
+        _close(res["y"][t], want, 1e-13, 1e-15, f"y[{t}]")
+
+
+def pin_full_rank(orc):
+    """k = d: every x lies in the subspace, rho = 0 and M g = W x."""
+    rng = _rng(12)
+    d, d_out = 10, 6
+    W = rng.standard_normal((d_out, d))
+    V = _orthonormal(rng, d, d)
+    X = rng.standard_normal((4, d))
+    M = orc.prepare(W, V)
+    res = orc.linear(W, V, M, X, 1e-6)
+    assert np.all(res["rho"] < 1e-14), res["rho"]
+    assert not res["slow"].any()
+    for t in range(4):
+        _close(res["y"][t], np.dot(W, X[t]), 1e-12, 1e-14, "y")
+
+
+def pin_in_span_and_orthogonal(orc):
+    """x in span(V_k) gives rho = 0 (fast); x orthogonal to V_k gives g = 0, rho = 1 (slow)."""
+    rng = _rng(13)
+    d, d_out, k = 20, 9, 5
+    Q = _orthonormal(rng, d, k + 3)
+    V, U = Q[:, :k], Q[:, k:]
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    x_in = V @ rng.standard_normal(k)
+    x_out = U @ rng.standard_normal(3)
+    r = orc.linear(W, V, M, np.stack([x_in, x_out]), 1e-6)
+    assert r["rho"][0] < 1e-14
+    assert not r["slow"][0]
+    _close(r["g"][1], np.zeros(k), 0, 1e-14, "g orthogonal")
+    _close(r["rho"][1], 1.0, 1e-14, 0, "rho orthogonal")
+    r2 = orc.linear(W, V, M, x_out[None], 0.99)
+    assert r2["slow"][0]
+    _close(r2["y"][0], np.dot(W, x_out), 1e-13, 1e-15, "slow y")
+
+
+def pin_construction(orc):
+    """Generator tokens with an orthogonal residual of known ratio (exact by construction)."""
+    d, k, m = 64, 8, 16
+    v, u = synth.orthonormal_frame(d, k, m, (99, 0, 0, synth.P_BASIS))
+    mask = torch.zeros(12, dtype=torch.bool)
+    mask[::2] = True
+    X, rho_built = synth.tokens(v, u, mask, (99, 0, 0))
+    V = v.numpy()
+    W = _rng(14).standard_normal((5, d))
+    res = orc.linear(W, V, orc.prepare(W, V), X.numpy(), 0.05)
+    sl = mask.numpy()
+    _close(res["rho"][sl], rho_built.numpy()[sl], 1e-12, 0, "constructed rho")
+    assert res["slow"][sl].all()
+    assert (res["rho"][~sl] < 0.0101).all() and not res["slow"][~sl].any()
+
+
+def pin_decomposition(orc):
+    """x = V_k g + r and M g + W r = W x (GSI-TS §2.1), in fp64."""
+    rng = _rng(15)
+    d, d_out, k = 48, 30, 7
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    X = rng.standard_normal((5, d))
+    res = orc.linear(W, V, M, X, 0.5)
+    for t in range(5):
+        _close(V @ res["g"][t] + res["r"][t], X[t], 1e-13, 1e-14, "x = Vg + r")
+        _close(M @ res["g"][t] + W @ res["r"][t], np.dot(W, X[t]), 1e-12, 1e-13, "Mg + Wr = Wx")
+        # r is orthogonal to the subspace (least-squares residual)
+        _close(V.T @ res["r"][t], np.zeros(k), 0, 1e-13, "V^T r")
+
+
+def pin_theorem4(orc):
+    """Fast-path error <= ||W||_2 rho ||x|| < ||W||_2 eps ||x|| (GSI-TS §2.2, Theorem 4)."""
+    rng = _rng(16)
+    d, d_out, k = 40, 25, 6
+    Q = _orthonormal(rng, d, k + 10)
+    V, U = Q[:, :k], Q[:, k:]
+    W = rng.standard_normal((d_out, d)) / np.sqrt(d)
+    M = orc.prepare(W, V)
+    # spectral norm from the eigenvalues of W^T W (independent of the oracle's SVD)
+    w2 = float(np.sqrt(np.max(np.linalg.eigvalsh(W.T @ W))))
+    eps = 0.2
+    xs = []
+    for rho in (0.0, 0.01, 0.05, 0.15, 0.19):
+        z = rng.standard_normal(k)
+        w = rng.standard_normal(10)
+        c = rho * np.linalg.norm(z) / (np.linalg.norm(w) * np.sqrt(1 - rho * rho))
+        xs.append(V @ z + c * (U @ w))
+    X = np.stack(xs)
+    res = orc.linear(W, V, M, X, eps, orc.FORCE_FAST)
+    gated = orc.linear(W, V, M, X, eps)
+    assert not gated["slow"].any()
+    for t in range(len(xs)):
+        err = np.linalg.norm(res["y"][t] - np.dot(W, X[t]))
+        nx = np.linalg.norm(X[t])
+        assert err <= w2 * res["rho"][t] * nx * (1 + 1e-10) + 1e-14, (t, err)
+        assert err <= w2 * eps * nx
+    # the bound is attained when the residual lies on W's top right-singular direction
+    _, s, vt = np.linalg.svd(W)
+    top = vt[0] - V @ (V.T @ vt[0])
+    top /= np.linalg.norm(top)
+    # choose W so that its top right-singular vector is orthogonal to V
+    W2 = np.outer(rng.standard_normal(d_out), top) * 3.0 + W @ (V @ V.T)
+    M2 = orc.prepare(W2, V)
+    x = V @ rng.standard_normal(k) + 0.1 * top
+    r = orc.linear(W2, V, M2, x[None], 0.5)
+    err = np.linalg.norm(r["y"][0] - np.dot(W2, x))
+    w22 = float(np.sqrt(np.max(np.linalg.eigvalsh(W2.T @ W2))))
+    bound = w22 * r["rho"][0] * np.linalg.norm(x)
+    assert err <= bound * (1 + 1e-10)
+    assert err >= 0.5 * bound, (err, bound)
+
+
+def pin_invariance(orc):
+    """V_k -> V_k Q leaves rho and y unchanged; x -> a x keeps rho and scales y."""
+    rng = _rng(17)
+    d, d_out, k = 30, 11, 6
+    V = _orthonormal(rng, d, k)
+    Qk = _orthonormal(rng, k, k)
+    W = rng.standard_normal((d_out, d))
+    X = rng.standard_normal((4, d))
+    X[:2] = (V @ rng.standard_normal((k, 2))).T + 1e-3 * rng.standard_normal((2, d))
+    a = orc.linear(W, V, orc.prepare(W, V), X, 0.05)
+    b = orc.linear(W, V @ Qk, orc.prepare(W, V @ Qk), X, 0.05)
+    _close(a["rho"], b["rho"], 1e-12, 1e-15, "rho under V Q")
+    _close(a["y"], b["y"], 1e-12, 1e-13, "y under V Q")
+    c = orc.linear(W, V, orc.prepare(W, V), -2.5 * X, 0.05)
+    _close(c["rho"], a["rho"], 1e-12, 1e-15, "rho under scaling")
+    _close(c["y"], -2.5 * a["y"], 1e-12, 1e-13, "y under scaling")
+    assert list(a["slow"]) == [False, False, True, True]
+
+
+def pin_least_squares(orc):
+    """Brute force: g and ||r|| from numpy's least-squares solve of V_k g ~ x."""
+    rng = _rng(18)
+    d, d_out, k = 25, 8, 5
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    X = rng.standard_normal((3, d))
+    res = orc.linear(W, V, orc.prepare(W, V), X, 0.05)
+    for t in range(3):
+        sol, rss, rank, _ = np.linalg.lstsq(V, X[t], rcond=None)
+        _close(res["g"][t], sol, 1e-12, 1e-14, "g vs lstsq")
+        _close(res["rho"][t], np.sqrt(rss[0]) / np.linalg.norm(X[t]), 1e-12, 0, "rho vs lstsq")
+
+
+def pin_gate_tie(orc):
+    """Fast needs rho strictly below eps; rho == eps goes slow (GSI-TS §2.2)."""
+    rng = _rng(19)
+    d, d_out, k = 16, 6, 4
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    x = V @ rng.standard_normal(k) + 0.05 * rng.standard_normal(d)
+    rho = orc.linear(W, V, M, x[None], 0.5)["rho"][0]
+    assert 0.0 < rho < 0.5
+    at = orc.linear(W, V, M, x[None], float(rho))
+    above = orc.linear(W, V, M, x[None], float(np.nextafter(rho, np.inf)))
+    below = orc.linear(W, V, M, x[None], float(np.nextafter(rho, -np.inf)))
+    assert at["slow"][0] and below["slow"][0] and not above["slow"][0]
+    _close(at["y"][0], np.dot(W, x), 1e-13, 1e-14, "tie -> W x")
+    _close(above["y"][0], M @ (V.T @ x), 1e-13, 1e-14, "above -> M g")
+
+
+def pin_zero_token(orc):
+    """x = 0: rho := 0, fast for eps > 0, y = 0; eps = 0 sends it slow, still y = 0."""
+    rng = _rng(20)
+    d, d_out, k = 10, 5, 3
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    r = orc.linear(W, V, M, np.zeros((1, d)), 0.05)
+    assert r["rho"][0] == 0.0 and not r["slow"][0]
+    assert np.all(r["y"][0] == 0.0)
+    r0 = orc.linear(W, V, M, np.zeros((1, d)), 0.0)
+    assert r0["slow"][0] and np.all(r0["y"][0] == 0.0)
+
+
+def pin_nonfinite(orc):
+    """NaN or Inf in x: rho is NaN, the token goes slow and y carries it."""
+    rng = _rng(21)
+    d, d_out, k = 10, 5, 3
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    X = rng.standard_normal((2, d))
+    X[0, 4] = np.nan
+    X[1, 2] = np.inf
+    r = orc.linear(W, V, M, X, 0.05)
+    assert np.isnan(r["rho"]).all()
+    assert r["slow"].all()
+    assert not np.isfinite(r["y"]).all(axis=1).any()
+
+
+def pin_modes(orc):
+    """Static projection (always fast) and dense (always slow) overrides."""
+    rng = _rng(22)
+    d, d_out, k = 14, 9, 5
+    W = rng.standard_normal((d_out, d))
+    V = np.eye(d)[:, :k]
+    M = orc.prepare(W, V)
+    X = rng.standard_normal((3, d))
+    f = orc.linear(W, V, M, X, 0.05, orc.FORCE_FAST)
+    s = orc.linear(W, V, M, X, 0.05, orc.FORCE_SLOW)
+    assert not f["slow"].any() and s["slow"].all()
+    for t in range(3):
+        _close(f["y"][t], W[:, :k] @ X[t, :k], 1e-13, 1e-15, "force fast")
+        _close(s["y"][t], np.dot(W, X[t]), 1e-13, 1e-15, "force slow")
+
+
+def pin_batching(orc):
+    """A batch equals its tokens one by one; row subsets equal full rows; stack equals calls."""
+    rng = _rng(23)
+    d, d_out, k = 18, 12, 4
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((d_out, d))
+    M = orc.prepare(W, V)
+    X = rng.standard_normal((5, d))
+    X[:3] = (V @ rng.standard_normal((k, 3))).T + 1e-3 * rng.standard_normal((3, d))
+    full = orc.linear(W, V, M, X, 0.05)
+    assert full["y"].shape == (5, d_out) and full["rho"].shape == (5,)
+    for t in range(5):
+        one = orc.linear(W, V, M, X[t:t + 1], 0.05)
+        _close(one["y"][0], full["y"][t], 0, 0, "token vs batch")
+        rows = [0, 3, 11]
+        sub = orc.linear_rows(W[rows], V, X[t], 0.05)
+        assert sub["slow"] == bool(full["slow"][t])
+        _close(sub["y"], full["y"][t, rows], 1e-13, 1e-15, "row subset")
+    calls = [dict(W=W, V=V, M=M, X=X[:2], eps=0.05), dict(W=W[:5], V=V, M=M[:5], X=X[2:], eps=0.5)]
+    st = orc.stack(calls)
+    _close(st[0]["y"], full["y"][:2], 0, 0, "stack call 0")
+    _close(st[1]["y"], orc.linear(W[:5], V, M[:5], X[2:], 0.5)["y"], 0, 0, "stack call 1")
+
+
+def pin_norm_identity(orc):
+    """For orthonormal V_k, rho also equals sqrt(1 - ||g||^2/||x||^2)."""
+    rng = _rng(24)
+    d, k = 64, 8
+    V = _orthonormal(rng, d, k)
+    W = rng.standard_normal((3, d))
+    X = (V @ rng.standard_normal((k, 4))).T + 0.2 * rng.standard_normal((4, d))
+    res = orc.linear(W, V, orc.prepare(W, V), X, 0.05)
+    for t in range(4):
+        _close(orc.rho_from_norms(X[t], res["g"][t]), res["rho"][t], 1e-10, 0, "pythagorean rho")
+
+
+ALL_PINS = [
+    pin_identity_basis, pin_full_rank, pin_in_span_and_orthogonal, pin_construction,
+    pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
+    pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity,
+]

@@ -1,0 +1,96 @@
+"""Plant plausible mistakes in a private copy of the oracle (on the CPU) and
+check that the pin suite catches every one of them.
+
+A mutant counts as caught when at least one pin raises (an assertion or any
+other error).  The real oracle module is never modified.
+"""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "gsi_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("gsi_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+f64 = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
+
+MUTANTS = {
+    # prepare: columns of V_k taken in the wrong order / transposed W
+    "prepare_column_order": ("prepare", lambda W, V: f64(W) @ f64(V)[:, ::-1]),
+    "prepare_transposed_W": ("prepare", lambda W, V: f64(W).T @ f64(V)),
+    # projection: dropped or reordered coordinates
+    "project_reversed": ("project", lambda V, x: f64(V)[:, ::-1].T @ f64(x)),
+    "project_drop_last": ("project", lambda V, x: np.concatenate([f64(V)[:, :-1].T @ f64(x), [0.0]])),
+    # residual: wrong sign, dropped basis term
+    "residual_sign": ("residual", lambda V, x, g: f64(x) + f64(V) @ f64(g)),
+    "residual_drop_term": ("residual", lambda V, x, g: f64(x) - f64(V)[:, :-1] @ f64(g)[:-1]),
+    # ratio: wrong denominator, squared, no zero guard
+    "ratio_over_g": ("residual_ratio", lambda x, r: float(np.linalg.norm(r) / max(np.linalg.norm(x[:1]), 1e-300))),
+    "ratio_squared": ("residual_ratio", lambda x, r: float(np.dot(r, r) / np.dot(x, x)) if np.dot(x, x) else 0.0),
+    "ratio_no_zero_guard": ("residual_ratio", lambda x, r: float(np.float64(np.linalg.norm(r)) / np.float64(np.linalg.norm(x)))),
+    # gate: tie goes fast, inverted, modes ignored
+    "gate_tie_fast": ("takes_slow_path", lambda rho, eps, mode=0: (mode == 2) or (mode != 1 and rho > eps)),
+    "gate_inverted": ("takes_slow_path", lambda rho, eps, mode=0: (mode == 2) or (mode != 1 and rho < eps)),
+    "gate_ignores_modes": ("takes_slow_path", lambda rho, eps, mode=0: not (rho < eps)),
+    # outputs: dropped terms, swapped path
+    "fast_drop_term": ("fast_output", lambda M, g: f64(M)[:, :-1] @ f64(g)[:-1]),
+    "slow_drop_term": ("slow_output", lambda W, x: f64(W)[:, :-1] @ f64(x)[:-1]),
+    "slow_uses_image": ("linear_token", None),
+    "batch_drops_token": ("linear", None),
+}
+
+
+def _mutant_linear_token(mod):
+    def linear_token(W, V, M, x, eps, mode=0):
+        g = mod.project(V, x)
+        r = mod.residual(V, x, g)
+        rho = mod.residual_ratio(x, r)
+        slow = mod.takes_slow_path(rho, eps, mode)
+        return {"g": g, "r": r, "rho": rho, "slow": slow, "y": mod.fast_output(M, g)}
+    return linear_token
+
+
+def _mutant_linear(mod, orig):
+    def linear(W, V, M, X, eps, mode=0):
+        out = orig(W, V, M, X, eps, mode)
+        if len(out["y"]) > 1:
+            out["y"] = out["y"].copy()
+            out["y"][-1] = out["y"][-2]
+        return out
+    return linear
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = fresh_oracle()
+    attr, fn = MUTANTS[name]
+    if name == "slow_uses_image":
+        fn = _mutant_linear_token(mod)
+    elif name == "batch_drops_token":
+        fn = _mutant_linear(mod, mod.linear)
+    setattr(mod, attr, fn)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in ALL_PINS:
+            try:
+                pin(mod)
+            except Exception as e:  # noqa: BLE001 - any failure counts as caught
+                caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutant {name} survived every pin"
+
+
+def test_unmutated_copy_passes():
+    mod = fresh_oracle()
+    for pin in ALL_PINS:
+        pin(mod)

@@ -1,0 +1,59 @@
+"""Properties of the seeded input generator (CPU only)."""
+import math
+
+import numpy as np
+import torch
+
+from rank_gated_memory_amd import synth
+
+
+def test_seeds_are_deterministic_and_distinct():
+    assert synth.seed_for(1, 2, 3, 4) == synth.seed_for(1, 2, 3, 4)
+    assert synth.seed_for(1, 2, 3, 4) != synth.seed_for(1, 2, 3, 5)
+    a = synth.gaussian_weight(8, 16, (1, 0, 0, 0), dtype=torch.float32)
+    b = synth.gaussian_weight(8, 16, (1, 0, 0, 0), dtype=torch.float32)
+    assert torch.equal(a, b)
+
+
+def test_frame_is_orthonormal():
+    v, u = synth.orthonormal_frame(256, 16, 64, (1, 0, 0, synth.P_BASIS))
+    q = torch.cat([v, u], 1)
+    assert torch.allclose(q.T @ q, torch.eye(80, dtype=torch.float64), atol=1e-12)
+
+
+def test_weight_scale():
+    w = synth.gaussian_weight(512, 1024, (7, 0, 0, 0), dtype=torch.float32).double()
+    assert abs(float(w.var()) * 1024 - 1.0) < 0.02
+
+
+def test_exact_slow_count():
+    m = synth.pick_slow(1000, 50, (2, 0, 0, synth.P_PICK))
+    assert int(m.sum()) == 50
+    m2 = synth.pick_slow(512, round(0.05 * 512), (3, 0, 0, synth.P_PICK))
+    assert int(m2.sum()) == 26
+
+
+def test_config1_shapes_and_dtypes():
+    c = synth.config1()
+    assert c.W.shape == (512, 256) and c.W.dtype == torch.float32
+    assert c.V.shape == (256, 16) and c.X.shape == (32, 256)
+    assert int(c.slow_mask.sum()) == 8
+    rb = c.rho_built[c.slow_mask]
+    assert bool(((rb >= 0.1) & (rb <= 0.5)).all())
+
+
+def test_cascade_coherence():
+    fr = synth.cascade_frames(1024, 64, 16, 4, (3, 0, 0, synth.P_CASCADE))
+    for (v1, _), (v2, u2) in zip(fr[:-1], fr[1:]):
+        c = synth.mean_principal_cosine(v1, v2)
+        assert 0.90 < c < 0.995, c
+        q = torch.cat([v2, u2], 1)
+        assert torch.allclose(q.T @ q, torch.eye(80, dtype=torch.float64), atol=1e-12)
+
+
+def test_cascade_coherence_at_full_width():
+    # GPT-J-shaped roles: d=4096, k=256 and d=16384, k=512 (two layers each)
+    for d, k in ((4096, 256),):
+        fr = synth.cascade_frames(d, k, 64, 2, (3, 0, 9, synth.P_CASCADE))
+        c = synth.mean_principal_cosine(fr[0][0], fr[1][0])
+        assert 0.90 < c < 0.99, c
