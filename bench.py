@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Batch-1 gated subspace linear maps on one MI355X: tokens/s and HBM roofline.
+
+Workload (default): a GPT-J-6B-shaped stack of 28 layers x 4 linear maps
+(QKV 4096->12288, out 4096->4096, fc_in 4096->16384 with k=256, fc_out
+16384->4096 with k=512), bf16 weights, per-layer bases that follow a depth
+cascade, eps=0.05 and exactly 5% slow tokens per map over 512 synthetic
+decode steps.  One step = one token through all 112 maps (one gsi_stack
+call = a projection launch and an output launch).  Inputs are synthetic and
+resident in HBM before timing starts.
+
+Prints one JSON line (rank 0, N=1):
+  value        decode steps (= tokens at batch 1) per second, wall clock
+  roofline     the output kernel (apply_kernel, the larger byte mover at 5%
+               slow): algorithmic bytes per launch / mean launch time from HIP
+               events on the launch stream, against 8 TB/s
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "GSI linear tokens/s at d=4096 batch-1 + achieved HBM GB/s vs peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=512)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--workload", default="gptj6b-28L", choices=["gptj6b-28L", "llama13b-40L"])
+    p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--dense-steps", type=int, default=16)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def build_workload(name, layers_override, dev):
+    import torch
+
+    from rank_gated_memory_amd import gsi, synth
+
+    cfg, layers, roles, steps, rate, cascade = synth.STACKS[name]
+    if layers_override:
+        layers = layers_override
+    t0 = time.perf_counter()
+    data = synth.stack_config(cfg, layers, roles, steps, rate, device=dev, cascade=cascade)
+    torch.cuda.synchronize()
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f}s")
+    t0 = time.perf_counter()
+    maps = [[gsi.Map(mi.W, mi.V) for mi in row] for row in data]
+    for row in maps:
+        for m in row:
+            gsi.gsi_prepare(m)
+    torch.cuda.synchronize()
+    log(f"images M prepared in {time.perf_counter() - t0:.2f}s")
+    outs = []
+    for row in data:
+        orow = []
+        for mi in row:
+            orow.append((torch.empty((steps, mi.d_out), dtype=torch.bfloat16, device=dev),
+                         torch.empty(steps, dtype=torch.float32, device=dev),
+                         torch.zeros(steps, dtype=torch.uint8, device=dev)))
+        outs.append(orow)
+    t0 = time.perf_counter()
+    plans = []
+    for s in range(steps):
+        calls = []
+        for row, mrow, orow in zip(data, maps, outs):
+            for mi, m, (Y, R, S) in zip(row, mrow, orow):
+                calls.append((m, mi.X[s], Y[s], 0.05, R[s:s + 1], S[s:s + 1]))
+        plans.append(gsi.Stack(calls, device=dev))
+    torch.cuda.synchronize()
+    log(f"{steps} stack plans of {len(plans[0]._keep)} calls built in {time.perf_counter() - t0:.2f}s")
+    return dict(cfg=cfg, layers=layers, roles=roles, steps=steps, rate=rate, data=data, maps=maps,
+                outs=outs, plans=plans)
+
+
+def step_bytes(wl, step_slow):
+    """Algorithmic bytes of one step split by phase, given its gate per map."""
+    from rank_gated_memory_amd import accounting as acc
+
+    proj = apply = 0
+    i = 0
+    for row in wl["data"]:
+        for mi in row:
+            slow = bool(step_slow[i])
+            proj += acc.project_bytes(mi.d, mi.k, 2)
+            apply += acc.apply_bytes(mi.d, mi.d_out, mi.k, 2, slow)
+            i += 1
+    return proj, apply
+
+
+def cpu_baseline(wl, seconds):
+    """The fp64 oracle on a bounded sample: two layers' maps, tokens in step order."""
+    import numpy as np
+    import torch
+
+    from oracle import gsi_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    layers = wl["layers"]
+    pick = [0, layers // 2] if layers > 1 else [0]
+    host = []
+    for l in pick:
+        for mi in wl["data"][l]:
+            W = mi.W.to("cpu", torch.float64).numpy()
+            V = mi.V.to("cpu", torch.float64).numpy()
+            host.append((W, V, orc.prepare(W, V), mi.X.to("cpu", torch.float64).numpy()))
+    # time whole steps of the sampled maps until the budget is spent
+    t0 = time.perf_counter()
+    done = 0
+    while done < wl["steps"]:
+        for W, V, M, X in host:
+            orc.linear_token(W, V, M, X[done], 0.05)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    maps_total = sum(len(r) for r in wl["data"])
+    per_step = el / done * (maps_total / len(host))
+    return {"value": 1.0 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} decode steps of {len(host)} of {maps_total} maps (layers {pick}), "
+                      f"fp64 numpy, {el:.1f}s; step time scaled by {maps_total}/{len(host)} maps"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("this build runs on one GPU only: --gpus must be 1 (the path would shard by output "
+              "rows or tokens across GPUs, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from rank_gated_memory_amd import accounting as acc
+    from rank_gated_memory_amd import gsi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    gsi.lib()
+    wl = build_workload(args.workload, args.layers, dev)
+    plans = wl["plans"]
+    S = wl["steps"]
+    ws = gsi.workspace(max(p.ws_bytes for p in plans), dev)
+    stream = torch.cuda.current_stream()
+
+    # copy bandwidth of torch's copy kernel (context for the roofline)
+    a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    log(f"torch copy: {copy_gbps:.0f} GB/s (read+write)")
+
+    # ---- timed region: K decode steps, gated ----
+    for i in range(args.warmup):
+        gsi.gsi_stack(plans[i % S], gsi.GATED, ws)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        gsi.gsi_stack(plans[i % S], gsi.GATED, ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tok_s = K / wall
+    log(f"gated: {K} steps in {wall * 1e3:.1f} ms -> {tok_s:.1f} tokens/s")
+
+    # gates of every (step, map): deterministic, written by every run
+    slow = torch.stack([S_ for row in wl["outs"] for (_, _, S_) in row], dim=1).cpu().numpy()
+    bytes_steps = [step_bytes(wl, slow[s]) for s in range(S)]
+    proj_b = np.array([b[0] for b in bytes_steps], dtype=np.float64)
+    apply_b = np.array([b[1] for b in bytes_steps], dtype=np.float64)
+    idx = np.arange(K) % S
+    total_bytes = float((proj_b[idx] + apply_b[idx]).sum())
+    step_gbps = total_bytes / wall / 1e9
+
+    # ---- per-kernel pass: HIP events around each phase on the launch stream ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        p = plans[i % S]
+        evs[i][0].record(stream)
+        gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_PROJECT, ws)
+        evs[i][1].record(stream)
+        gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_APPLY, ws)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_proj = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_apply = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    proj_gbps = float(proj_b[idx].sum() / t_proj.sum() / 1e9)
+    apply_gbps = float(apply_b[idx].sum() / t_apply.sum() / 1e9)
+    log(f"proj_kernel  mean {t_proj.mean() * 1e6:.1f} us, {proj_gbps:.0f} GB/s")
+    log(f"apply_kernel mean {t_apply.mean() * 1e6:.1f} us, {apply_gbps:.0f} GB/s")
+
+    # ---- dense baseline (same kernels, every token slow) and static projection ----
+    D = max(1, args.dense_steps)
+    for i in range(2):
+        gsi.gsi_stack(plans[i % S], gsi.FORCE_SLOW, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(D):
+        gsi.gsi_stack(plans[i % S], gsi.FORCE_SLOW, ws)
+    torch.cuda.synchronize()
+    dense_wall = time.perf_counter() - t0
+    dense_tok_s = D / dense_wall
+    dense_bytes = sum(acc.token_bytes(mi.d, mi.d_out, mi.k, 2, True) for row in wl["data"] for mi in row)
+    t0 = time.perf_counter()
+    for i in range(K):
+        gsi.gsi_stack(plans[i % S], gsi.FORCE_FAST, ws)
+    torch.cuda.synchronize()
+    fast_wall = time.perf_counter() - t0
+    fast_bytes = sum(acc.token_bytes(mi.d, mi.d_out, mi.k, 2, False) for row in wl["data"] for mi in row)
+    # restore the gated outputs of the last steps (the forced runs overwrote them)
+    for i in range(min(K, S)):
+        gsi.gsi_stack(plans[i], gsi.GATED, ws)
+    torch.cuda.synchronize()
+    log(f"dense (forced slow): {dense_tok_s:.1f} tokens/s, {D * dense_bytes / dense_wall / 1e9:.0f} GB/s; "
+        f"all-fast: {K / fast_wall:.1f} tokens/s, {K * fast_bytes / fast_wall / 1e9:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+
+    maps_per_step = sum(len(r) for r in wl["data"])
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {wl['layers']} layers x {len(wl['roles'])} maps "
+                        f"({maps_per_step} gated batch-1 calls per step), "
+                        f"{wl['rate'] * 100:.0f}% slow tokens per map, eps=0.05",
+            "layers": wl["layers"],
+            "maps": [[n, d, o, k] for n, d, o, k in wl["roles"]],
+            "distinct_steps": S,
+            "slow_share": float(slow.mean()),
+        },
+        "hbm_gbps": step_gbps,
+        "hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "bytes_per_step": total_bytes / K,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "apply_kernel",
+            "achieved": apply_gbps,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": apply_gbps / PEAK_HBM_GBPS,
+            "traffic": None,
+            "bytes_per_launch": float(apply_b[idx].mean()),
+            "mean_launch_us": float(t_apply.mean() * 1e6),
+        },
+        "kernels": {
+            "proj_kernel": {"gbps": proj_gbps, "mean_us": float(t_proj.mean() * 1e6),
+                            "bytes_per_launch": float(proj_b[idx].mean())},
+            "apply_kernel": {"gbps": apply_gbps, "mean_us": float(t_apply.mean() * 1e6),
+                             "bytes_per_launch": float(apply_b[idx].mean())},
+        },
+        "dense_tokens_per_s": dense_tok_s,
+        "speedup_vs_dense": tok_s / dense_tok_s,
+        "all_fast_tokens_per_s": K / fast_wall,
+        "copy_gbps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,363 @@
+// C ABI of libgsi: argument checks, workspace sizing, stack plans, launches.
+// The operations themselves are defined in include/gsi.h and follow the
+// technical summary of "Gated Subspace Inference for Transformer
+// Acceleration" (S. J. Thomas, 2026), §2.1-§2.2.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/gsi.h"
+#include "gsi_internal.h"
+
+namespace gsi {
+hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int d, int d_out,
+                          int k, hipStream_t s);
+hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s);
+}  // namespace gsi
+
+using namespace gsi;
+
+namespace {
+
+int esize_of(int32_t dtype) { return dtype == GSI_FP32 ? 4 : (dtype == GSI_BF16 ? 2 : 0); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gsi_status check_shape(int32_t d, int32_t d_out, int32_t k, int32_t dtype) {
+  const int es = esize_of(dtype);
+  if (es == 0) return GSI_E_DTYPE;
+  if (d <= 0 || d_out <= 0 || k <= 0) return GSI_E_SHAPE;
+  if (d % 8 || d_out % 8 || k % 8) return GSI_E_SHAPE;
+  if (k > d || k > kMaxK) return GSI_E_SHAPE;
+  if ((int64_t)d * es > kMaxRowBytes) return GSI_E_SHAPE;
+  return GSI_OK;
+}
+
+gsi_status check_map(const gsi_map *m) {
+  if (!m) return GSI_E_NULL;
+  const gsi_status s = check_shape(m->d, m->d_out, m->k, m->dtype);
+  if (s != GSI_OK) return s;
+  if (!m->W || !m->V || !m->M) return GSI_E_NULL;
+  if (!aligned(m->W, 16) || !aligned(m->V, 16) || !aligned(m->M, 16)) return GSI_E_ALIGN;
+  return GSI_OK;
+}
+
+// Device compute-unit count (cached per device); sizes the persistent grid.
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// Bytes of V_k one projection unit aims at, given the total projection
+// bytes of a launch: enough units to fill 256 CUs several times over, each
+// large enough to keep a workgroup streaming.
+int64_t proj_target_bytes(int64_t total_v_bytes) {
+  int64_t t = total_v_bytes / (256 * 4);
+  if (t < 16 * 1024) t = 16 * 1024;
+  if (t > 128 * 1024) t = 128 * 1024;
+  return t;
+}
+
+struct WsLayout {
+  uint64_t gate_off, float_off, total;
+};
+
+WsLayout ws_layout(int64_t n, int64_t floats) {
+  WsLayout w;
+  w.gate_off = align_up((uint64_t)n * 4, 256);
+  w.float_off = align_up(w.gate_off + (uint64_t)n * 16, 256);
+  w.total = align_up(w.float_off + (uint64_t)floats * 4, 256);
+  return w;
+}
+
+int apply_grid(int64_t units_b_max) {
+  int64_t g = (int64_t)cu_count() * 8;
+  if (units_b_max < g) g = units_b_max;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gsi_abi_version(void) { return GSI_ABI_VERSION; }
+
+const char *gsi_status_str(int32_t s) {
+  switch (s) {
+    case GSI_OK: return "GSI_OK";
+    case GSI_E_NULL: return "GSI_E_NULL";
+    case GSI_E_SHAPE: return "GSI_E_SHAPE";
+    case GSI_E_DTYPE: return "GSI_E_DTYPE";
+    case GSI_E_ALIGN: return "GSI_E_ALIGN";
+    case GSI_E_WORKSPACE: return "GSI_E_WORKSPACE";
+    case GSI_E_HIP: return "GSI_E_HIP";
+    case GSI_E_ARG: return "GSI_E_ARG";
+    default: return "GSI_E_UNKNOWN";
+  }
+}
+
+size_t gsi_image_bytes(int32_t d_out, int32_t k, int32_t dtype) {
+  const int es = esize_of(dtype);
+  if (es == 0 || d_out <= 0 || k <= 0) return 0;
+  const int64_t tiles = (d_out + kTileRows - 1) / kTileRows;
+  return (size_t)(tiles * kTileRows * (int64_t)k * es);
+}
+
+gsi_status gsi_prepare(const gsi_map *map, void *stream) {
+  const gsi_status s = check_map(map);
+  if (s != GSI_OK) return s;
+  const hipError_t e = launch_prepare(map->dtype, map->W, map->V, map->M, map->d, map->d_out,
+                                      map->k, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSI_OK : GSI_E_HIP;
+}
+
+static uint64_t linear_ws_bytes(const gsi_map *map, int64_t n) {
+  const int es = esize_of(map->dtype);
+  const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
+                                  proj_target_bytes((int64_t)map->d * map->k * es * n));
+  return ws_layout(n, n * (us.g_floats + us.part_floats)).total;
+}
+
+size_t gsi_linear_workspace(const gsi_map *map, int32_t T) {
+  if (check_map(map) != GSI_OK || T <= 0) return 0;
+  // launches of kMaxCalls tokens, then one with the remainder
+  uint64_t need = 0;
+  if (T >= kMaxCalls) need = linear_ws_bytes(map, kMaxCalls);
+  if (T % kMaxCalls) {
+    const uint64_t r = linear_ws_bytes(map, T % kMaxCalls);
+    if (r > need) need = r;
+  }
+  return (size_t)need;
+}
+
+gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, float eps,
+                      int32_t mode, float *rho, uint8_t *slow, void *ws, size_t ws_bytes,
+                      void *stream) {
+  gsi_status s = check_map(map);
+  if (s != GSI_OK) return s;
+  if (T < 0) return GSI_E_SHAPE;
+  if (mode < GSI_GATED || mode > GSI_FORCE_SLOW) return GSI_E_ARG;
+  if (T == 0) return GSI_OK;
+  if (!x || !y || !ws) return GSI_E_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || (rho && !aligned(rho, 4)))
+    return GSI_E_ALIGN;
+  const size_t need = gsi_linear_workspace(map, T);
+  if (ws_bytes < need) return GSI_E_WORKSPACE;
+
+  const int es = esize_of(map->dtype);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Tokens are processed in launches of at most kMaxCalls tokens; each
+  // launch reuses the same workspace (stream order separates them).
+  for (int32_t t0 = 0; t0 < T; t0 += kMaxCalls) {
+    const int32_t n = (T - t0) < kMaxCalls ? (T - t0) : kMaxCalls;
+    const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
+                                    proj_target_bytes((int64_t)map->d * map->k * es * n));
+    const WsLayout wl = ws_layout(n, n * (us.g_floats + us.part_floats));
+    KArgs a{};
+    a.table = nullptr;
+    a.unit_call = nullptr;
+    CallDesc &o = a.one;
+    o.W = map->W;
+    o.V = map->V;
+    o.M = map->M;
+    o.x = static_cast<const char *>(x) + (int64_t)t0 * map->d * es;
+    o.y = static_cast<char *>(y) + (int64_t)t0 * map->d_out * es;
+    o.rho = rho ? rho + t0 : nullptr;
+    o.slow = slow ? slow + t0 : nullptr;
+    o.d = map->d;
+    o.d_out = map->d_out;
+    o.k = map->k;
+    o.eps = eps;
+    o.a_begin = 0;
+    o.a_units = us.a_units;
+    o.a_rows = us.a_rows;
+    o.fast_units = us.fast_units;
+    o.slow_units = us.slow_units;
+    o.slow_rows = us.slow_rows;
+    o.g_off = 0;
+    o.part_off = (int64_t)n * us.g_floats;
+    o.gate_off = 0;
+    a.x_stride = (int64_t)map->d * es;
+    a.y_stride = (int64_t)map->d_out * es;
+    a.n = n;
+    a.units_a = n * us.a_units;
+    a.mode = mode;
+    a.max_k = map->k;
+    a.max_d = map->d;
+    a.counters = static_cast<uint32_t *>(ws);
+    a.gate = static_cast<char *>(ws) + wl.gate_off;
+    a.wsf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.float_off);
+    const int64_t ub = (int64_t)n * (us.fast_units > us.slow_units ? us.fast_units : us.slow_units);
+    const hipError_t e = launch_batch1(map->dtype, a, apply_grid(ub), 3, st);
+    if (e != hipSuccess) return GSI_E_HIP;
+  }
+  return GSI_OK;
+}
+
+// ---- stacks ----------------------------------------------------------------
+
+static gsi_status check_call(const gsi_call &c, int32_t dtype) {
+  gsi_status s = check_map(&c.map);
+  if (s != GSI_OK) return s;
+  if (c.map.dtype != dtype) return GSI_E_DTYPE;
+  if (!c.x || !c.y) return GSI_E_NULL;
+  if (!aligned(c.x, 16) || !aligned(c.y, 16) || (c.rho && !aligned(c.rho, 4))) return GSI_E_ALIGN;
+  return GSI_OK;
+}
+
+static gsi_status plan_sizes(const gsi_call *calls, int32_t n, int64_t *units_a,
+                             int64_t *target, size_t *bytes) {
+  if (n < 0 || n > kMaxCalls) return GSI_E_SHAPE;
+  if (n > 0 && !calls) return GSI_E_NULL;
+  const int32_t dtype = n > 0 ? calls[0].map.dtype : GSI_BF16;
+  int64_t vbytes = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const gsi_status s = check_call(calls[i], dtype);
+    if (s != GSI_OK) return s;
+    vbytes += (int64_t)calls[i].map.d * calls[i].map.k * esize_of(dtype);
+  }
+  const int64_t t = proj_target_bytes(vbytes);
+  int64_t ua = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const UnitShape us =
+        unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, esize_of(dtype), t);
+    ua += us.a_units;
+  }
+  *units_a = ua;
+  *target = t;
+  const uint64_t desc_off = align_up(sizeof(PlanHeader), 128);
+  const uint64_t unit_off = desc_off + (uint64_t)n * sizeof(CallDesc);
+  *bytes = (size_t)align_up(unit_off + (uint64_t)ua * 4, 256);
+  return GSI_OK;
+}
+
+size_t gsi_stack_plan_bytes(const gsi_call *calls, int32_t n) {
+  int64_t ua = 0, t = 0;
+  size_t bytes = 0;
+  if (plan_sizes(calls, n, &ua, &t, &bytes) != GSI_OK) return 0;
+  return bytes;
+}
+
+gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t plan_bytes) {
+  int64_t ua = 0, target = 0;
+  size_t bytes = 0;
+  const gsi_status s = plan_sizes(calls, n, &ua, &target, &bytes);
+  if (s != GSI_OK) return s;
+  if (!plan) return GSI_E_NULL;
+  if (!aligned(plan, 16)) return GSI_E_ALIGN;
+  if (plan_bytes < bytes) return GSI_E_WORKSPACE;
+  std::memset(plan, 0, bytes);
+  auto *h = static_cast<PlanHeader *>(plan);
+  h->magic = kPlanMagic;
+  h->version = kPlanVersion;
+  h->n = n;
+  h->dtype = n > 0 ? calls[0].map.dtype : GSI_BF16;
+  h->desc_off = align_up(sizeof(PlanHeader), 128);
+  h->unit_off = h->desc_off + (uint64_t)n * sizeof(CallDesc);
+  h->total_bytes = bytes;
+  auto *desc = reinterpret_cast<CallDesc *>(static_cast<char *>(plan) + h->desc_off);
+  auto *unit_call = reinterpret_cast<int32_t *>(static_cast<char *>(plan) + h->unit_off);
+  const int es = esize_of(h->dtype);
+  // float offsets: g of every call first, then the partials
+  int64_t g_total = 0;
+  for (int32_t i = 0; i < n; ++i) g_total += (calls[i].map.k + 3) / 4 * 4;
+  int64_t g_off = 0, part_off = g_total, a_begin = 0, units_b = 0;
+  int32_t max_k = 8, max_d = 8;
+  for (int32_t i = 0; i < n; ++i) {
+    const gsi_call &c = calls[i];
+    const UnitShape us = unit_shape(c.map.d, c.map.d_out, c.map.k, es, target);
+    CallDesc &o = desc[i];
+    o.W = c.map.W;
+    o.V = c.map.V;
+    o.M = c.map.M;
+    o.x = c.x;
+    o.y = c.y;
+    o.rho = c.rho;
+    o.slow = c.slow;
+    o.d = c.map.d;
+    o.d_out = c.map.d_out;
+    o.k = c.map.k;
+    o.eps = c.eps;
+    o.a_begin = (int32_t)a_begin;
+    o.a_units = us.a_units;
+    o.a_rows = us.a_rows;
+    o.fast_units = us.fast_units;
+    o.slow_units = us.slow_units;
+    o.slow_rows = us.slow_rows;
+    o.g_off = g_off;
+    o.part_off = part_off;
+    o.gate_off = i;
+    for (int32_t q = 0; q < us.a_units; ++q) unit_call[a_begin + q] = i;
+    a_begin += us.a_units;
+    g_off += us.g_floats;
+    part_off += us.part_floats;
+    units_b += us.fast_units > us.slow_units ? us.fast_units : us.slow_units;
+    if (c.map.k > max_k) max_k = c.map.k;
+    if (c.map.d > max_d) max_d = c.map.d;
+  }
+  h->units_a = (int32_t)a_begin;
+  h->units_b = (int32_t)units_b;
+  h->max_k = max_k;
+  h->max_d = max_d;
+  const WsLayout wl = ws_layout(n, part_off);
+  h->ws_bytes = n > 0 ? wl.total : 0;
+  h->ws_gate_off = wl.gate_off;
+  h->ws_float_off = wl.float_off;
+  return GSI_OK;
+}
+
+size_t gsi_stack_workspace(const void *plan_host) {
+  if (!plan_host) return 0;
+  const auto *h = static_cast<const PlanHeader *>(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion) return 0;
+  return (size_t)h->ws_bytes;
+}
+
+gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, void *ws,
+                     size_t ws_bytes, void *stream) {
+  return gsi_stack_phase(plan_host, plan_dev, mode, GSI_PHASE_PROJECT | GSI_PHASE_APPLY, ws,
+                         ws_bytes, stream);
+}
+
+gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t mode,
+                           int32_t phase, void *ws, size_t ws_bytes, void *stream) {
+  if (!plan_host) return GSI_E_NULL;
+  const auto *h = static_cast<const PlanHeader *>(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->n < 0 || h->n > kMaxCalls)
+    return GSI_E_ARG;
+  if (mode < GSI_GATED || mode > GSI_FORCE_SLOW) return GSI_E_ARG;
+  if (phase < 1 || phase > 3) return GSI_E_ARG;
+  if (h->n == 0) return GSI_OK;
+  if (!plan_dev || !ws) return GSI_E_NULL;
+  if (!aligned(plan_dev, 16) || !aligned(ws, 256)) return GSI_E_ALIGN;
+  if (ws_bytes < h->ws_bytes) return GSI_E_WORKSPACE;
+  KArgs a{};
+  a.table = reinterpret_cast<const CallDesc *>(static_cast<const char *>(plan_dev) + h->desc_off);
+  a.unit_call =
+      reinterpret_cast<const int32_t *>(static_cast<const char *>(plan_dev) + h->unit_off);
+  a.n = h->n;
+  a.units_a = h->units_a;
+  a.mode = mode;
+  a.max_k = h->max_k;
+  a.max_d = h->max_d;
+  a.counters = static_cast<uint32_t *>(ws);
+  a.gate = static_cast<char *>(ws) + h->ws_gate_off;
+  a.wsf = reinterpret_cast<float *>(static_cast<char *>(ws) + h->ws_float_off);
+  const hipError_t e = launch_batch1(h->dtype, a, apply_grid(h->units_b), phase,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSI_OK : GSI_E_HIP;
+}
+
+}  // extern "C"

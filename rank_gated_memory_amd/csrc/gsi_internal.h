@@ -1,0 +1,123 @@
+// Internal layout shared by the host library (gsi_api.cpp) and the kernels
+// (gsi_kernels.hip).  Nothing here is part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gsi {
+
+constexpr uint32_t kPlanMagic = 0x50495347u;  // "GSIP"
+constexpr uint32_t kPlanVersion = 1;
+constexpr int kBlock = 256;          // threads per workgroup of every kernel
+constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
+constexpr int kTileRows = 64;        // image rows per tile (one per lane)
+constexpr int kMaxK = 1024;
+constexpr int kMaxRowBytes = 32768;  // d * sizeof(element) limit (x staged in LDS)
+constexpr int kMaxCalls = 4096;      // calls per stack / tokens per launch
+constexpr int kProjRowsMax = 2048;   // rows of V_k per projection unit (x chunk in LDS)
+
+// Device descriptor of one batch-1 call (one token through one map).
+struct alignas(16) CallDesc {
+  const void *W;
+  const void *V;
+  const void *M;
+  const void *x;
+  void *y;
+  float *rho;
+  uint8_t *slow;
+  int32_t d, d_out, k;
+  float eps;
+  int32_t a_begin;     // first projection unit of this call
+  int32_t a_units;     // projection units (row chunks of V_k)
+  int32_t a_rows;      // rows of V_k per projection unit
+  int32_t fast_units;  // output units when the fast path is taken
+  int32_t slow_units;  // output units when the slow path is taken
+  int32_t slow_rows;   // rows of W per slow output unit
+  int64_t part_off;    // float offset in the workspace of the partials [a_units][k + 4]
+  int64_t g_off;       // float offset in the workspace of g [k]
+  int32_t gate_off;    // index of this call's gate record / counter
+  int32_t pad_[3];
+};
+static_assert(sizeof(CallDesc) == 128, "CallDesc layout");
+
+// Header of a stack plan (host buffer, copied verbatim to the device).
+struct alignas(16) PlanHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t n;           // calls
+  int32_t dtype;       // gsi_dtype of every call
+  int32_t units_a;     // projection units over all calls
+  int32_t units_b;     // sum over calls of max(fast_units, slow_units)
+  int32_t max_k;
+  int32_t max_d;
+  uint64_t ws_bytes;   // workspace bytes
+  uint64_t desc_off;   // byte offset of CallDesc[n]
+  uint64_t unit_off;   // byte offset of int32 unit_call[units_a]
+  uint64_t total_bytes;
+  uint64_t ws_gate_off;  // byte offsets of the workspace regions
+  uint64_t ws_float_off;
+};
+static_assert(sizeof(PlanHeader) == 80, "PlanHeader layout");
+
+// Workspace regions (byte offsets from the workspace base):
+//   [0, 4n)            uint32 counters, one per call (zero between calls)
+//   [gate_off, +16n)   float4 gate record per call: rho, slow flag bits, ||x||^2, ||g||^2
+//   [float_off, ...)   floats: g of every call, then projection partials
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// Arguments of the two batch-1 kernels.  Either `table` points at the
+// device copy of a plan's CallDesc array (stack), or it is null and the n
+// calls are the n tokens of one map described by `one` (single map, token
+// stride x_stride / y_stride elements).
+struct KArgs {
+  const CallDesc *table;
+  const int32_t *unit_call;
+  CallDesc one;
+  int64_t x_stride;
+  int64_t y_stride;
+  int32_t n;
+  int32_t units_a;
+  int32_t mode;
+  int32_t max_k;
+  int32_t max_d;
+  int32_t pad_;
+  uint32_t *counters;
+  void *gate;   // float4 records
+  float *wsf;
+};
+
+// Unit sizing shared by the stack plan and the single-map path.
+struct UnitShape {
+  int32_t a_units, a_rows, fast_units, slow_units, slow_rows;
+  int64_t part_floats;  // a_units * (k + 4)
+  int64_t g_floats;     // k rounded up to a multiple of 4
+};
+
+inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_proj_bytes) {
+  UnitShape s{};
+  const int64_t row_bytes = (int64_t)k * esize;
+  int64_t rows = target_proj_bytes / row_bytes;
+  rows = (rows + 15) / 16 * 16;
+  if (rows < 16) rows = 16;
+  if (rows > kProjRowsMax) rows = kProjRowsMax;
+  if (rows > d) rows = d;
+  s.a_rows = (int32_t)rows;
+  s.a_units = (int32_t)((d + rows - 1) / rows);
+  const int tiles = (d_out + kTileRows - 1) / kTileRows;
+  s.fast_units = (tiles + kWaves - 1) / kWaves;
+  int64_t srows = (256 * 1024) / ((int64_t)d * esize);
+  srows = srows / kWaves * kWaves;
+  if (srows < kWaves) srows = kWaves;
+  if (srows > 256) srows = 256;
+  s.slow_rows = (int32_t)srows;
+  s.slow_units = (int32_t)((d_out + srows - 1) / srows);
+  s.part_floats = (int64_t)s.a_units * (k + 4);
+  s.g_floats = (k + 3) / 4 * 4;
+  return s;
+}
+
+}  // namespace gsi

@@ -1,0 +1,494 @@
+// HIP kernels of the gated subspace linear map for gfx950 (CDNA4, wave64).
+//
+// Method: "Gated Subspace Inference for Transformer Acceleration"
+// (S. J. Thomas, 2026), technical summary (GSI-TS) §2.1-§2.2.
+//
+// Batch-1 path (one token per call, many calls per launch):
+//   proj_kernel  : one workgroup per row chunk of V_k.  x's chunk is staged
+//                  in LDS; lanes own 16-byte column slices of V_k rows, so a
+//                  wavefront reads whole rows contiguously and accumulates
+//                  partial g = V_k^T x (fp32) plus the partial ||x||^2.  The
+//                  last workgroup of a call (device-scope counter) sums the
+//                  partials in a fixed order, forms ||g||^2, rho and the gate
+//                  (GSI-TS §2.2) and publishes them.  Bitwise deterministic.
+//   apply_kernel : persistent loop over output units.  Every workgroup
+//                  derives the same prefix over calls of "units needed by the
+//                  path this call's gate chose", so only the chosen path's
+//                  bytes are ever read.  Fast units: one lane per output row,
+//                  reading the tiled image M in 16-byte vectors against g in
+//                  LDS (y = M g).  Slow units: one wavefront per row of W,
+//                  x staged in LDS, wave reduction (y = W x).
+// prepare_kernel: M = W V_k (fp32 FMA, LDS tiled), written in the tiled
+//                 layout described in gsi.h.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "gsi_internal.h"
+
+namespace gsi {
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ uint16_t float_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                             // nearest-even
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Vec;
+
+template <>
+struct Vec<float> {
+  static constexpr int VW = 4;
+  static constexpr int ESIZE = 4;
+  __device__ __forceinline__ static void unpack(const uint4 &u, float *f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  __device__ __forceinline__ static float load1(const void *p, size_t i) {
+    return static_cast<const float *>(p)[i];
+  }
+  __device__ __forceinline__ static void store1(void *p, size_t i, float v) {
+    static_cast<float *>(p)[i] = v;
+  }
+};
+
+template <>
+struct Vec<bf16_t> {
+  static constexpr int VW = 8;
+  static constexpr int ESIZE = 2;
+  __device__ __forceinline__ static void unpack(const uint4 &u, float *f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
+    f[4] = __uint_as_float(u.z << 16);
+    f[5] = __uint_as_float(u.z & 0xffff0000u);
+    f[6] = __uint_as_float(u.w << 16);
+    f[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+  __device__ __forceinline__ static float load1(const void *p, size_t i) {
+    return __uint_as_float((uint32_t) static_cast<const uint16_t *>(p)[i] << 16);
+  }
+  __device__ __forceinline__ static void store1(void *p, size_t i, float v) {
+    static_cast<uint16_t *>(p)[i] = float_to_bf16(v);
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // Butterfly: every lane ends with the same, order-fixed sum.
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread returns the same value.
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += sh[i];
+  return t;
+}
+
+// rho from ||x||^2 and ||g||^2 (exact for an orthonormal basis).
+// ||x|| = 0 gives 0; a non-finite norm gives NaN so that the gate sends the
+// token down the slow path.
+__device__ __forceinline__ float rho_from_norms(float xx, float gg) {
+  if (!(xx <= FLT_MAX) || !(gg <= FLT_MAX)) return __builtin_nanf("");
+  if (xx == 0.f) return 0.f;
+  const float t = 1.f - gg / xx;
+  return t > 0.f ? sqrtf(t) : 0.f;
+}
+
+__device__ __forceinline__ CallDesc load_call(const KArgs &a, int c) {
+  if (a.table) return a.table[c];
+  CallDesc d = a.one;
+  d.x = static_cast<const char *>(a.one.x) + (int64_t)c * a.x_stride;
+  d.y = static_cast<char *>(a.one.y) + (int64_t)c * a.y_stride;
+  if (d.rho) d.rho += c;
+  if (d.slow) d.slow += c;
+  d.a_begin = c * a.one.a_units;
+  d.part_off = a.one.part_off + (int64_t)c * ((int64_t)a.one.a_units * (a.one.k + 4));
+  d.g_off = a.one.g_off + (int64_t)c * ((a.one.k + 3) / 4 * 4);
+  d.gate_off = c;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// Projection: partial g and ||x||^2 per row chunk, gate by the last chunk.
+// ---------------------------------------------------------------------------
+template <typename T, int UNROLL>
+__global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
+  constexpr int VW = Vec<T>::VW;
+  __shared__ float xs[kProjRowsMax];
+  __shared__ float red[kBlock * VW];
+  __shared__ float sh[kWaves];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int c = a.table ? a.unit_call[u] : (u / a.one.a_units);
+  const CallDesc cd = load_call(a, c);
+  const int q = u - cd.a_begin;
+  const int row0 = q * cd.a_rows;
+  const int rows = min(cd.a_rows, cd.d - row0);
+  const int k = cd.k;
+
+  float xx = 0.f;
+  for (int i = tid; i < rows; i += kBlock) {
+    const float v = Vec<T>::load1(cd.x, (size_t)row0 + i);
+    xs[i] = v;
+    xx = fmaf(v, v, xx);
+  }
+  xx = block_sum(xx, sh);  // also publishes xs to the workgroup
+
+  const int tpr = k / VW;        // lanes per row of V_k
+  const int rpp = kBlock / tpr;  // rows per pass
+  const int slot = tid / tpr;
+  const int col = tid - slot * tpr;
+  if (slot < rpp) {
+    float acc[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+    const uint4 *vp =
+        reinterpret_cast<const uint4 *>(static_cast<const T *>(cd.V) + (size_t)row0 * k) + col;
+    for (int r = slot; r < rows; r += rpp * UNROLL) {
+      uint4 v[UNROLL];
+      float xv[UNROLL];
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) {
+        const int rr = r + j * rpp;
+        if (rr < rows) {
+          v[j] = vp[(size_t)rr * tpr];
+          xv[j] = xs[rr];
+        } else {
+          v[j] = make_uint4(0u, 0u, 0u, 0u);
+          xv[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) {
+        float f[VW];
+        Vec<T>::unpack(v[j], f);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) acc[e] = fmaf(f[e], xv[j], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VW; ++e) red[slot * k + col * VW + e] = acc[e];
+  }
+  __syncthreads();
+
+  const int stride = k + 4;
+  float *part = a.wsf + cd.part_off + (int64_t)q * stride;
+  for (int j = tid; j < k; j += kBlock) {
+    float s = 0.f;
+    for (int sl = 0; sl < rpp; ++sl) s += red[sl * k + j];
+    part[j] = s;
+  }
+  if (tid == 0) part[k] = xx;
+
+  // Release the partials; the last chunk of this call finishes the gate.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned)(cd.a_units - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  const float *p0 = a.wsf + cd.part_off;
+  float *g = a.wsf + cd.g_off;
+  float gg = 0.f;
+  for (int j = tid; j < k; j += kBlock) {
+    float s = 0.f;
+    int qq = 0;
+    for (; qq + 8 <= cd.a_units; qq += 8) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = p0[(int64_t)(qq + i) * stride + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += t[i];
+    }
+    for (; qq < cd.a_units; ++qq) s += p0[(int64_t)qq * stride + j];
+    g[j] = s;
+    gg = fmaf(s, s, gg);
+  }
+  float xp = 0.f;
+  for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += p0[(int64_t)qq * stride + k];
+  gg = block_sum(gg, sh);
+  const float xxt = block_sum(xp, sh);
+  if (tid == 0) {
+    const float rho = rho_from_norms(xxt, gg);
+    const int slow = a.mode == 2 ? 1 : (a.mode == 1 ? 0 : !(rho < cd.eps));
+    reinterpret_cast<float4 *>(a.gate)[cd.gate_off] =
+        make_float4(rho, __int_as_float(slow), xxt, gg);
+    if (cd.rho) *cd.rho = rho;
+    if (cd.slow) *cd.slow = (uint8_t)slow;
+    a.counters[cd.gate_off] = 0u;  // ready for the next call on this workspace
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Output: fast units (y = M g) and slow units (y = W x) of the chosen paths.
+// ---------------------------------------------------------------------------
+template <typename T, int UNROLL>
+__device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const float *gs) {
+  constexpr int VW = Vec<T>::VW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int tiles = (cd.d_out + kTileRows - 1) / kTileRows;
+  const int tile = local * kWaves + wave;
+  if (tile >= tiles) return;
+  const int kv = cd.k / VW;
+  const uint4 *mp = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * kTileRows * kv + lane;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int cg = 0; cg < kv; cg += UNROLL) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j)
+      v[j] = (cg + j < kv) ? mp[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      if (cg + j < kv) {
+        float f[VW];
+        Vec<T>::unpack(v[j], f);
+        const float *gp = gs + (cg + j) * VW;
+#pragma unroll
+        for (int e = 0; e < VW; e += 2) {
+          acc0 = fmaf(f[e], gp[e], acc0);
+          acc1 = fmaf(f[e + 1], gp[e + 1], acc1);
+        }
+      }
+    }
+  }
+  const int o = tile * kTileRows + lane;
+  if (o < cd.d_out) Vec<T>::store1(cd.y, o, acc0 + acc1);
+}
+
+template <typename T, int UNROLL>
+__device__ __forceinline__ void slow_unit(const CallDesc &cd, int local, const uint4 *xs) {
+  constexpr int VW = Vec<T>::VW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r0 = local * cd.slow_rows;
+  const int r1 = min(r0 + cd.slow_rows, cd.d_out);
+  const int nv = cd.d / VW;
+  for (int r = r0 + wave; r < r1; r += kWaves) {
+    const uint4 *wp =
+        reinterpret_cast<const uint4 *>(static_cast<const T *>(cd.W) + (size_t)r * cd.d);
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int v0 = lane; v0 < nv; v0 += 64 * UNROLL) {
+      uint4 w[UNROLL];
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) {
+        const int vv = v0 + j * 64;
+        w[j] = vv < nv ? wp[vv] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) {
+        const int vv = v0 + j * 64;
+        if (vv < nv) {
+          float f[VW], xf[VW];
+          Vec<T>::unpack(w[j], f);
+          Vec<T>::unpack(xs[vv], xf);
+#pragma unroll
+          for (int e = 0; e < VW; e += 2) {
+            acc0 = fmaf(f[e], xf[e], acc0);
+            acc1 = fmaf(f[e + 1], xf[e + 1], acc1);
+          }
+        }
+      }
+    }
+    const float s = wave_sum(acc0 + acc1);
+    if (lane == 0) Vec<T>::store1(cd.y, r, s);
+  }
+}
+
+__device__ __forceinline__ int call_units(const KArgs &a, int c) {
+  int fu, su, go;
+  if (a.table) {
+    fu = a.table[c].fast_units;
+    su = a.table[c].slow_units;
+    go = a.table[c].gate_off;
+  } else {
+    fu = a.one.fast_units;
+    su = a.one.slow_units;
+    go = c;
+  }
+  const float4 gi = reinterpret_cast<const float4 *>(a.gate)[go];
+  return __float_as_int(gi.y) ? su : fu;
+}
+
+template <typename T, int UNROLL>
+__global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int tmp[kBlock];
+  const int tid = threadIdx.x;
+  const int n = a.n;
+  const size_t pref_bytes = align_up((uint64_t)(n + 1) * 4, 16);
+  const size_t g_bytes = align_up((uint64_t)a.max_k * 4, 16);
+  int *pref = reinterpret_cast<int *>(smem);
+  float *gs = reinterpret_cast<float *>(smem + pref_bytes);
+  uint4 *xs = reinterpret_cast<uint4 *>(smem + pref_bytes + g_bytes);
+
+  // Prefix over calls of the units their chosen path needs.
+  if (tid == 0) pref[0] = 0;
+  int carry = 0;
+  for (int base = 0; base < n; base += kBlock) {
+    const int c = base + tid;
+    tmp[tid] = c < n ? call_units(a, c) : 0;
+    __syncthreads();
+    for (int off = 1; off < kBlock; off <<= 1) {
+      const int t = tid >= off ? tmp[tid - off] : 0;
+      __syncthreads();
+      tmp[tid] += t;
+      __syncthreads();
+    }
+    if (c < n) pref[c + 1] = carry + tmp[tid];
+    carry += tmp[kBlock - 1];
+    __syncthreads();
+  }
+  const int total = carry;
+
+  int cur = -1;
+  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= u)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int c = lo;
+    const int local = u - pref[c];
+    const CallDesc cd = load_call(a, c);
+    const float4 gi = reinterpret_cast<const float4 *>(a.gate)[cd.gate_off];
+    const bool slow = __float_as_int(gi.y) != 0;
+    if (c != cur) {
+      __syncthreads();
+      if (slow) {
+        const int nv = cd.d / Vec<T>::VW;
+        const uint4 *xp = static_cast<const uint4 *>(cd.x);
+        for (int i = tid; i < nv; i += kBlock) xs[i] = xp[i];
+      } else {
+        for (int j = tid; j < cd.k; j += kBlock) gs[j] = a.wsf[cd.g_off + j];
+      }
+      __syncthreads();
+      cur = c;
+    }
+    if (slow)
+      slow_unit<T, UNROLL>(cd, local, xs);
+    else
+      fast_unit<T, UNROLL>(cd, local, gs);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// M = W V_k into the tiled layout (one 64-row tile x up to 256 columns per
+// workgroup; fp32 FMA over d in chunks of 32 staged through LDS).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(kBlock)
+    prepare_kernel(const T *__restrict__ W, const T *__restrict__ V, T *__restrict__ M, int d,
+                   int d_out, int k) {
+  constexpr int VW = Vec<T>::VW;
+  constexpr int KC = 32;
+  __shared__ float Ws[kTileRows][KC + 1];
+  __shared__ float Vs[KC][256];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int cb = blockIdx.y * 256;
+  const int r = tid & 63;
+  const int cgi = tid >> 6;  // 64-column group of this thread
+  float acc[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) acc[j] = 0.f;
+
+  for (int k0 = 0; k0 < d; k0 += KC) {
+    for (int i = tid; i < kTileRows * KC; i += kBlock) {
+      const int rr = i / KC, cc = i % KC;
+      const int gr = tile * kTileRows + rr, gc = k0 + cc;
+      Ws[rr][cc] = (gr < d_out && gc < d) ? Vec<T>::load1(W, (size_t)gr * d + gc) : 0.f;
+    }
+    for (int i = tid; i < KC * 256; i += kBlock) {
+      const int rr = i / 256, cc = i % 256;
+      const int gr = k0 + rr, gc = cb + cc;
+      Vs[rr][cc] = (gr < d && gc < k) ? Vec<T>::load1(V, (size_t)gr * k + gc) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      const float w = Ws[r][kk];
+#pragma unroll
+      for (int j = 0; j < 64; ++j) acc[j] = fmaf(w, Vs[kk][cgi * 64 + j], acc[j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const int c = cb + cgi * 64 + j;
+    if (c < k) {
+      const size_t idx = (size_t)tile * kTileRows * k + (size_t)(c / VW) * kTileRows * VW +
+                         (size_t)r * VW + (c % VW);
+      Vec<T>::store1(M, idx, acc[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called from gsi_api.cpp).
+// ---------------------------------------------------------------------------
+hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int d, int d_out,
+                          int k, hipStream_t s) {
+  const dim3 grid((d_out + kTileRows - 1) / kTileRows, (k + 255) / 256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kBlock), 0, s,
+                       static_cast<const float *>(W), static_cast<const float *>(V),
+                       static_cast<float *>(M), d, d_out, k);
+  else
+    hipLaunchKernelGGL(prepare_kernel<bf16_t>, grid, dim3(kBlock), 0, s,
+                       static_cast<const bf16_t *>(W), static_cast<const bf16_t *>(V),
+                       static_cast<bf16_t *>(M), d, d_out, k);
+  return hipGetLastError();
+}
+
+size_t apply_lds_bytes(const KArgs &a, int esize) {
+  return align_up((uint64_t)(a.n + 1) * 4, 16) + align_up((uint64_t)a.max_k * 4, 16) +
+         align_up((uint64_t)a.max_d * esize, 16);
+}
+
+hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s) {
+  constexpr int U = 8;
+  const int esize = dtype == 0 ? 4 : 2;
+  const size_t lds = apply_lds_bytes(a, esize);
+  if (dtype == 0) {
+    if (phases & 1)
+      hipLaunchKernelGGL((proj_kernel<float, U>), dim3(a.units_a), dim3(kBlock), 0, s, a);
+    if (phases & 2)
+      hipLaunchKernelGGL((apply_kernel<float, U>), dim3(grid_b), dim3(kBlock), lds, s, a);
+  } else {
+    if (phases & 1)
+      hipLaunchKernelGGL((proj_kernel<bf16_t, U>), dim3(a.units_a), dim3(kBlock), 0, s, a);
+    if (phases & 2)
+      hipLaunchKernelGGL((apply_kernel<bf16_t, U>), dim3(grid_b), dim3(kBlock), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gsi

@@ -1,0 +1,224 @@
+"""Python binding of libgsi (include/gsi.h): argument marshalling only.
+
+Every operation runs in the HIP kernels of libgsi.so; this module only turns
+torch tensors into device pointers and status codes into exceptions.  If the
+library is not built the first call raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsi.so")
+
+GSI_FP32, GSI_BF16 = 0, 1
+GATED, FORCE_FAST, FORCE_SLOW = 0, 1, 2
+PHASE_PROJECT, PHASE_APPLY = 1, 2
+GSI_OK = 0
+
+_DTYPES = {torch.float32: GSI_FP32, torch.bfloat16: GSI_BF16}
+
+
+class GsiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class GsiMapStruct(ctypes.Structure):
+    _fields_ = [("d", c_int32), ("d_out", c_int32), ("k", c_int32), ("dtype", c_int32),
+                ("W", c_void_p), ("V", c_void_p), ("M", c_void_p)]
+
+
+class GsiCallStruct(ctypes.Structure):
+    _fields_ = [("map", GsiMapStruct), ("x", c_void_p), ("y", c_void_p), ("eps", c_float),
+                ("reserved", c_int32), ("rho", c_void_p), ("slow", c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgsi.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgsi.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gsi_abi_version.restype = c_int32
+        L.gsi_status_str.restype = ctypes.c_char_p
+        L.gsi_status_str.argtypes = [c_int32]
+        L.gsi_image_bytes.restype = c_size_t
+        L.gsi_image_bytes.argtypes = [c_int32, c_int32, c_int32]
+        L.gsi_prepare.restype = c_int32
+        L.gsi_prepare.argtypes = [POINTER(GsiMapStruct), c_void_p]
+        L.gsi_linear_workspace.restype = c_size_t
+        L.gsi_linear_workspace.argtypes = [POINTER(GsiMapStruct), c_int32]
+        L.gsi_linear.restype = c_int32
+        L.gsi_linear.argtypes = [POINTER(GsiMapStruct), c_void_p, c_void_p, c_int32, c_float,
+                                 c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.gsi_stack_plan_bytes.restype = c_size_t
+        L.gsi_stack_plan_bytes.argtypes = [POINTER(GsiCallStruct), c_int32]
+        L.gsi_stack_plan.restype = c_int32
+        L.gsi_stack_plan.argtypes = [POINTER(GsiCallStruct), c_int32, c_void_p, c_size_t]
+        L.gsi_stack_workspace.restype = c_size_t
+        L.gsi_stack_workspace.argtypes = [c_void_p]
+        L.gsi_stack.restype = c_int32
+        L.gsi_stack.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+        L.gsi_stack_phase.restype = c_int32
+        L.gsi_stack_phase.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
+                                      c_void_p]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().gsi_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != GSI_OK:
+        raise GsiError(status, where)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def gsi_abi_version() -> int:
+    return int(lib().gsi_abi_version())
+
+
+def gsi_image_bytes(d_out: int, k: int, dtype: int) -> int:
+    return int(lib().gsi_image_bytes(d_out, k, dtype))
+
+
+class Map:
+    """A linear map W [d_out][d] with basis V [d][k] and its cached image M."""
+
+    def __init__(self, W: torch.Tensor, V: torch.Tensor, M: torch.Tensor | None = None):
+        if W.dim() != 2 or V.dim() != 2 or W.shape[1] != V.shape[0]:
+            raise ValueError(f"shapes W {tuple(W.shape)} and V {tuple(V.shape)} do not chain")
+        if W.dtype != V.dtype:
+            raise TypeError("W and V must share a dtype")
+        if not (W.is_contiguous() and V.is_contiguous()):
+            raise ValueError("W and V must be contiguous")
+        self.W, self.V = W, V
+        self.d_out, self.d = W.shape
+        self.k = V.shape[1]
+        self.dtype = _dtype_code(W)
+        nbytes = gsi_image_bytes(self.d_out, self.k, self.dtype)
+        if M is None:
+            M = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=W.device)
+        self.M = M
+        self.struct = GsiMapStruct(self.d, self.d_out, self.k, self.dtype,
+                                   _ptr(W), _ptr(V), _ptr(M))
+
+    def image_rows(self) -> torch.Tensor:
+        """The image M as a [d_out][k] tensor (un-tiles the library layout)."""
+        el = self.W.dtype
+        vw = 16 // self.W.element_size()
+        tiles = (self.d_out + 63) // 64
+        m = self.M[: tiles * 64 * self.k * self.W.element_size()].view(el)
+        m = m.view(tiles, self.k // vw, 64, vw).permute(0, 2, 1, 3).reshape(tiles * 64, self.k)
+        return m[: self.d_out]
+
+
+def gsi_prepare(m: Map, stream=None) -> Map:
+    """Build M = W V_k into m.M."""
+    _check(lib().gsi_prepare(ctypes.byref(m.struct), _stream(stream)), "gsi_prepare")
+    return m
+
+
+def gsi_linear_workspace(m: Map, T: int) -> int:
+    return int(lib().gsi_linear_workspace(ctypes.byref(m.struct), int(T)))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace buffer (zero before first use, as gsi.h requires)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def gsi_linear(m: Map, x: torch.Tensor, eps: float, mode: int = GATED, y=None, rho=None,
+               slow=None, ws=None, stream=None):
+    """Gated map on x [T][d]; returns (y [T][d_out], rho [T], slow [T] uint8)."""
+    if x.dim() == 1:
+        x = x[None]
+    T = x.shape[0]
+    if x.dtype != m.W.dtype or not x.is_contiguous() or x.shape[1] != m.d:
+        raise ValueError("x must be a contiguous [T][d] tensor in the map's dtype")
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, m.d_out), dtype=x.dtype, device=dev)
+    if rho is None:
+        rho = torch.empty(T, dtype=torch.float32, device=dev)
+    if slow is None:
+        slow = torch.empty(T, dtype=torch.uint8, device=dev)
+    need = gsi_linear_workspace(m, T)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = lib().gsi_linear(ctypes.byref(m.struct), _ptr(x), _ptr(y), int(T), float(eps), int(mode),
+                          _ptr(rho), _ptr(slow), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(stream))
+    _check(st, "gsi_linear")
+    return y, rho, slow
+
+
+class Stack:
+    """A stack plan over independent batch-1 calls, with its device copy.
+
+    calls: list of (Map, x [d], y [d_out], eps, rho (1 float) or None,
+    slow (1 byte) or None).  Tensors must stay alive as long as the plan.
+    """
+
+    def __init__(self, calls, device=None):
+        self._keep = calls
+        n = len(calls)
+        arr = (GsiCallStruct * max(n, 1))()
+        for i, (m, x, y, eps, rho, slow) in enumerate(calls):
+            arr[i] = GsiCallStruct(m.struct, _ptr(x), _ptr(y), float(eps), 0, _ptr(rho), _ptr(slow))
+        self._arr = arr
+        nbytes = int(lib().gsi_stack_plan_bytes(arr, n))
+        if n > 0 and nbytes == 0:
+            # run the full check to get the failing status
+            _check(lib().gsi_stack_plan(arr, n, None, 0), "gsi_stack_plan")
+            raise GsiError(7, "gsi_stack_plan_bytes")
+        self.host = torch.zeros(max(nbytes, 256), dtype=torch.uint8)
+        _check(lib().gsi_stack_plan(arr, n, _ptr(self.host), self.host.numel()), "gsi_stack_plan")
+        self.n = n
+        self.ws_bytes = int(lib().gsi_stack_workspace(_ptr(self.host)))
+        dev = device if device is not None else (calls[0][1].device if n else "cpu")
+        self.dev = self.host.to(dev) if n else None
+
+    def run(self, mode: int = GATED, ws=None, stream=None):
+        if ws is None:
+            ws = workspace(self.ws_bytes, self.dev.device)
+        gsi_stack(self, mode, ws, stream)
+        return ws
+
+
+def gsi_stack(plan: Stack, mode: int, ws: torch.Tensor, stream=None):
+    st = lib().gsi_stack(_ptr(plan.host), _ptr(plan.dev), int(mode), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "gsi_stack")
+
+
+def gsi_stack_phase(plan: Stack, mode: int, phase: int, ws: torch.Tensor, stream=None):
+    st = lib().gsi_stack_phase(_ptr(plan.host), _ptr(plan.dev), int(mode), int(phase), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "gsi_stack_phase")

@@ -188,7 +188,7 @@ class MapInputs:
 
 def single_map(cfg: int, layer: int, idx: int, name: str, d: int, d_out: int, k: int,
                T: int, n_slow: int, dtype, device="cpu", w_device=None, extra_cols: int = 64,
-               frame=None) -> MapInputs:
+               frame=None, keep_fp64: bool = True) -> MapInputs:
     """One map with T tokens of which exactly n_slow are slow by construction."""
     w_device = device if w_device is None else w_device
     W = gaussian_weight(d_out, d, (cfg, layer, idx, P_WEIGHT), w_device, dtype)
@@ -197,8 +197,8 @@ def single_map(cfg: int, layer: int, idx: int, name: str, d: int, d_out: int, k:
     v64, u64 = frame
     mask = pick_slow(T, n_slow, (cfg, layer, idx, P_PICK), device)
     x64, rb = tokens(v64, u64, mask, (cfg, layer, idx))
-    return MapInputs(name, d, d_out, k, W, v64.to(dtype), x64.to(dtype), mask, rb,
-                     extra={"V64": v64, "U64": u64, "X64": x64})
+    extra = {"V64": v64, "U64": u64, "X64": x64} if keep_fp64 else {}
+    return MapInputs(name, d, d_out, k, W, v64.to(dtype), x64.to(dtype), mask, rb, extra=extra)
 
 
 def config1(device="cpu") -> MapInputs:
@@ -223,7 +223,7 @@ def config5(k: int, slow_frac: float, T: int = 256, d: int = 4096, d_out: int = 
 
 
 def stack_config(cfg: int, layers: int, maps, steps: int, slow_rate: float,
-                 device="cpu", cascade: bool = True, extra_cols: int = 64):
+                 device="cpu", cascade: bool = True, extra_cols: int = 64, keep_fp64: bool = False):
     """Layer stack: per map role a (cascaded or independent) basis per layer.
 
     Returns a list over layers of lists over roles of MapInputs whose X holds
@@ -240,9 +240,19 @@ def stack_config(cfg: int, layers: int, maps, steps: int, slow_rate: float,
         for ridx, (name, d, d_out, k) in enumerate(maps):
             fr = frames[ridx][layer] if cascade else None
             row.append(single_map(cfg, layer, ridx, name, d, d_out, k, steps, n_slow,
-                                  torch.bfloat16, device, device, extra_cols, frame=fr))
+                                  torch.bfloat16, device, device, extra_cols, frame=fr,
+                                  keep_fp64=keep_fp64))
+            if cascade and not keep_fp64:
+                frames[ridx][layer] = None
         out.append(row)
     return out
+
+
+STACKS = {
+    # name: (config id, layers, map roles, decode steps, slow-token rate, cascaded bases)
+    "gptj6b-28L": (3, 28, GPTJ_MAPS, 512, 0.05, True),
+    "llama13b-40L": (4, 40, LLAMA13_MAPS, 256, 0.02, False),
+}
 
 
 def mean_principal_cosine(v1: torch.Tensor, v2: torch.Tensor) -> float:

@@ -1,0 +1,177 @@
+"""C ABI of libgsi without a GPU: symbols, status codes, host-side checks, plans.
+
+Every call here returns before any kernel launch (argument errors or pure
+host work), so no device is touched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from rank_gated_memory_amd import gsi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsi.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gsi.LIB_PATH), reason="libgsi.so not built")
+
+GSI_OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_HIP, E_ARG = range(8)
+FAKE = 0x7f0000000000  # 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gsi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = gsi.lib()
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"libgsi.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    assert gsi.gsi_abi_version() == 1
+    m = re.search(r"#define GSI_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == gsi.gsi_abi_version()
+    assert gsi.status_str(0) == "GSI_OK"
+    assert gsi.status_str(5) == "GSI_E_WORKSPACE"
+    assert gsi.status_str(99) == "GSI_E_UNKNOWN"
+
+
+def test_image_bytes():
+    assert gsi.gsi_image_bytes(512, 16, 0) == 512 * 16 * 4
+    assert gsi.gsi_image_bytes(100, 8, 1) == 128 * 8 * 2      # padded to two 64-row tiles
+    assert gsi.gsi_image_bytes(12288, 256, 1) == 12288 * 256 * 2
+    assert gsi.gsi_image_bytes(0, 8, 1) == 0
+    assert gsi.gsi_image_bytes(64, 8, 7) == 0
+
+
+def mk_map(d=256, d_out=512, k=16, dtype=1, W=FAKE, V=FAKE + 0x100000, M=FAKE + 0x200000):
+    return gsi.GsiMapStruct(d, d_out, k, dtype, W, V, M)
+
+
+def prep(m):
+    return gsi.lib().gsi_prepare(ctypes.byref(m), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=12), E_SHAPE), (dict(d=250), E_SHAPE), (dict(d_out=0), E_SHAPE),
+    (dict(k=512, d=256), E_SHAPE), (dict(k=2048, d=4096), E_SHAPE),
+    (dict(d=32768, dtype=1), E_SHAPE), (dict(d=16384, dtype=0, k=16), E_SHAPE),
+    (dict(dtype=3), E_DTYPE), (dict(W=0), E_NULL), (dict(M=0), E_NULL),
+    (dict(V=FAKE + 8), E_ALIGN),
+])
+def test_prepare_rejects_before_launch(kw, status):
+    assert prep(mk_map(**kw)) == status
+
+
+def test_prepare_null_map():
+    assert gsi.lib().gsi_prepare(None, None) == E_NULL
+
+
+def linear(m, T=1, x=FAKE + 0x300000, y=FAKE + 0x400000, mode=0, ws=FAKE + 0x500000,
+           ws_bytes=1 << 30, rho=0, slow=0, eps=0.05):
+    return gsi.lib().gsi_linear(ctypes.byref(m), x, y, T, eps, mode, rho, slow, ws, ws_bytes, None)
+
+
+def test_linear_rejects_before_launch():
+    m = mk_map()
+    assert linear(m, T=0) == GSI_OK                    # empty batch: nothing to do
+    assert linear(m, T=-1) == E_SHAPE
+    assert linear(m, mode=3) == E_ARG
+    assert linear(m, x=0) == E_NULL
+    assert linear(m, ws=0) == E_NULL
+    assert linear(m, y=FAKE + 2) == E_ALIGN
+    assert linear(m, ws=FAKE + 16) == E_ALIGN
+    assert linear(m, rho=FAKE + 1) == E_ALIGN
+    need = gsi.lib().gsi_linear_workspace(ctypes.byref(m), 1)
+    assert need > 0
+    assert linear(m, ws_bytes=need - 1) == E_WS
+
+
+def test_linear_workspace_grows_with_tokens():
+    m = mk_map(d=4096, d_out=12288, k=256)
+    L = gsi.lib()
+    w1 = L.gsi_linear_workspace(ctypes.byref(m), 1)
+    w256 = L.gsi_linear_workspace(ctypes.byref(m), 256)
+    w5000 = L.gsi_linear_workspace(ctypes.byref(m), 5000)
+    assert 0 < w1 < w256 <= w5000
+    assert L.gsi_linear_workspace(ctypes.byref(m), 0) == 0
+
+
+def calls_array(specs):
+    arr = (gsi.GsiCallStruct * len(specs))()
+    base = FAKE
+    for i, (d, d_out, k, dt) in enumerate(specs):
+        mp = gsi.GsiMapStruct(d, d_out, k, dt, base, base + 0x1000000, base + 0x2000000)
+        arr[i] = gsi.GsiCallStruct(mp, base + 0x3000000, base + 0x4000000, 0.05, 0, 0, 0)
+        base += 0x10000000
+    return arr
+
+
+PLAN_HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("n", "<i4"), ("dtype", "<i4"),
+                     ("units_a", "<i4"), ("units_b", "<i4"), ("max_k", "<i4"), ("max_d", "<i4"),
+                     ("ws_bytes", "<u8"), ("desc_off", "<u8"), ("unit_off", "<u8"),
+                     ("total_bytes", "<u8"), ("ws_gate_off", "<u8"), ("ws_float_off", "<u8")])
+
+
+def build_plan(specs):
+    L = gsi.lib()
+    arr = calls_array(specs)
+    nb = L.gsi_stack_plan_bytes(arr, len(specs))
+    buf = np.zeros(nb + 64, dtype=np.uint8)
+    off = (-buf.ctypes.data) % 16
+    view = buf[off:off + nb]
+    st = L.gsi_stack_plan(arr, len(specs), view.ctypes.data, nb)
+    return st, view, nb
+
+
+def test_stack_plan_layout():
+    specs = [(4096, 12288, 256, 1), (4096, 4096, 256, 1), (4096, 16384, 256, 1),
+             (16384, 4096, 512, 1)] * 3
+    st, plan, nb = build_plan(specs)
+    assert st == GSI_OK
+    h = np.frombuffer(plan[:PLAN_HDR.itemsize].tobytes(), dtype=PLAN_HDR)[0]
+    assert h["magic"] == 0x50495347 and h["n"] == 12 and h["dtype"] == 1
+    assert h["total_bytes"] == nb and h["max_k"] == 512 and h["max_d"] == 16384
+    uo, ua = int(h["unit_off"]), int(h["units_a"])
+    unit_call = np.frombuffer(plan[uo:uo + 4 * ua].tobytes(), "<i4")
+    assert len(unit_call) == h["units_a"]
+    assert np.all(np.diff(unit_call) >= 0) and unit_call[0] == 0 and unit_call[-1] == 11
+    assert gsi.lib().gsi_stack_workspace(plan.ctypes.data) == h["ws_bytes"] > 0
+
+
+def test_stack_plan_rejects():
+    L = gsi.lib()
+    st, _, _ = build_plan([(4096, 4096, 256, 1), (4096, 4096, 256, 0)])
+    assert st == E_DTYPE
+    st, _, _ = build_plan([(4096, 4096, 12, 1)])
+    assert st == E_SHAPE
+    arr = calls_array([(256, 512, 16, 0)])
+    assert L.gsi_stack_plan(arr, 1, None, 0) == E_NULL
+    assert L.gsi_stack_plan_bytes(arr, 5000) == 0
+    assert L.gsi_stack_plan(arr, -1, None, 0) == E_SHAPE
+
+
+def test_stack_rejects_before_launch():
+    L = gsi.lib()
+    st, plan, nb = build_plan([(256, 512, 16, 0)])
+    assert st == GSI_OK
+    ws_need = L.gsi_stack_workspace(plan.ctypes.data)
+    p = plan.ctypes.data
+    assert L.gsi_stack(None, FAKE, 0, FAKE, ws_need, None) == E_NULL
+    assert L.gsi_stack(p, FAKE, 4, FAKE, ws_need, None) == E_ARG
+    assert L.gsi_stack(p, 0, 0, FAKE, ws_need, None) == E_NULL
+    assert L.gsi_stack(p, FAKE, 0, FAKE, ws_need - 1, None) == E_WS
+    bad = plan.copy()
+    bad[0] ^= 0xFF
+    assert L.gsi_stack(bad.ctypes.data, FAKE, 0, FAKE, ws_need, None) == E_ARG
+    st0, plan0, _ = build_plan([])
+    assert st0 == GSI_OK
+    assert L.gsi_stack(plan0.ctypes.data, 0, 0, 0, 0, None) == GSI_OK

@@ -1,0 +1,291 @@
+"""GPU parity of the HIP path against the fp64 oracle (calls go through the C ABI).
+
+Workloads follow the GSI technical summary's experiments, made synthetic:
+a small fp32 map (d=256 -> 512, k=16, 32 tokens, 8 with a large residual),
+the four GPT-J-6B-shaped maps in bf16 (1000 batch-1 tokens each, 50 slow),
+ragged stacks, and the edge cases of the gate.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gsi_oracle as orc
+from rank_gated_memory_amd import gsi, synth
+from tests.parity import compare_tokens, eps32, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def new_map(W, V):
+    m = gsi.Map(W.to(DEV).contiguous(), V.to(DEV).contiguous())
+    gsi.gsi_prepare(m)
+    return m
+
+
+# ---------------------------------------------------------------- prepare ----
+
+@pytest.mark.parametrize("d,d_out,k,dtype", [
+    (256, 512, 16, torch.float32), (264, 200, 24, torch.float32), (4096, 4096, 256, torch.bfloat16),
+    (512, 72, 8, torch.bfloat16), (1024, 1000, 320, torch.bfloat16), (2048, 640, 640, torch.bfloat16),
+])
+def test_prepare_image(d, d_out, k, dtype):
+    W = synth.gaussian_weight(d_out, d, (90, d, d_out, k), dtype=dtype)
+    v, _ = synth.orthonormal_frame(d, k, 0, (90, d, k, 1))
+    V = v.to(dtype)
+    m = new_map(W, V)
+    sync()
+    got = f64(m.image_rows())
+    want = orc.prepare(f64(W), f64(V))
+    rel = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    tol = 1e-6 if dtype == torch.float32 else 4e-3
+    assert rel.max() <= tol, rel.max()
+    # padding rows of the last tile are zero
+    tiles = (d_out + 63) // 64
+    full = m.M[: tiles * 64 * k * W.element_size()].view(dtype)
+    full = full.view(tiles, k * W.element_size() // 16, 64, 16 // W.element_size())
+    full = full.permute(0, 2, 1, 3).reshape(tiles * 64, k)
+    assert torch.all(full[d_out:] == 0)
+
+
+# --------------------------------------------------------------- config 1 ----
+
+def test_config1_single_tokens_and_batch():
+    c = synth.config1()
+    m = new_map(c.W, c.V)
+    X = c.X.to(DEV)
+    W, V, X64 = f64(c.W), f64(c.V), f64(c.X)
+    # batched: all 32 tokens in one call
+    y, rho, slow = gsi.gsi_linear(m, X, 0.05)
+    sync()
+    assert int(slow.sum()) == 8
+    compare_tokens(W, V, X64, 0.05, f64(y), slow.cpu().numpy(), f64(rho), torch.float32,
+                   rho_tol=1e-4, what="config1 batch")
+    # one token per call
+    ys, rhos, slows = [], [], []
+    for t in range(X.shape[0]):
+        y1, r1, s1 = gsi.gsi_linear(m, X[t:t + 1], 0.05)
+        ys.append(y1)
+        rhos.append(r1)
+        slows.append(s1)
+    sync()
+    y1 = torch.cat(ys)
+    compare_tokens(W, V, X64, 0.05, f64(y1), torch.cat(slows).cpu().numpy(), f64(torch.cat(rhos)),
+                   torch.float32, rho_tol=1e-4, what="config1 T=1")
+    # batching invariance
+    assert torch.equal(torch.cat(slows), slow)
+    assert torch.allclose(y1, y, rtol=1e-5, atol=1e-6)
+
+
+# --------------------------------------------------------------- config 2 ----
+
+GPTJ = {name: (d, d_out, k) for name, d, d_out, k in synth.GPTJ_MAPS}
+
+
+@pytest.fixture(scope="module")
+def config2_maps():
+    return synth.config2(T=1000, device=DEV, w_device=DEV)
+
+
+@pytest.mark.parametrize("idx", range(4), ids=[n for n, *_ in synth.GPTJ_MAPS])
+def test_config2_map(config2_maps, idx):
+    mi = config2_maps[idx]
+    m = new_map(mi.W, mi.V)
+    y, rho, slow = gsi.gsi_linear(m, mi.X, 0.05)
+    sync()
+    assert int(slow.sum()) == 50, int(slow.sum())
+    assert torch.equal(slow.bool().cpu(), mi.slow_mask.cpu())
+    W, V, X = f64(mi.W), f64(mi.V), f64(mi.X)
+    M = orc.prepare(W, V)
+    worst, band = compare_tokens(W, V, X, 0.05, f64(y), slow.cpu().numpy(), f64(rho),
+                                 torch.bfloat16, M=M, rho_tol=2e-2, what=f"config2 {mi.name}")
+    # 20 tokens one call each (batch-1 decode), incl. slow ones
+    pick = torch.cat([torch.nonzero(mi.slow_mask).flatten()[:5],
+                      torch.nonzero(~mi.slow_mask).flatten()[:15]]).cpu()
+    ys, ss, rs = [], [], []
+    for t in pick.tolist():
+        a, b, c = gsi.gsi_linear(m, mi.X[t:t + 1], 0.05)
+        ys.append(a)
+        rs.append(b)
+        ss.append(c)
+    sync()
+    compare_tokens(W, V, X[pick.numpy()], 0.05, f64(torch.cat(ys)), torch.cat(ss).cpu().numpy(),
+                   f64(torch.cat(rs)), torch.bfloat16, M=M, rho_tol=2e-2, what=f"config2 {mi.name} T=1")
+    print(f"{mi.name}: worst rel L2 {worst:.2e}, band tokens {band}")
+
+
+def test_config2_stack(config2_maps):
+    """The four maps x 8 tokens as one 32-call stack equals the oracle per call."""
+    maps = [new_map(mi.W, mi.V) for mi in config2_maps]
+    calls, outs = [], []
+    for t in range(8):
+        for mi, m in zip(config2_maps, maps):
+            y = torch.empty(mi.d_out, dtype=torch.bfloat16, device=DEV)
+            r = torch.empty(1, dtype=torch.float32, device=DEV)
+            s = torch.empty(1, dtype=torch.uint8, device=DEV)
+            calls.append((m, mi.X[t], y, 0.05, r, s))
+            outs.append((mi, t, y, r, s))
+    st = gsi.Stack(calls)
+    ws = st.run()
+    sync()
+    for mi in config2_maps:
+        W, V = f64(mi.W), f64(mi.V)
+        M = orc.prepare(W, V)
+        sel = [(t, y, r, s) for (mm, t, y, r, s) in outs if mm is mi]
+        X = f64(mi.X[[t for t, *_ in sel]])
+        compare_tokens(W, V, X, 0.05, np.stack([f64(y) for _, y, _, _ in sel]),
+                       np.array([int(s.item()) for *_, s in sel]),
+                       np.array([float(r.item()) for _, _, r, _ in sel]), torch.bfloat16, M=M,
+                       rho_tol=2e-2, what=f"stack {mi.name}")
+    # the workspace counters are back at zero: a second run gives identical bits
+    y0 = [o[2].clone() for o in outs]
+    st.run(ws=ws)
+    sync()
+    for (mi, t, y, r, s), yy in zip(outs, y0):
+        assert torch.equal(y, yy)
+
+
+# ------------------------------------------------------- ragged stacks -------
+
+def ragged_stack_inputs(dtype, seed):
+    shapes = [(264, 200, 24), (512, 72, 8), (1024, 1000, 64), (256, 8, 256), (2048, 1096, 128),
+              (776, 520, 40)]
+    items = []
+    for i, (d, d_out, k) in enumerate(shapes):
+        W = synth.gaussian_weight(d_out, d, (91, seed, i, 0), dtype=dtype)
+        v, u = synth.orthonormal_frame(d, k, min(16, d - k) if d > k else 0, (91, seed, i, 1))
+        if u.shape[1] == 0:
+            u = torch.zeros((d, 1), dtype=torch.float64)
+        mask = torch.tensor([i % 2 == 1 and d > k])
+        X, _ = synth.tokens(v, u, mask, (91, seed, i))
+        items.append((W, v.to(dtype), X.to(dtype)))
+    return items
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_ragged_stack(dtype):
+    items = ragged_stack_inputs(dtype, 1)
+    calls, keep = [], []
+    for W, V, X in items:
+        m = new_map(W, V)
+        y = torch.empty(W.shape[0], dtype=dtype, device=DEV)
+        r = torch.empty(1, dtype=torch.float32, device=DEV)
+        s = torch.empty(1, dtype=torch.uint8, device=DEV)
+        xd = X[0].to(DEV)
+        calls.append((m, xd, y, 0.05, r, s))
+        keep.append((W, V, X, y, r, s))
+    st = gsi.Stack(calls)
+    st.run()
+    sync()
+    for i, (W, V, X, y, r, s) in enumerate(keep):
+        compare_tokens(f64(W), f64(V), f64(X[:1]), 0.05, f64(y)[None], np.array([int(s.item())]),
+                       np.array([float(r.item())]), dtype, rho_tol=2e-2, what=f"ragged {i}")
+
+
+# ------------------------------------------------------------ edge cases -----
+
+def small_map(dtype=torch.bfloat16, d=512, d_out=328, k=32, seed=5):
+    W = synth.gaussian_weight(d_out, d, (92, seed, 0, 0), dtype=dtype)
+    v, u = synth.orthonormal_frame(d, k, 16, (92, seed, 0, 1))
+    return W, v, u
+
+
+def test_zero_nan_and_thresholds():
+    W, v, u = small_map()
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    X, _ = synth.tokens(v, u, torch.tensor([False, True, False, False]), (92, 5, 0))
+    X = X.to(torch.bfloat16)
+    X[2] = 0
+    X[3, 7] = float("nan")
+    Xd = X.to(DEV)
+    y, rho, slow = gsi.gsi_linear(m, Xd, 0.05)
+    sync()
+    assert slow.tolist() == [0, 1, 0, 1]
+    assert rho[2].item() == 0.0 and torch.all(y[2] == 0)
+    assert torch.isnan(rho[3]) and not torch.isfinite(y[3]).all()
+    compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y), slow.cpu().numpy(), f64(rho),
+                   torch.bfloat16, what="edge")
+    # eps <= 0: every token slow (x = 0 included, its output is still 0)
+    _, _, s0 = gsi.gsi_linear(m, Xd, 0.0)
+    # eps > 1: every finite token fast
+    y2, _, s2 = gsi.gsi_linear(m, Xd, 2.0)
+    sync()
+    assert s0.tolist() == [1, 1, 1, 1]
+    assert s2.tolist() == [0, 0, 0, 1]
+    compare_tokens(f64(W), f64(V), f64(X), 2.0, f64(y2), s2.cpu().numpy(), np.zeros(4),
+                   torch.bfloat16, what="eps>1")
+
+
+def test_forced_modes_and_full_rank():
+    W, v, u = small_map(torch.float32, d=256, d_out=136, k=256 - 16)
+    V = v.to(torch.float32)
+    m = new_map(W, V)
+    X, _ = synth.tokens(v, u, torch.tensor([False, True, True]), (92, 6, 0))
+    X = X.to(torch.float32)
+    Xd = X.to(DEV)
+    for mode in (gsi.FORCE_FAST, gsi.FORCE_SLOW):
+        y, rho, slow = gsi.gsi_linear(m, Xd, 0.05, mode=mode)
+        sync()
+        assert slow.tolist() == ([0, 0, 0] if mode == gsi.FORCE_FAST else [1, 1, 1])
+        compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y), slow.cpu().numpy(), f64(rho),
+                       torch.float32, mode=mode, what=f"mode {mode}")
+    # k = d: every token lies in the subspace; the fast output equals W x
+    Wf = synth.gaussian_weight(64, 128, (92, 7, 0, 0), dtype=torch.float32)
+    vf, _ = synth.orthonormal_frame(128, 128, 0, (92, 7, 0, 1))
+    mf = new_map(Wf, vf.to(torch.float32))
+    Xf = torch.randn(5, 128, generator=synth.generator("cpu", 92, 7, 0, 2)).to(torch.float32)
+    y, rho, slow = gsi.gsi_linear(mf, Xf.to(DEV), 0.05)
+    sync()
+    assert slow.tolist() == [0] * 5 and float(rho.max()) < 1e-3
+    ref = f64(Xf) @ f64(Wf).T
+    assert np.allclose(f64(y), ref, rtol=1e-4, atol=1e-4)
+
+
+def test_determinism_and_workspace_reuse():
+    W, v, u = small_map(d=2048, d_out=1000, k=128)
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    mask = torch.zeros(64, dtype=torch.bool)
+    mask[::7] = True
+    X, _ = synth.tokens(v, u, mask, (92, 8, 0))
+    Xd = X.to(torch.bfloat16).to(DEV)
+    ws = gsi.workspace(gsi.gsi_linear_workspace(m, 64), DEV)
+    a = gsi.gsi_linear(m, Xd, 0.05, ws=ws)
+    b = gsi.gsi_linear(m, Xd, 0.05, ws=ws)
+    sync()
+    for p, q in zip(a, b):
+        assert torch.equal(p.view(torch.uint8), q.view(torch.uint8))
+    assert torch.equal(a[2].bool().cpu(), mask)
+
+
+def test_empty_batch_is_noop():
+    W, v, _ = small_map()
+    m = new_map(W, v.to(torch.bfloat16))
+    y = torch.full((0, W.shape[0]), 7.0, dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((0, W.shape[1]), dtype=torch.bfloat16, device=DEV)
+    out = gsi.gsi_linear(m, x, 0.05, y=y)
+    sync()
+    assert out[0].shape == (0, W.shape[0])
+
+
+def test_many_tokens_multiple_launches():
+    """More tokens than one launch takes (4096): split launches, same results."""
+    W = synth.gaussian_weight(64, 64, (93, 0, 0, 0), dtype=torch.float32)
+    v, u = synth.orthonormal_frame(64, 8, 16, (93, 0, 0, 1))
+    mask = torch.zeros(5000, dtype=torch.bool)
+    mask[::10] = True
+    X, _ = synth.tokens(v, u, mask, (93, 0, 0))
+    X = X.to(torch.float32)
+    m = new_map(W, v.to(torch.float32))
+    y, rho, slow = gsi.gsi_linear(m, X.to(DEV), 0.05)
+    sync()
+    assert torch.equal(slow.bool().cpu(), mask)
+    sel = np.r_[0:40, 4090:4110, 4980:5000]
+    compare_tokens(f64(W), f64(v.to(torch.float32)), f64(X)[sel], 0.05, f64(y)[sel],
+                   slow.cpu().numpy()[sel], f64(rho)[sel], torch.float32, what="T=5000")
