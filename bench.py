@@ -141,6 +141,30 @@ def cpu_baseline(wl, seconds):
                       f"fp64 numpy, {el:.1f}s; step time scaled by {maps_total}/{len(host)} maps"}
 
 
+def kernel_source_sha() -> str:
+    """sha256 of the kernel sources; counter figures are only reported for the code they measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gsi_kernels.hip", "gsi_internal.h"):
+        with open(os.path.join(ROOT, "rank_gated_memory_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this code."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else float(k["hbm_bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -280,7 +304,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": apply_gbps / PEAK_HBM_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, "apply_kernel"),
             "bytes_per_launch": float(apply_b[idx].mean()),
             "mean_launch_us": float(t_apply.mean() * 1e6),
         },

@@ -62,27 +62,46 @@ int cu_count() {
 // Bytes of V_k one projection unit aims at, given the total projection
 // bytes of a launch: enough units to fill 256 CUs several times over, each
 // large enough to keep a workgroup streaming.
+#ifndef GSI_PROJ_UNIT_KB
+#define GSI_PROJ_UNIT_KB 512
+#endif
+#ifndef GSI_APPLY_BLOCKS_PER_CU
+#define GSI_APPLY_BLOCKS_PER_CU 32
+#endif
+
 int64_t proj_target_bytes(int64_t total_v_bytes) {
   int64_t t = total_v_bytes / (256 * 4);
   if (t < 16 * 1024) t = 16 * 1024;
-  if (t > 128 * 1024) t = 128 * 1024;
+  if (t > GSI_PROJ_UNIT_KB * 1024) t = GSI_PROJ_UNIT_KB * 1024;
   return t;
 }
 
 struct WsLayout {
-  uint64_t gate_off, float_off, total;
+  uint64_t gate_off, need_off, pref_off, float_off, total;
 };
 
 WsLayout ws_layout(int64_t n, int64_t floats) {
   WsLayout w;
-  w.gate_off = align_up((uint64_t)n * 4, 256);
-  w.float_off = align_up(w.gate_off + (uint64_t)n * 16, 256);
+  w.gate_off = align_up((uint64_t)(n + 1) * 4, 256);
+  w.need_off = align_up(w.gate_off + (uint64_t)n * 16, 256);
+  w.pref_off = align_up(w.need_off + (uint64_t)n * 4, 256);
+  w.float_off = align_up(w.pref_off + (uint64_t)(n + 1) * 4, 256);
   w.total = align_up(w.float_off + (uint64_t)floats * 4, 256);
   return w;
 }
 
+void set_ws(KArgs &a, void *ws, uint64_t gate_off, uint64_t need_off, uint64_t pref_off,
+            uint64_t float_off) {
+  char *b = static_cast<char *>(ws);
+  a.counters = reinterpret_cast<uint32_t *>(b);
+  a.gate = b + gate_off;
+  a.need = reinterpret_cast<int32_t *>(b + need_off);
+  a.pref = reinterpret_cast<int32_t *>(b + pref_off);
+  a.wsf = reinterpret_cast<float *>(b + float_off);
+}
+
 int apply_grid(int64_t units_b_max) {
-  int64_t g = (int64_t)cu_count() * 8;
+  int64_t g = (int64_t)cu_count() * GSI_APPLY_BLOCKS_PER_CU;
   if (units_b_max < g) g = units_b_max;
   if (g < 1) g = 1;
   return (int)g;
@@ -184,6 +203,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     o.a_units = us.a_units;
     o.a_rows = us.a_rows;
     o.fast_units = us.fast_units;
+    o.fast_tiles = us.fast_tiles;
     o.slow_units = us.slow_units;
     o.slow_rows = us.slow_rows;
     o.g_off = 0;
@@ -196,9 +216,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     a.mode = mode;
     a.max_k = map->k;
     a.max_d = map->d;
-    a.counters = static_cast<uint32_t *>(ws);
-    a.gate = static_cast<char *>(ws) + wl.gate_off;
-    a.wsf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.float_off);
+    set_ws(a, ws, wl.gate_off, wl.need_off, wl.pref_off, wl.float_off);
     const int64_t ub = (int64_t)n * (us.fast_units > us.slow_units ? us.fast_units : us.slow_units);
     const hipError_t e = launch_batch1(map->dtype, a, apply_grid(ub), 3, st);
     if (e != hipSuccess) return GSI_E_HIP;
@@ -294,6 +312,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.a_units = us.a_units;
     o.a_rows = us.a_rows;
     o.fast_units = us.fast_units;
+    o.fast_tiles = us.fast_tiles;
     o.slow_units = us.slow_units;
     o.slow_rows = us.slow_rows;
     o.g_off = g_off;
@@ -314,6 +333,8 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   const WsLayout wl = ws_layout(n, part_off);
   h->ws_bytes = n > 0 ? wl.total : 0;
   h->ws_gate_off = wl.gate_off;
+  h->ws_need_off = wl.need_off;
+  h->ws_pref_off = wl.pref_off;
   h->ws_float_off = wl.float_off;
   return GSI_OK;
 }
@@ -352,9 +373,7 @@ gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t 
   a.mode = mode;
   a.max_k = h->max_k;
   a.max_d = h->max_d;
-  a.counters = static_cast<uint32_t *>(ws);
-  a.gate = static_cast<char *>(ws) + h->ws_gate_off;
-  a.wsf = reinterpret_cast<float *>(static_cast<char *>(ws) + h->ws_float_off);
+  set_ws(a, ws, h->ws_gate_off, h->ws_need_off, h->ws_pref_off, h->ws_float_off);
   const hipError_t e = launch_batch1(h->dtype, a, apply_grid(h->units_b), phase,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;

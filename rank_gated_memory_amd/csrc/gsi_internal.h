@@ -37,7 +37,8 @@ struct alignas(16) CallDesc {
   int64_t part_off;    // float offset in the workspace of the partials [a_units][k + 4]
   int64_t g_off;       // float offset in the workspace of g [k]
   int32_t gate_off;    // index of this call's gate record / counter
-  int32_t pad_[3];
+  int32_t fast_tiles;  // 64-row image tiles per fast output unit (multiple of kWaves)
+  int32_t pad_[2];
 };
 static_assert(sizeof(CallDesc) == 128, "CallDesc layout");
 
@@ -56,14 +57,19 @@ struct alignas(16) PlanHeader {
   uint64_t unit_off;   // byte offset of int32 unit_call[units_a]
   uint64_t total_bytes;
   uint64_t ws_gate_off;  // byte offsets of the workspace regions
+  uint64_t ws_need_off;
+  uint64_t ws_pref_off;
   uint64_t ws_float_off;
 };
-static_assert(sizeof(PlanHeader) == 80, "PlanHeader layout");
+static_assert(sizeof(PlanHeader) == 96, "PlanHeader layout");
 
 // Workspace regions (byte offsets from the workspace base):
-//   [0, 4n)            uint32 counters, one per call (zero between calls)
-//   [gate_off, +16n)   float4 gate record per call: rho, slow flag bits, ||x||^2, ||g||^2
-//   [float_off, ...)   floats: g of every call, then projection partials
+//   [0, 4(n+1))         uint32 counters: one per call, then one for the whole
+//                       launch (all zero between launches)
+//   [gate_off, +16n)    float4 gate record per call: rho, slow flag bits, ||x||^2, ||g||^2
+//   [need_off, +4n)     int32 output units the chosen path of each call needs
+//   [pref_off, +4(n+1)) int32 exclusive prefix of need (pref[n] = all units)
+//   [float_off, ...)    floats: g of every call, then projection partials
 #if defined(__HIPCC__)
 __host__ __device__
 #endif
@@ -87,15 +93,21 @@ struct KArgs {
   int32_t pad_;
   uint32_t *counters;
   void *gate;   // float4 records
+  int32_t *need;
+  int32_t *pref;
   float *wsf;
 };
 
 // Unit sizing shared by the stack plan and the single-map path.
 struct UnitShape {
-  int32_t a_units, a_rows, fast_units, slow_units, slow_rows;
+  int32_t a_units, a_rows, fast_units, fast_tiles, slow_units, slow_rows;
   int64_t part_floats;  // a_units * (k + 4)
   int64_t g_floats;     // k rounded up to a multiple of 4
 };
+
+// Output units aim at this many bytes of M (fast) or W (slow), so that a
+// contiguous range of units is a balanced share of a launch.
+constexpr int64_t kApplyUnitBytes = 128 * 1024;
 
 inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_proj_bytes) {
   UnitShape s{};
@@ -108,8 +120,13 @@ inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_p
   s.a_rows = (int32_t)rows;
   s.a_units = (int32_t)((d + rows - 1) / rows);
   const int tiles = (d_out + kTileRows - 1) / kTileRows;
-  s.fast_units = (tiles + kWaves - 1) / kWaves;
-  int64_t srows = (256 * 1024) / ((int64_t)d * esize);
+  int64_t ft = kApplyUnitBytes / ((int64_t)kTileRows * k * esize);
+  ft = (ft + kWaves - 1) / kWaves * kWaves;
+  if (ft < kWaves) ft = kWaves;
+  if (ft > 8 * kWaves) ft = 8 * kWaves;
+  s.fast_tiles = (int32_t)ft;
+  s.fast_units = (int32_t)((tiles + ft - 1) / ft);
+  int64_t srows = kApplyUnitBytes / ((int64_t)d * esize);
   srows = srows / kWaves * kWaves;
   if (srows < kWaves) srows = kWaves;
   if (srows > 256) srows = 256;

@@ -11,10 +11,25 @@
 //                  last workgroup of a call (device-scope counter) sums the
 //                  partials in a fixed order, forms ||g||^2, rho and the gate
 //                  (GSI-TS §2.2) and publishes them.  Bitwise deterministic.
-//   apply_kernel : persistent loop over output units.  Every workgroup
-//                  derives the same prefix over calls of "units needed by the
-//                  path this call's gate chose", so only the chosen path's
-//                  bytes are ever read.  Fast units: one lane per output row,
+//
+//                  Cross-XCD hand-off without cache maintenance: the eight
+//                  XCDs of gfx950 have private L2s, and an agent-scope fence
+//                  compiles to an L2 write-back + invalidate that costs ~10x
+//                  the whole kernel when every workgroup issues one.  So the
+//                  partials are written with agent-scope atomic stores
+//                  (write-through, "sc1"), each thread waits for its stores to
+//                  be acknowledged (s_waitcnt 0) before the workgroup barrier,
+//                  one thread bumps the call's counter with a relaxed
+//                  agent-scope atomic, and the last workgroup reads the
+//                  partials with agent-scope atomic loads (which bypass stale
+//                  L2 lines).  Nothing else crosses workgroups inside the
+//                  launch; g and the gate reach apply_kernel through the
+//                  kernel boundary.
+//   apply_kernel : persistent loop over output units.  The projection
+//                  launch leaves a prefix over calls of "units needed by the
+//                  path this call's gate chose" (written by the last call to
+//                  finish), so only the chosen path's bytes are ever read and
+//                  each workgroup takes a contiguous, equal share of units.  Fast units: one lane per output row,
 //                  reading the tiled image M in 16-byte vectors against g in
 //                  LDS (y = M g).  Slow units: one wavefront per row of W,
 //                  x staged in LDS, wave reduction (y = W x).
@@ -111,6 +126,14 @@ __device__ __forceinline__ float rho_from_norms(float xx, float gg) {
   return t > 0.f ? sqrtf(t) : 0.f;
 }
 
+// Agent-coherent accesses used for the partials handed between workgroups.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ CallDesc load_call(const KArgs &a, int c) {
   if (a.table) return a.table[c];
   CallDesc d = a.one;
@@ -127,13 +150,51 @@ __device__ __forceinline__ CallDesc load_call(const KArgs &a, int c) {
 
 // ---------------------------------------------------------------------------
 // Projection: partial g and ||x||^2 per row chunk, gate by the last chunk.
+// MODE is the gsi_mode (a template argument so that each mode is a distinct
+// kernel in traces).
 // ---------------------------------------------------------------------------
-template <typename T, int UNROLL>
+__device__ __forceinline__ void store_coherent_i(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent_i(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix of need[0..n) into pref[0..n] by one workgroup (the last
+// call to finish its gate); need[] is read with agent-coherent loads.
+__device__ void launch_prefix(const KArgs &a, int *sh_int) {
+  const int tid = threadIdx.x;
+  const int n = a.n;
+  const int per = (n + kBlock - 1) / kBlock;  // calls per thread (n <= kMaxCalls)
+  const int c0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (c0 + i < n) local += load_coherent_i(a.need + c0 + i);
+  sh_int[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kBlock; off <<= 1) {
+    const int t = tid >= off ? sh_int[tid - off] : 0;
+    __syncthreads();
+    sh_int[tid] += t;
+    __syncthreads();
+  }
+  int run = sh_int[tid] - local;  // exclusive prefix at c0
+  for (int i = 0; i < per; ++i) {
+    if (c0 + i < n) {
+      a.pref[c0 + i] = run;
+      run += load_coherent_i(a.need + c0 + i);
+    }
+  }
+  if (tid == kBlock - 1) a.pref[n] = sh_int[kBlock - 1];
+}
+
+template <typename T, int UNROLL, int MODE>
 __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   constexpr int VW = Vec<T>::VW;
   __shared__ float xs[kProjRowsMax];
   __shared__ float red[kBlock * VW];
   __shared__ float sh[kWaves];
+  __shared__ int sh_int[kBlock];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -144,20 +205,20 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   const int row0 = q * cd.a_rows;
   const int rows = min(cd.a_rows, cd.d - row0);
   const int k = cd.k;
-
-  float xx = 0.f;
-  for (int i = tid; i < rows; i += kBlock) {
-    const float v = Vec<T>::load1(cd.x, (size_t)row0 + i);
-    xs[i] = v;
-    xx = fmaf(v, v, xx);
-  }
-  xx = block_sum(xx, sh);  // also publishes xs to the workgroup
-
   const int tpr = k / VW;        // lanes per row of V_k
   const int rpp = kBlock / tpr;  // rows per pass
   const int slot = tid / tpr;
   const int col = tid - slot * tpr;
-  if (slot < rpp) {
+  const bool active = slot < rpp;
+  float xx = 0.f;
+  for (int i = tid; i < rows; i += kBlock) {
+    const float xv = Vec<T>::load1(cd.x, (size_t)row0 + i);
+    xs[i] = xv;
+    xx = fmaf(xv, xv, xx);
+  }
+  xx = block_sum(xx, sh);  // also publishes xs to the workgroup
+
+  if (active) {
     float acc[VW];
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[e] = 0.f;
@@ -195,21 +256,20 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   for (int j = tid; j < k; j += kBlock) {
     float s = 0.f;
     for (int sl = 0; sl < rpp; ++sl) s += red[sl * k + j];
-    part[j] = s;
+    store_coherent(part + j, s);
   }
-  if (tid == 0) part[k] = xx;
+  if (tid == 0) store_coherent(part + k, xx);
 
-  // Release the partials; the last chunk of this call finishes the gate.
-  __threadfence();
+  // Hand the partials over (see the header); the last chunk finishes the gate.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_ACQ_REL,
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (unsigned)(cd.a_units - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   const float *p0 = a.wsf + cd.part_off;
   float *g = a.wsf + cd.g_off;
@@ -220,27 +280,41 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
     for (; qq + 8 <= cd.a_units; qq += 8) {
       float t[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = p0[(int64_t)(qq + i) * stride + j];
+      for (int i = 0; i < 8; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
 #pragma unroll
       for (int i = 0; i < 8; ++i) s += t[i];
     }
-    for (; qq < cd.a_units; ++qq) s += p0[(int64_t)qq * stride + j];
+    for (; qq < cd.a_units; ++qq) s += load_coherent(p0 + (int64_t)qq * stride + j);
     g[j] = s;
     gg = fmaf(s, s, gg);
   }
   float xp = 0.f;
-  for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += p0[(int64_t)qq * stride + k];
+  for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += load_coherent(p0 + (int64_t)qq * stride + k);
   gg = block_sum(gg, sh);
   const float xxt = block_sum(xp, sh);
   if (tid == 0) {
     const float rho = rho_from_norms(xxt, gg);
-    const int slow = a.mode == 2 ? 1 : (a.mode == 1 ? 0 : !(rho < cd.eps));
+    const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < cd.eps));
     reinterpret_cast<float4 *>(a.gate)[cd.gate_off] =
         make_float4(rho, __int_as_float(slow), xxt, gg);
     if (cd.rho) *cd.rho = rho;
     if (cd.slow) *cd.slow = (uint8_t)slow;
-    a.counters[cd.gate_off] = 0u;  // ready for the next call on this workspace
+    a.counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
+    store_coherent_i(a.need + c, slow ? cd.slow_units : cd.fast_units);
   }
+
+  // The last call to finish writes the launch-wide prefix of output units.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + a.n, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned)(a.n - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  launch_prefix(a, sh_int);
+  if (tid == 0) a.counters[a.n] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -252,32 +326,46 @@ __device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const f
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int tiles = (cd.d_out + kTileRows - 1) / kTileRows;
-  const int tile = local * kWaves + wave;
-  if (tile >= tiles) return;
+  const int t1 = min((local + 1) * cd.fast_tiles, tiles);
   const int kv = cd.k / VW;
-  const uint4 *mp = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * kTileRows * kv + lane;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int cg = 0; cg < kv; cg += UNROLL) {
-    uint4 v[UNROLL];
+  const size_t tile_vecs = (size_t)kTileRows * kv;
+  // Each wavefront streams two tiles at a time (tiles t and t + kWaves), one
+  // output row per lane in each, so 2 * UNROLL 16-byte loads are in flight.
+  for (int tile = local * cd.fast_tiles + wave; tile < t1; tile += 2 * kWaves) {
+    const bool two = tile + kWaves < t1;
+    const uint4 *ma = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * tile_vecs + lane;
+    const uint4 *mb = ma + (two ? (size_t)kWaves * tile_vecs : 0);
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    for (int cg = 0; cg < kv; cg += UNROLL) {
+      uint4 va[UNROLL], vb[UNROLL];
 #pragma unroll
-    for (int j = 0; j < UNROLL; ++j)
-      v[j] = (cg + j < kv) ? mp[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < UNROLL; ++j) {
+        const bool ok = cg + j < kv;
+        va[j] = ok ? ma[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+        vb[j] = (ok && two) ? mb[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+      }
 #pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      if (cg + j < kv) {
-        float f[VW];
-        Vec<T>::unpack(v[j], f);
-        const float *gp = gs + (cg + j) * VW;
+      for (int j = 0; j < UNROLL; ++j) {
+        if (cg + j < kv) {
+          float fa[VW], fb[VW];
+          Vec<T>::unpack(va[j], fa);
+          Vec<T>::unpack(vb[j], fb);
+          const float *gp = gs + (cg + j) * VW;
 #pragma unroll
-        for (int e = 0; e < VW; e += 2) {
-          acc0 = fmaf(f[e], gp[e], acc0);
-          acc1 = fmaf(f[e + 1], gp[e + 1], acc1);
+          for (int e = 0; e < VW; e += 2) {
+            a0 = fmaf(fa[e], gp[e], a0);
+            a1 = fmaf(fa[e + 1], gp[e + 1], a1);
+            b0 = fmaf(fb[e], gp[e], b0);
+            b1 = fmaf(fb[e + 1], gp[e + 1], b1);
+          }
         }
       }
     }
+    const int oa = tile * kTileRows + lane;
+    if (oa < cd.d_out) Vec<T>::store1(cd.y, oa, a0 + a1);
+    const int ob = (tile + kWaves) * kTileRows + lane;
+    if (two && ob < cd.d_out) Vec<T>::store1(cd.y, ob, b0 + b1);
   }
-  const int o = tile * kTileRows + lane;
-  if (o < cd.d_out) Vec<T>::store1(cd.y, o, acc0 + acc1);
 }
 
 template <typename T, int UNROLL>
@@ -288,56 +376,51 @@ __device__ __forceinline__ void slow_unit(const CallDesc &cd, int local, const u
   const int r0 = local * cd.slow_rows;
   const int r1 = min(r0 + cd.slow_rows, cd.d_out);
   const int nv = cd.d / VW;
-  for (int r = r0 + wave; r < r1; r += kWaves) {
-    const uint4 *wp =
-        reinterpret_cast<const uint4 *>(static_cast<const T *>(cd.W) + (size_t)r * cd.d);
-    float acc0 = 0.f, acc1 = 0.f;
+  // Each wavefront takes two rows of W at a time (rows r and r + kWaves) so
+  // that 2 * UNROLL 16-byte loads per lane are in flight.
+  for (int r = r0 + wave; r < r1; r += 2 * kWaves) {
+    const bool two = r + kWaves < r1;
+    const uint4 *wa = reinterpret_cast<const uint4 *>(static_cast<const T *>(cd.W) + (size_t)r * cd.d);
+    const uint4 *wb = wa + (two ? (size_t)kWaves * nv : 0);
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
     for (int v0 = lane; v0 < nv; v0 += 64 * UNROLL) {
-      uint4 w[UNROLL];
+      uint4 wA[UNROLL], wB[UNROLL];
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         const int vv = v0 + j * 64;
-        w[j] = vv < nv ? wp[vv] : make_uint4(0u, 0u, 0u, 0u);
+        wA[j] = vv < nv ? wa[vv] : make_uint4(0u, 0u, 0u, 0u);
+        wB[j] = (two && vv < nv) ? wb[vv] : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         const int vv = v0 + j * 64;
         if (vv < nv) {
-          float f[VW], xf[VW];
-          Vec<T>::unpack(w[j], f);
+          float fa[VW], fb[VW], xf[VW];
+          Vec<T>::unpack(wA[j], fa);
+          Vec<T>::unpack(wB[j], fb);
           Vec<T>::unpack(xs[vv], xf);
 #pragma unroll
           for (int e = 0; e < VW; e += 2) {
-            acc0 = fmaf(f[e], xf[e], acc0);
-            acc1 = fmaf(f[e + 1], xf[e + 1], acc1);
+            a0 = fmaf(fa[e], xf[e], a0);
+            a1 = fmaf(fa[e + 1], xf[e + 1], a1);
+            b0 = fmaf(fb[e], xf[e], b0);
+            b1 = fmaf(fb[e + 1], xf[e + 1], b1);
           }
         }
       }
     }
-    const float s = wave_sum(acc0 + acc1);
-    if (lane == 0) Vec<T>::store1(cd.y, r, s);
+    const float sa = wave_sum(a0 + a1);
+    const float sb = wave_sum(b0 + b1);
+    if (lane == 0) {
+      Vec<T>::store1(cd.y, r, sa);
+      if (two) Vec<T>::store1(cd.y, r + kWaves, sb);
+    }
   }
 }
 
-__device__ __forceinline__ int call_units(const KArgs &a, int c) {
-  int fu, su, go;
-  if (a.table) {
-    fu = a.table[c].fast_units;
-    su = a.table[c].slow_units;
-    go = a.table[c].gate_off;
-  } else {
-    fu = a.one.fast_units;
-    su = a.one.slow_units;
-    go = c;
-  }
-  const float4 gi = reinterpret_cast<const float4 *>(a.gate)[go];
-  return __float_as_int(gi.y) ? su : fu;
-}
-
-template <typename T, int UNROLL>
+template <typename T, int UNROLL, int MODE>
 __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int tmp[kBlock];
   const int tid = threadIdx.x;
   const int n = a.n;
   const size_t pref_bytes = align_up((uint64_t)(n + 1) * 4, 16);
@@ -346,41 +429,38 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
   float *gs = reinterpret_cast<float *>(smem + pref_bytes);
   uint4 *xs = reinterpret_cast<uint4 *>(smem + pref_bytes + g_bytes);
 
-  // Prefix over calls of the units their chosen path needs.
-  if (tid == 0) pref[0] = 0;
-  int carry = 0;
-  for (int base = 0; base < n; base += kBlock) {
-    const int c = base + tid;
-    tmp[tid] = c < n ? call_units(a, c) : 0;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-      const int t = tid >= off ? tmp[tid - off] : 0;
-      __syncthreads();
-      tmp[tid] += t;
-      __syncthreads();
-    }
-    if (c < n) pref[c + 1] = carry + tmp[tid];
-    carry += tmp[kBlock - 1];
-    __syncthreads();
-  }
-  const int total = carry;
+  // Prefix over calls of the units their chosen path needs (written by the
+  // projection launch).
+  for (int i = tid; i <= n; i += kBlock) pref[i] = a.pref[i];
+  __syncthreads();
+  const int total = pref[n];
 
+  // Each workgroup takes a contiguous range of units, so x or g is staged
+  // again only when the range crosses into the next call.
+  const int u0 = (int)((int64_t)total * blockIdx.x / gridDim.x);
+  const int u1 = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
   int cur = -1;
-  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+  int c = 0;
+  if (u0 < u1) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (pref[mid] <= u)
+      if (pref[mid] <= u0)
         lo = mid;
       else
         hi = mid - 1;
     }
-    const int c = lo;
+    c = lo;
+  }
+  CallDesc cd;
+  bool slow = false;
+  for (int u = u0; u < u1; ++u) {
+    while (pref[c + 1] <= u) ++c;
     const int local = u - pref[c];
-    const CallDesc cd = load_call(a, c);
-    const float4 gi = reinterpret_cast<const float4 *>(a.gate)[cd.gate_off];
-    const bool slow = __float_as_int(gi.y) != 0;
     if (c != cur) {
+      cd = load_call(a, c);
+      const float4 gi = reinterpret_cast<const float4 *>(a.gate)[cd.gate_off];
+      slow = __float_as_int(gi.y) != 0;
       __syncthreads();
       if (slow) {
         const int nv = cd.d / Vec<T>::VW;
@@ -473,21 +553,37 @@ size_t apply_lds_bytes(const KArgs &a, int esize) {
          align_up((uint64_t)a.max_d * esize, 16);
 }
 
-hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s) {
+#ifndef GSI_PROJ_UNROLL
+#define GSI_PROJ_UNROLL 8
+#endif
+
+template <typename T, int MODE>
+void launch_modes(const KArgs &a, int grid_b, int phases, size_t lds, hipStream_t s) {
   constexpr int U = 8;
+  constexpr int UP = GSI_PROJ_UNROLL;
+  if (phases & 1)
+    hipLaunchKernelGGL((proj_kernel<T, UP, MODE>), dim3(a.units_a), dim3(kBlock), 0, s, a);
+  if (phases & 2)
+    hipLaunchKernelGGL((apply_kernel<T, U, MODE>), dim3(grid_b), dim3(kBlock), lds, s, a);
+}
+
+template <typename T>
+void launch_typed(const KArgs &a, int grid_b, int phases, size_t lds, hipStream_t s) {
+  if (a.mode == 1)
+    launch_modes<T, 1>(a, grid_b, phases, lds, s);
+  else if (a.mode == 2)
+    launch_modes<T, 2>(a, grid_b, phases, lds, s);
+  else
+    launch_modes<T, 0>(a, grid_b, phases, lds, s);
+}
+
+hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s) {
   const int esize = dtype == 0 ? 4 : 2;
   const size_t lds = apply_lds_bytes(a, esize);
-  if (dtype == 0) {
-    if (phases & 1)
-      hipLaunchKernelGGL((proj_kernel<float, U>), dim3(a.units_a), dim3(kBlock), 0, s, a);
-    if (phases & 2)
-      hipLaunchKernelGGL((apply_kernel<float, U>), dim3(grid_b), dim3(kBlock), lds, s, a);
-  } else {
-    if (phases & 1)
-      hipLaunchKernelGGL((proj_kernel<bf16_t, U>), dim3(a.units_a), dim3(kBlock), 0, s, a);
-    if (phases & 2)
-      hipLaunchKernelGGL((apply_kernel<bf16_t, U>), dim3(grid_b), dim3(kBlock), lds, s, a);
-  }
+  if (dtype == 0)
+    launch_typed<float>(a, grid_b, phases, lds, s);
+  else
+    launch_typed<bf16_t>(a, grid_b, phases, lds, s);
   return hipGetLastError();
 }
 

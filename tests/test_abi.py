@@ -118,7 +118,8 @@ def calls_array(specs):
 PLAN_HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("n", "<i4"), ("dtype", "<i4"),
                      ("units_a", "<i4"), ("units_b", "<i4"), ("max_k", "<i4"), ("max_d", "<i4"),
                      ("ws_bytes", "<u8"), ("desc_off", "<u8"), ("unit_off", "<u8"),
-                     ("total_bytes", "<u8"), ("ws_gate_off", "<u8"), ("ws_float_off", "<u8")])
+                     ("total_bytes", "<u8"), ("ws_gate_off", "<u8"), ("ws_need_off", "<u8"),
+                     ("ws_pref_off", "<u8"), ("ws_float_off", "<u8")])
 
 
 def build_plan(specs):
