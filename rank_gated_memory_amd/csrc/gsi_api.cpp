@@ -15,6 +15,7 @@ namespace gsi {
 hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int d, int d_out,
                           int k, hipStream_t s);
 hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s);
+hipError_t launch_batched(const BArgs &a, hipStream_t s);
 }  // namespace gsi
 
 using namespace gsi;
@@ -149,16 +150,64 @@ static uint64_t linear_ws_bytes(const gsi_map *map, int64_t n) {
   return ws_layout(n, n * (us.g_floats + us.part_floats)).total;
 }
 
+// bf16 maps with two or more tokens take the batched MFMA path; fp32 maps
+// and single tokens take the batch-1 kernels.
+static bool use_batched(const gsi_map *map, int32_t T) { return map->dtype == GSI_BF16 && T >= 2; }
+
 size_t gsi_linear_workspace(const gsi_map *map, int32_t T) {
   if (check_map(map) != GSI_OK || T <= 0) return 0;
-  // launches of kMaxCalls tokens, then one with the remainder
   uint64_t need = 0;
+  if (use_batched(map, T)) {
+    // launches of kMaxBatch tokens, then one with the remainder
+    if (T >= kMaxBatch) need = batch_shape(kMaxBatch, map->d, map->k).total;
+    if (T % kMaxBatch) {
+      const uint64_t r = batch_shape(T % kMaxBatch, map->d, map->k).total;
+      if (r > need) need = r;
+    }
+    return (size_t)need;
+  }
+  // launches of kMaxCalls tokens, then one with the remainder
   if (T >= kMaxCalls) need = linear_ws_bytes(map, kMaxCalls);
   if (T % kMaxCalls) {
     const uint64_t r = linear_ws_bytes(map, T % kMaxCalls);
     if (r > need) need = r;
   }
   return (size_t)need;
+}
+
+static gsi_status linear_batched(const gsi_map *map, const void *x, void *y, int32_t T, float eps,
+                                 int32_t mode, float *rho, uint8_t *slow, void *ws,
+                                 hipStream_t st) {
+  for (int32_t t0 = 0; t0 < T; t0 += kMaxBatch) {
+    const int32_t n = (T - t0) < kMaxBatch ? (T - t0) : kMaxBatch;
+    const BatchShape b = batch_shape(n, map->d, map->k);
+    BArgs a{};
+    a.W = map->W;
+    a.V = map->V;
+    a.M = map->M;
+    a.x = static_cast<const char *>(x) + (int64_t)t0 * map->d * 2;
+    a.y = static_cast<char *>(y) + (int64_t)t0 * map->d_out * 2;
+    a.rho = rho ? rho + t0 : nullptr;
+    a.slow = slow ? slow + t0 : nullptr;
+    a.n = n;
+    a.d = map->d;
+    a.d_out = map->d_out;
+    a.k = map->k;
+    a.kpad = b.kpad;
+    a.kc = b.kc;
+    a.splits = b.splits;
+    a.mode = mode;
+    a.eps = eps;
+    char *w = static_cast<char *>(ws);
+    a.part = reinterpret_cast<float *>(w + b.part_off);
+    a.xxp = reinterpret_cast<float *>(w + b.xxp_off);
+    a.ghi = reinterpret_cast<uint16_t *>(w + b.ghi_off);
+    a.glo = reinterpret_cast<uint16_t *>(w + b.glo_off);
+    a.flags = reinterpret_cast<int32_t *>(w + b.flags_off);
+    a.zeros = w + b.zeros_off;
+    if (launch_batched(a, st) != hipSuccess) return GSI_E_HIP;
+  }
+  return GSI_OK;
 }
 
 gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, float eps,
@@ -177,6 +226,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
 
   const int es = esize_of(map->dtype);
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_batched(map, T)) return linear_batched(map, x, y, T, eps, mode, rho, slow, ws, st);
   // Tokens are processed in launches of at most kMaxCalls tokens; each
   // launch reuses the same workspace (stream order separates them).
   for (int32_t t0 = 0; t0 < T; t0 += kMaxCalls) {
