@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=512)
     p.add_argument("--warmup", type=int, default=32)
-    p.add_argument("--workload", default="gptj6b-28L", choices=["gptj6b-28L", "llama13b-40L"])
+    p.add_argument("--workload", default="gptj6b-28L",
+                   choices=["gptj6b-28L", "llama13b-40L", "batched-t256"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -165,12 +166,72 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else float(k["hbm_bytes_per_launch"])
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def bench_batched(args):
+    """T=256 tokens through one bf16 map d=4096 -> 16384, k x slow-share sweep.
+
+    Prints one JSON line: tokens/s per cell (whole gsi_linear call: projection
+    GEMM, gate, compacted fast and slow GEMMs), algorithmic GB/s, and the
+    matrix-core fraction of the whole call at each cell.
+    """
+    import torch
+
+    from rank_gated_memory_amd import gsi, synth
+
+    dev = torch.device("cuda:0")
+    cells = []
+    for k in (64, 256, 512):
+        for frac in (0.0, 0.1, 0.5, 1.0):
+            mi = synth.config5(k, frac, device=dev, w_device=dev)
+            m = gsi.Map(mi.W, mi.V)
+            gsi.gsi_prepare(m)
+            T = mi.X.shape[0]
+            y = torch.empty(T, mi.d_out, dtype=torch.bfloat16, device=dev)
+            rho = torch.empty(T, device=dev)
+            sl = torch.empty(T, dtype=torch.uint8, device=dev)
+            ws = gsi.workspace(gsi.gsi_linear_workspace(m, T), dev)
+            for _ in range(args.warmup):
+                gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            ns = int(sl.sum())
+            nf = T - ns
+            d, do = mi.d, mi.d_out
+            byts = 2 * (d * k + T * d + T * do) + (2 * do * k if nf else 0) + (2 * d * do if ns else 0)
+            flops = 2 * T * d * k + 2 * 2 * nf * do * k + 2 * ns * d * do
+            cells.append({"k": k, "slow_share": frac, "slow_tokens": ns, "us_per_call": us,
+                          "tokens_per_s": T / (us * 1e-6), "gbps": byts / us / 1e3,
+                          "tflops": flops / us / 1e6, "mfma_frac": flops / us / 1e6 / PEAK_BF16_TFLOPS})
+            log(f"k={k} slow={frac}: {us:.1f} us, {T / us * 1e6:.0f} tokens/s")
+            del m, mi, ws, y
+    head = [c for c in cells if c["k"] == 256 and c["slow_share"] == 0.1][0]
+    print(json.dumps({
+        "metric": "GSI batched gated linear tokens/s (T=256, d=4096 -> 16384)",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["us_per_call"] / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "batched-t256: T=256, d=4096, d_out=16384, value at k=256, 10% slow",
+                   "cells": cells},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("this build runs on one GPU only: --gpus must be 1 (the path would shard by output "
               "rows or tokens across GPUs, see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "batched-t256":
+        bench_batched(args)
+        return
     import numpy as np
     import torch
 

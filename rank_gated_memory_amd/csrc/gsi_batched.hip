@@ -380,6 +380,69 @@ __global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Image M = W V_k (bf16, once per map): workgroup = 64 rows of W x 64 columns
+// of V_k over all of d.  V_k is staged 256 rows at a time, transposed in LDS;
+// wavefront w multiplies rows 16 w.. of the W tile (v_mfma_f32_16x16x32_bf16).
+// The result is rounded to bf16 into the tiled image layout.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock)
+    bprep_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ V,
+                 uint16_t *__restrict__ M, int d, int d_out, int k) {
+  __shared__ __align__(16) uint16_t Vt[64][kBatchKc + 8];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int o0 = blockIdx.x * 64;
+  const int j0 = blockIdx.y * 64;
+  const int o = o0 + wave * 16 + (lane & 15);
+  const bool row_ok = o < d_out;
+  const int kq = 8 * (lane >> 4);
+  f32x4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < d; i0 += kBatchKc) {
+    const int rows = min(kBatchKc, d - i0);
+    __syncthreads();
+    for (int v = tid; v < kBatchKc * 8; v += kBlock) {
+      const int r = v >> 3, cg = v & 7;
+      const int j = j0 + cg * 8;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows && j < k) u = *reinterpret_cast<const uint4 *>(V + (size_t)(i0 + r) * k + j);
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(&u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[cg * 8 + e][r] = h[e];
+    }
+    __syncthreads();
+    for (int kk = 0; kk < rows; kk += 32) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok && kk + kq < rows) u = *reinterpret_cast<const uint4 *>(W + (size_t)o * d + i0 + kk + kq);
+      const bf16x8_t A = as_bf16x8(u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 b = *reinterpret_cast<const uint4 *>(&Vt[c * 16 + (lane & 15)][kk + kq]);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(b), acc[c], 0, 0, 0);
+      }
+    }
+  }
+  // tiled image: element (r, j) at ((r/64)(k/8) + j/8) 512 + (r%64) 8 + j%8
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = o0 + wave * 16 + 4 * (lane >> 4) + i;  // rows past d_out hold zeros (W rows read as 0)
+      const int j = j0 + c * 16 + (lane & 15);
+      if (j < k) M[((size_t)(r / 64) * (k / 8) + j / 8) * 512 + (r % 64) * 8 + (j % 8)] = f2bf(acc[c][i]);
+    }
+}
+
+hipError_t launch_prepare_bf16(const void *W, const void *V, void *M, int d, int d_out, int k,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(bprep_kernel, dim3((d_out + 63) / 64, (k + 63) / 64), dim3(kBlock), 0, s,
+                     static_cast<const uint16_t *>(W), static_cast<const uint16_t *>(V),
+                     static_cast<uint16_t *>(M), d, d_out, k);
+  return hipGetLastError();
+}
+
 hipError_t launch_batched(const BArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(bproj_kernel, dim3((a.n + 63) / 64, (a.k + 63) / 64, a.splits), dim3(kBlock), 0,
                      s, a);

@@ -33,8 +33,9 @@
 //                  reading the tiled image M in 16-byte vectors against g in
 //                  LDS (y = M g).  Slow units: one wavefront per row of W,
 //                  x staged in LDS, wave reduction (y = W x).
-// prepare_kernel: M = W V_k (fp32 FMA, LDS tiled), written in the tiled
-//                 layout described in gsi.h.
+// prepare_kernel: M = W V_k for fp32 maps (FMA, LDS tiled), written in the
+//                 tiled layout described in gsi.h (bf16 maps use the MFMA
+//                 kernel in gsi_batched.hip).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -534,17 +535,18 @@ __global__ void __launch_bounds__(kBlock)
 // ---------------------------------------------------------------------------
 // Host-side launchers (called from gsi_api.cpp).
 // ---------------------------------------------------------------------------
+hipError_t launch_prepare_bf16(const void *W, const void *V, void *M, int d, int d_out, int k,
+                               hipStream_t s);
+
+// bf16 images are built on the matrix cores (gsi_batched.hip); fp32 images
+// with the FMA kernel above.
 hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int d, int d_out,
                           int k, hipStream_t s) {
+  if (dtype != 0) return launch_prepare_bf16(W, V, M, d, d_out, k, s);
   const dim3 grid((d_out + kTileRows - 1) / kTileRows, (k + 255) / 256);
-  if (dtype == 0)
-    hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kBlock), 0, s,
-                       static_cast<const float *>(W), static_cast<const float *>(V),
-                       static_cast<float *>(M), d, d_out, k);
-  else
-    hipLaunchKernelGGL(prepare_kernel<bf16_t>, grid, dim3(kBlock), 0, s,
-                       static_cast<const bf16_t *>(W), static_cast<const bf16_t *>(V),
-                       static_cast<bf16_t *>(M), d, d_out, k);
+  hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kBlock), 0, s,
+                     static_cast<const float *>(W), static_cast<const float *>(V),
+                     static_cast<float *>(M), d, d_out, k);
   return hipGetLastError();
 }
 
