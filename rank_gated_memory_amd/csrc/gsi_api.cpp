@@ -4,6 +4,7 @@
 // Acceleration" (S. J. Thomas, 2026), §2.1-§2.2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -341,11 +342,29 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   // float offsets: g of every call first, then the partials
   int64_t g_total = 0;
   for (int32_t i = 0; i < n; ++i) g_total += (calls[i].map.k + 3) / 4 * 4;
+  // Projection units of the calls with the most units go first: their
+  // final reductions are the longest and should not be the launch's tail.
+  std::vector<int32_t> order(n);
+  for (int32_t i = 0; i < n; ++i) order[i] = i;
+  std::vector<int32_t> nunits(n);
+  for (int32_t i = 0; i < n; ++i)
+    nunits[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, target).a_units;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return nunits[x] > nunits[y]; });
+  std::vector<int32_t> first_unit(n);
+  {
+    int64_t u = 0;
+    for (int32_t i : order) {
+      first_unit[i] = (int32_t)u;
+      u += nunits[i];
+    }
+  }
   int64_t g_off = 0, part_off = g_total, a_begin = 0, units_b = 0;
   int32_t max_k = 8, max_d = 8;
   for (int32_t i = 0; i < n; ++i) {
     const gsi_call &c = calls[i];
     const UnitShape us = unit_shape(c.map.d, c.map.d_out, c.map.k, es, target);
+    a_begin = first_unit[i];
     CallDesc &o = desc[i];
     o.W = c.map.W;
     o.V = c.map.V;
@@ -369,14 +388,17 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.part_off = part_off;
     o.gate_off = i;
     for (int32_t q = 0; q < us.a_units; ++q) unit_call[a_begin + q] = i;
-    a_begin += us.a_units;
     g_off += us.g_floats;
     part_off += us.part_floats;
     units_b += us.fast_units > us.slow_units ? us.fast_units : us.slow_units;
     if (c.map.k > max_k) max_k = c.map.k;
     if (c.map.d > max_d) max_d = c.map.d;
   }
-  h->units_a = (int32_t)a_begin;
+  {
+    int64_t ua = 0;
+    for (int32_t i = 0; i < n; ++i) ua += nunits[i];
+    h->units_a = (int32_t)ua;
+  }
   h->units_b = (int32_t)units_b;
   h->max_k = max_k;
   h->max_d = max_d;

@@ -167,7 +167,10 @@ struct UnitShape {
 
 // Output units aim at this many bytes of M (fast) or W (slow), so that a
 // contiguous range of units is a balanced share of a launch.
-constexpr int64_t kApplyUnitBytes = 128 * 1024;
+#ifndef GSI_APPLY_UNIT_KB
+#define GSI_APPLY_UNIT_KB 128
+#endif
+constexpr int64_t kApplyUnitBytes = GSI_APPLY_UNIT_KB * 1024;
 
 inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_proj_bytes) {
   UnitShape s{};

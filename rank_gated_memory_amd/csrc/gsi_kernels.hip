@@ -192,7 +192,6 @@ __device__ void launch_prefix(const KArgs &a, int *sh_int) {
 template <typename T, int UNROLL, int MODE>
 __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   constexpr int VW = Vec<T>::VW;
-  __shared__ float xs[kProjRowsMax];
   __shared__ float red[kBlock * VW];
   __shared__ float sh[kWaves];
   __shared__ int sh_int[kBlock];
@@ -211,33 +210,26 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   const int slot = tid / tpr;
   const int col = tid - slot * tpr;
   const bool active = slot < rpp;
+  // Each thread reads the x entry of every V_k row it multiplies (the lanes
+  // of a row share the address), so streaming starts without a staging
+  // barrier; the column-0 lane of each row also accumulates ||x||^2.
   float xx = 0.f;
-  for (int i = tid; i < rows; i += kBlock) {
-    const float xv = Vec<T>::load1(cd.x, (size_t)row0 + i);
-    xs[i] = xv;
-    xx = fmaf(xv, xv, xx);
-  }
-  xx = block_sum(xx, sh);  // also publishes xs to the workgroup
-
   if (active) {
     float acc[VW];
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[e] = 0.f;
     const uint4 *vp =
         reinterpret_cast<const uint4 *>(static_cast<const T *>(cd.V) + (size_t)row0 * k) + col;
-    for (int r = slot; r < rows; r += rpp * UNROLL) {
+    const T *xp = static_cast<const T *>(cd.x) + row0;
+    int r = slot;
+    // full batches: no branch around any load
+    for (; r + (UNROLL - 1) * rpp < rows; r += rpp * UNROLL) {
       uint4 v[UNROLL];
       float xv[UNROLL];
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
-        const int rr = r + j * rpp;
-        if (rr < rows) {
-          v[j] = vp[(size_t)rr * tpr];
-          xv[j] = xs[rr];
-        } else {
-          v[j] = make_uint4(0u, 0u, 0u, 0u);
-          xv[j] = 0.f;
-        }
+        v[j] = vp[(size_t)(r + j * rpp) * tpr];
+        xv[j] = Vec<T>::load1(xp, r + j * rpp);
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
@@ -245,12 +237,23 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
         Vec<T>::unpack(v[j], f);
 #pragma unroll
         for (int e = 0; e < VW; ++e) acc[e] = fmaf(f[e], xv[j], acc[e]);
+        if (col == 0) xx = fmaf(xv[j], xv[j], xx);
       }
+    }
+    // remainder rows of the last chunk of a call
+    for (; r < rows; r += rpp) {
+      const uint4 v = vp[(size_t)r * tpr];
+      const float xv = Vec<T>::load1(xp, r);
+      float f[VW];
+      Vec<T>::unpack(v, f);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[e] = fmaf(f[e], xv, acc[e]);
+      if (col == 0) xx = fmaf(xv, xv, xx);
     }
 #pragma unroll
     for (int e = 0; e < VW; ++e) red[slot * k + col * VW + e] = acc[e];
   }
-  __syncthreads();
+  xx = block_sum(xx, sh);  // also publishes red to the workgroup
 
   const int stride = k + 4;
   float *part = a.wsf + cd.part_off + (int64_t)q * stride;
@@ -278,6 +281,13 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   for (int j = tid; j < k; j += kBlock) {
     float s = 0.f;
     int qq = 0;
+    for (; qq + 32 <= cd.a_units; qq += 32) {
+      float t[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s += t[i];
+    }
     for (; qq + 8 <= cd.a_units; qq += 8) {
       float t[8];
 #pragma unroll

@@ -289,3 +289,69 @@ def test_many_tokens_multiple_launches():
     sel = np.r_[0:40, 4090:4110, 4980:5000]
     compare_tokens(f64(W), f64(v.to(torch.float32)), f64(X)[sel], 0.05, f64(y)[sel],
                    slow.cpu().numpy()[sel], f64(rho)[sel], torch.float32, what="T=5000")
+
+
+# ------------------------------------------------------ batched (MFMA) path ---
+
+@pytest.mark.parametrize("d,d_out,k,T", [
+    (264, 200, 24, 2),       # smallest batch, ragged shapes, k not a multiple of 16
+    (512, 72, 8, 3),         # k = 8, d_out below one 64-column tile
+    (2048, 1096, 128, 97),   # ragged T and d_out
+    (776, 520, 40, 300),     # T beyond one 256-token pass
+    (256, 136, 256, 33),     # k = d
+])
+def test_batched_ragged(d, d_out, k, T):
+    W = synth.gaussian_weight(d_out, d, (94, d, d_out, k), dtype=torch.bfloat16)
+    extra = min(16, d - k)
+    v, u = synth.orthonormal_frame(d, k, extra, (94, d, k, 1))
+    if extra == 0:
+        u = torch.zeros((d, 1), dtype=torch.float64)
+    mask = torch.zeros(T, dtype=torch.bool)
+    if extra:
+        mask[1::3] = True
+    X, _ = synth.tokens(v, u, mask, (94, d, k))
+    X = X.to(torch.bfloat16)
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    for mode in (gsi.GATED, gsi.FORCE_FAST, gsi.FORCE_SLOW):
+        y, rho, slow = gsi.gsi_linear(m, X.to(DEV), 0.05, mode=mode)
+        sync()
+        if mode == gsi.GATED:
+            assert torch.equal(slow.bool().cpu(), mask)
+        compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y), slow.cpu().numpy(), f64(rho),
+                       torch.bfloat16, mode=mode, rho_tol=2e-2, what=f"batched {d},{d_out},{k},T={T},mode={mode}")
+
+
+def test_batched_matches_single_token_calls():
+    """A token's output does not depend on the batch it is in (batch vs. T=1 kernels)."""
+    W, v, u = small_map(d=1024, d_out=640, k=64, seed=9)
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    mask = torch.zeros(40, dtype=torch.bool)
+    mask[::4] = True
+    X, _ = synth.tokens(v, u, mask, (92, 9, 0))
+    Xd = X.to(torch.bfloat16).to(DEV)
+    yb, rb, sb = gsi.gsi_linear(m, Xd, 0.05)
+    ys = torch.cat([gsi.gsi_linear(m, Xd[t:t + 1], 0.05)[0] for t in range(40)])
+    sync()
+    assert torch.equal(sb.bool().cpu(), mask)
+    err = (yb.double() - ys.double()).norm(dim=1) / ys.double().norm(dim=1)
+    assert float(err.max()) < 1e-2
+
+
+def test_batched_many_tokens_multiple_launches():
+    """More tokens than one batched launch takes (4096)."""
+    W = synth.gaussian_weight(96, 128, (95, 0, 0, 0), dtype=torch.bfloat16)
+    v, u = synth.orthonormal_frame(128, 16, 16, (95, 0, 0, 1))
+    mask = torch.zeros(4500, dtype=torch.bool)
+    mask[::9] = True
+    X, _ = synth.tokens(v, u, mask, (95, 0, 0))
+    X = X.to(torch.bfloat16)
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    y, rho, slow = gsi.gsi_linear(m, X.to(DEV), 0.05)
+    sync()
+    assert torch.equal(slow.bool().cpu(), mask)
+    sel = np.r_[0:30, 4080:4110, 4470:4500]
+    compare_tokens(f64(W), f64(V), f64(X)[sel], 0.05, f64(y)[sel], slow.cpu().numpy()[sel],
+                   f64(rho)[sel], torch.bfloat16, what="batched T=4500")
