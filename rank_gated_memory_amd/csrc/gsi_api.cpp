@@ -65,7 +65,7 @@ int cu_count() {
 // bytes of a launch: enough units to fill 256 CUs several times over, each
 // large enough to keep a workgroup streaming.
 #ifndef GSI_PROJ_UNIT_KB
-#define GSI_PROJ_UNIT_KB 512
+#define GSI_PROJ_UNIT_KB 768
 #endif
 #ifndef GSI_APPLY_BLOCKS_PER_CU
 #define GSI_APPLY_BLOCKS_PER_CU 32
