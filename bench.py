@@ -125,12 +125,13 @@ def cpu_baseline(wl, seconds):
             W = mi.W.to("cpu", torch.float64).numpy()
             V = mi.V.to("cpu", torch.float64).numpy()
             host.append((W, V, orc.prepare(W, V), mi.X.to("cpu", torch.float64).numpy()))
-    # time whole steps of the sampled maps until the budget is spent
+    # time whole steps of the sampled maps, in step order (wrapping round the
+    # workload's steps), until the time budget is spent
     t0 = time.perf_counter()
     done = 0
-    while done < wl["steps"]:
+    while True:
         for W, V, M, X in host:
-            orc.linear_token(W, V, M, X[done], 0.05)
+            orc.linear_token(W, V, M, X[done % wl["steps"]], 0.05)
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -138,8 +139,9 @@ def cpu_baseline(wl, seconds):
     maps_total = sum(len(r) for r in wl["data"])
     per_step = el / done * (maps_total / len(host))
     return {"value": 1.0 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} decode steps of {len(host)} of {maps_total} maps (layers {pick}), "
-                      f"fp64 numpy, {el:.1f}s; step time scaled by {maps_total}/{len(host)} maps"}
+            "sample": f"{done} decode steps (of the workload's {wl['steps']}, in order, wrapping) "
+                      f"through {len(host)} of {maps_total} maps (layers {pick}), fp64 numpy, "
+                      f"{el:.1f}s; step time scaled by {maps_total}/{len(host)} maps"}
 
 
 def kernel_source_sha() -> str:
