@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/gsi.h"
+#include "gsi_batched.h"
 #include "gsi_internal.h"
 
 namespace gsi {
@@ -206,6 +207,8 @@ static gsi_status linear_batched(const gsi_map *map, const void *x, void *y, int
     a.glo = reinterpret_cast<uint16_t *>(w + b.glo_off);
     a.flags = reinterpret_cast<int32_t *>(w + b.flags_off);
     a.zeros = w + b.zeros_off;
+    a.ctl = reinterpret_cast<int32_t *>(w + b.ctl_off);
+    a.list = reinterpret_cast<int32_t *>(w + b.list_off);
     if (launch_batched(a, st) != hipSuccess) return GSI_E_HIP;
   }
   return GSI_OK;

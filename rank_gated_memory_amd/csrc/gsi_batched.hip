@@ -28,7 +28,7 @@
 
 #include <cfloat>
 
-#include "gsi_internal.h"
+#include "gsi_batched.h"
 
 namespace gsi {
 
@@ -58,6 +58,14 @@ __device__ __forceinline__ float wsum(float v) {
   return v;
 }
 
+// Keeps the compiler from moving LDS accesses across this point; the LDS
+// accesses of one wavefront complete in order, so this suffices between a
+// wavefront's writes to its own region and its reads of them.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ float rho_of(float xx, float gg) {
   if (!(xx <= FLT_MAX) || !(gg <= FLT_MAX)) return __builtin_nanf("");
   if (xx == 0.f) return 0.f;
@@ -67,10 +75,58 @@ __device__ __forceinline__ float rho_of(float xx, float gg) {
 
 }  // namespace
 
+namespace {
+
+__device__ __forceinline__ void store_flag(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_flag(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Hands this workgroup's agent-coherent stores over to whichever workgroup
+// arrives last at counter c (of `expect` arrivals); returns true in that one,
+// which also puts the counter back to 0 for the next launch.
+__device__ __forceinline__ bool arrive_last(int32_t *c, int expect, int *s_last) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = prev == expect - 1;
+    if (*s_last) *c = 0;
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
+
+// Inclusive workgroup scan of two counters at once (Hillis-Steele in LDS).
+__device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kBlock; off <<= 1) {
+    const int2 u = tid >= off ? sh[tid - off] : make_int2(0, 0);
+    __syncthreads();
+    sh[tid].x += u.x;
+    sh[tid].y += u.y;
+    __syncthreads();
+  }
+  return sh[tid];
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
-// G partials: tile of 64 tokens x 64 columns of g over the rows [i0, i1) of V_k.
+// G partials: tile of 64 tokens x 64 columns of g over the rows [i0, i1) of
+// V_k (v_mfma_f32_16x16x32_bf16, the V_k chunk transposed in LDS).  Every
+// load of the tile is issued before the first is used (x fragments, then the
+// V_k chunk), so the workgroup waits for memory about once.  Partials
+// [splits][n][k] and ||x||^2 partials [splits][n] are summed by the gate
+// kernel after the launch boundary.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
+  constexpr int KS = kBatchKc / 32;                         // k-steps of 32 rows per split
+  constexpr int VL = kBatchKc * 8 / kBlock;                 // 16-byte pieces of V per thread
   __shared__ __align__(16) uint16_t Vt[64][kBatchKc + 8];  // V chunk transposed: [col][row]
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -81,41 +137,60 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
   const int rows = min(a.kc, a.d - i0);
   const uint16_t *V = static_cast<const uint16_t *>(a.V);
   const uint16_t *X = static_cast<const uint16_t *>(a.x);
+  // one zero piece per lane: with a uniform fallback address the compiler
+  // turns the address select into a branch around the load
+  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
 
-  // stage V[i0 + r][j0 + c] as Vt[c][r] (zero outside the map)
-  for (int v = tid; v < kBatchKc * 8; v += kBlock) {
-    const int r = v >> 3, cg = v & 7;
-    const int j = j0 + cg * 8;
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows && j < a.k) u = *reinterpret_cast<const uint4 *>(V + (size_t)(i0 + r) * a.k + j);
-    const uint16_t *h = reinterpret_cast<const uint16_t *>(&u);
+  const int tok = t0 + wave * 16 + (lane & 15);
+  const bool tok_ok = tok < a.n;
+  const int kq = 8 * (lane >> 4);
+  u32x4_t xv[KS];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Vt[cg * 8 + e][r] = h[e];
+  for (int q = 0; q < KS; ++q) {
+    const int kk = q * 32 + kq;
+    const bool ok = tok_ok && kk < rows;
+    xv[q] = *(ok ? reinterpret_cast<const u32x4_t *>(X + (size_t)tok * a.d + i0 + kk) : zero);
+  }
+  u32x4_t vv[VL];
+#pragma unroll
+  for (int q = 0; q < VL; ++q) {
+    const int v = tid + q * kBlock;
+    const int r = v >> 3, j = j0 + (v & 7) * 8;
+    const bool ok = r < rows && j < a.k;
+    vv[q] = *(ok ? reinterpret_cast<const u32x4_t *>(V + (size_t)(i0 + r) * a.k + j) : zero);
+  }
+  // stage V[i0 + r][j0 + c] as Vt[c][r] (zero outside the map)
+#pragma unroll
+  for (int q = 0; q < VL; ++q) {
+    const int v = tid + q * kBlock;
+    const int r = v >> 3, cg = v & 7;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Vt[cg * 8 + 2 * e][r] = (uint16_t)(vv[q][e] & 0xffffu);
+      Vt[cg * 8 + 2 * e + 1][r] = (uint16_t)(vv[q][e] >> 16);
+    }
   }
   __syncthreads();
 
   f32x4_t acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int tok = t0 + wave * 16 + (lane & 15);
-  const bool tok_ok = tok < a.n;
-  const int kq = 8 * (lane >> 4);
   float xx = 0.f;
-  for (int kk = 0; kk < rows; kk += 32) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (tok_ok && kk + kq < rows) u = *reinterpret_cast<const uint4 *>(X + (size_t)tok * a.d + i0 + kk + kq);
-    if (blockIdx.y == 0) {
-      const uint16_t *h = reinterpret_cast<const uint16_t *>(&u);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = bf2f(h[e]);
-        xx = fmaf(f, f, xx);
+  for (int q = 0; q < KS; ++q) {
+    if (q * 32 >= rows) break;
+    if (blockIdx.y == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(xv[q][e] << 16), hi = __uint_as_float(xv[q][e] & 0xffff0000u);
+        xx = fmaf(lo, lo, xx);
+        xx = fmaf(hi, hi, xx);
       }
     }
-    const bf16x8_t A = as_bf16x8(u);
+    const bf16x8_t A = as_bf16x8(xv[q]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 b = *reinterpret_cast<const uint4 *>(&Vt[c * 16 + (lane & 15)][kk + kq]);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Vt[c * 16 + (lane & 15)][q * 32 + kq]);
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(b), acc[c], 0, 0, 0);
     }
   }
@@ -138,13 +213,19 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate per token: one workgroup per token; every split partial of a column
-// is requested before any is summed (fixed order), so a token costs one or
-// two memory round trips.
+// Gate per token: one workgroup per token sums the split partials of g in
+// split order (every partial of a column requested before any is summed),
+// writes g as bf16 hi + lo (g = hi + lo to ~2^-16) for the fast GEMM, and
+// forms rho and the gate (GSI-TS §2.2).  The flags travel to the last
+// workgroup to finish the way the batch-1 partials do (agent-scope stores,
+// s_waitcnt 0, barrier, relaxed agent-scope counter); that workgroup writes
+// the per-path token lists and counts the output kernels read.
 // ---------------------------------------------------------------------------
 template <int MODE>
 __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   __shared__ float sh[kWaves];
+  __shared__ int2 scan[kBlock];
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   float gg = 0.f;
@@ -188,9 +269,33 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   if (tid == 0) {
     const float rho = rho_of(xx, ggt);
     const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < a.eps));
-    a.flags[t] = slow;
+    store_flag(a.flags + t, slow);
     if (a.rho) a.rho[t] = rho;
     if (a.slow) a.slow[t] = (uint8_t)slow;
+  }
+  if (!arrive_last(a.ctl, a.n, &s_last)) return;
+
+  // compaction: tokens of each path in increasing order
+  const int per = (a.n + kBlock - 1) / kBlock;
+  const int c0 = tid * per;
+  int fl[kMaxBatch / kBlock];
+  int2 mine = make_int2(0, 0);
+#pragma unroll
+  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+    fl[i] = (i < per && c0 + i < a.n) ? load_flag(a.flags + c0 + i) : -1;
+    mine.x += fl[i] == 0;
+    mine.y += fl[i] == 1;
+  }
+  const int2 inc = block_scan2(mine, scan);
+  int wf = inc.x - mine.x, ws = inc.y - mine.y;
+#pragma unroll
+  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+    if (fl[i] == 1) a.list[a.n + ws++] = c0 + i;
+    if (fl[i] == 0) a.list[wf++] = c0 + i;
+  }
+  if (tid == kBlock - 1) {
+    a.ctl[1] = inc.x;
+    a.ctl[2] = inc.y;
   }
 }
 
@@ -204,13 +309,16 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 // the B chunk and every wavefront its own token rows of the A chunk two
 // chunks ahead into registers; the B chunk goes through a double-buffered
 // LDS tile shared by the four wavefronts.  One workgroup per CU streams its
-// 64 rows of W (or M) exactly once per 256 tokens.
+// 64 rows of W (or M) exactly once per 256 tokens.  The A chunk is loaded
+// row-contiguously (eight lanes per 128-byte token row) and transposed
+// through the wavefront's own LDS region, since loading it in operand layout
+// would touch a different token row, and cache line, in every lane.
 // ---------------------------------------------------------------------------
 template <int PATH>
 struct OutStage {
   static constexpr int NA = PATH == 0 ? 2 : 1;  // A matrices: (hi, lo) or (x)
   u32x4_t b0, b1;                               // this thread's two 16-byte pieces of B
-  u32x4_t a[NA][2][4];                          // [matrix][m subtile][k step]
+  u32x4_t a[NA][8];                             // piece i * 64 + lane of the 64 x 128-byte A chunk
 };
 
 // Address of the 16-byte piece v (0..511) of the B chunk at K offset kk0.
@@ -237,34 +345,34 @@ __device__ __forceinline__ const u32x4_t *out_b_ptr(const BArgs &a, int kk0, int
 // prefetched load in flight.
 template <int PATH>
 __device__ __forceinline__ void out_load(OutStage<PATH> &st, const BArgs &a, int kk0, int o0,
-                                         const int (&tokr)[2]) {
+                                         const int (&tk)[8], const u32x4_t *zero) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros);
   st.b0 = *out_b_ptr<PATH>(a, kk0, o0, tid, zero);
   st.b1 = *out_b_ptr<PATH>(a, kk0, o0, tid + kBlock, zero);
-  const int K = PATH == 0 ? a.kpad : a.d;
-  const int kq = 8 * (lane >> 5);
+  const int K = PATH == 0 ? a.k : a.d;
+  const int kg = kk0 + (lane & 7) * 8;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kg = kk0 + ks * 16 + kq;
-      const bool ok = tokr[m] >= 0 && kg < K;
-      if (PATH == 0) {
-        const size_t off = (size_t)tokr[m] * a.kpad + kg;
-        st.a[0][m][ks] = *(ok ? reinterpret_cast<const u32x4_t *>(a.ghi + off) : zero);
-        st.a[OutStage<PATH>::NA - 1][m][ks] = *(ok ? reinterpret_cast<const u32x4_t *>(a.glo + off) : zero);
-      } else {
-        const size_t off = (size_t)tokr[m] * a.d + kg;
-        st.a[0][m][ks] =
-            *(ok ? reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) + off) : zero);
-      }
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = tk[i] >= 0 && kg < K;
+    if (PATH == 0) {
+      const size_t off = (size_t)tk[i] * a.kpad + kg;
+      st.a[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.ghi + off) : zero);
+      st.a[OutStage<PATH>::NA - 1][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.glo + off) : zero);
+    } else {
+      const size_t off = (size_t)tk[i] * a.d + kg;
+      st.a[0][i] =
+          *(ok ? reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) + off) : zero);
     }
+  }
 }
 
+// The wavefront's A region: 64 token rows of 8 pieces, padded to 9 so that
+// the 16 rows read by a quarter-wave fall in different banks.
+constexpr int kOutArow = 9;
+
 template <int PATH>
-__device__ __forceinline__ void out_store_b(const OutStage<PATH> &st, u32x4_t (*Bs)[64]) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void out_store(const OutStage<PATH> &st, u32x4_t (*Bs)[64], u32x4_t *As) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int v1 = tid + kBlock;
   if (PATH == 0) {
     Bs[tid >> 6][tid & 63] = st.b0;
@@ -273,11 +381,15 @@ __device__ __forceinline__ void out_store_b(const OutStage<PATH> &st, u32x4_t (*
     Bs[tid & 7][tid >> 3] = st.b0;
     Bs[v1 & 7][v1 >> 3] = st.b1;
   }
+  wave_lds_fence();  // the previous chunk's reads of As are done
+#pragma unroll
+  for (int q = 0; q < OutStage<PATH>::NA; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) As[(q * 64 + i * 8 + (lane >> 3)) * kOutArow + (lane & 7)] = st.a[q][i];
 }
 
 template <int PATH>
-__device__ __forceinline__ void out_mma(const OutStage<PATH> &st, const u32x4_t (*Bs)[64],
-                                        f32x16_t (&acc)[2][2]) {
+__device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *As, f32x16_t (&acc)[2][2]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -287,56 +399,46 @@ __device__ __forceinline__ void out_mma(const OutStage<PATH> &st, const u32x4_t 
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int q = 0; q < OutStage<PATH>::NA; ++q) {
-        const bf16x8_t A = as_bf16x8(st.a[q][m][ks]);
+        const bf16x8_t A = as_bf16x8(As[(q * 64 + m * 32 + (lane & 31)) * kOutArow + ks * 2 + (lane >> 5)]);
         acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b0, acc[m][0], 0, 0, 0);
         acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b1, acc[m][1], 0, 0, 0);
       }
   }
 }
 
+// LDS of the wide kernel, sized for the fast path (two A matrices).
+struct OutLds {
+  u32x4_t Bs[2][8][64];                  // double-buffered 64-wide K chunk: [k group][column]
+  u32x4_t As[kWaves][2 * 64 * kOutArow];  // each wavefront's A chunk
+  int16_t idx[kMaxBatch];                // tokens of the path
+};
+
 template <int PATH>
-__global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
-  __shared__ __align__(16) u32x4_t Bs[2][8][64];  // double-buffered 64-wide K chunk: [k group][column]
-  __shared__ int16_t idx[kMaxBatch];
-  __shared__ int scan[kBlock];
+__device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L) {
+  auto &Bs = L.Bs;
+  auto &As = L.As;
+  auto &idx = L.idx;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int o0 = blockIdx.x * 64;
-  const int n = a.n;
-
-  // tokens of this path in increasing order
-  const int per = (n + kBlock - 1) / kBlock;
-  const int c0 = tid * per;
-  int mine = 0;
-  for (int i = 0; i < per; ++i)
-    if (c0 + i < n && a.flags[c0 + i] == PATH) ++mine;
-  scan[tid] = mine;
+  const int count = a.ctl[1 + PATH];
+  if (count <= kThin) return;  // none, or few enough for bthin_kernel
+  for (int i = tid; i < count; i += kBlock) idx[i] = (int16_t)a.list[PATH * a.n + i];
   __syncthreads();
-  for (int off = 1; off < kBlock; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  {
-    int w = scan[tid] - mine;
-    for (int i = 0; i < per; ++i)
-      if (c0 + i < n && a.flags[c0 + i] == PATH) idx[w++] = (int16_t)(c0 + i);
-  }
-  const int count = scan[kBlock - 1];
-  __syncthreads();
-  if (count == 0) return;
+  // one zero piece per lane (a uniform fallback address becomes a branch)
+  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
 
   const int K = PATH == 0 ? a.kpad : a.d;
   const int nch = (K + 63) / 64;
+  const int nch3 = nch - nch % 3;
   uint16_t *Y = static_cast<uint16_t *>(a.y);
 
   for (int base = 0; base < count; base += 256) {
-    int tokr[2];
+    int tk[8];  // token of each of this lane's A pieces
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int row = base + wave * 64 + m * 32 + (lane & 31);
-      tokr[m] = row < count ? idx[row] : -1;
+    for (int i = 0; i < 8; ++i) {
+      const int row = base + wave * 64 + i * 8 + (lane >> 3);
+      tk[i] = row < count ? idx[row] : -1;
     }
     f32x16_t acc[2][2];
 #pragma unroll
@@ -347,23 +449,28 @@ __global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
         for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.f;
 
     // Three named stages (an array of stages would live in scratch memory):
-    // chunk i is consumed while chunks i+1 and i+2 load.  The loop is
-    // branch-free and runs a multiple of three chunks; chunks past K read the
-    // zero block and wavefronts without tokens multiply zeros.
+    // chunk i is consumed while chunks i+1 and i+2 load.  The main loop is
+    // branch-free and runs a multiple of three chunks, the last one or two
+    // chunks follow it; loads past K read the zero block and wavefronts
+    // without tokens multiply zeros.
     OutStage<PATH> s0, s1, s2;
-#define GSI_OUT_STEP(cur, ahead, i)                       \
-  do {                                                    \
-    out_load<PATH>(ahead, a, ((i) + 2) * 64, o0, tokr);   \
-    out_store_b<PATH>(cur, Bs[(i) & 1]);                  \
-    __syncthreads();                                      \
-    out_mma<PATH>(cur, Bs[(i) & 1], acc);                 \
+#define GSI_OUT_STEP(cur, ahead, i)                        \
+  do {                                                     \
+    out_load<PATH>(ahead, a, ((i) + 2) * 64, o0, tk, zero); \
+    out_store<PATH>(cur, Bs[(i) & 1], As[wave]);           \
+    __syncthreads();                                       \
+    out_mma<PATH>(Bs[(i) & 1], As[wave], acc);             \
   } while (0)
-    out_load<PATH>(s0, a, 0, o0, tokr);
-    out_load<PATH>(s1, a, 64, o0, tokr);
-    for (int i = 0; i < nch; i += 3) {
+    out_load<PATH>(s0, a, 0, o0, tk, zero);
+    out_load<PATH>(s1, a, 64, o0, tk, zero);
+    for (int i = 0; i < nch3; i += 3) {
       GSI_OUT_STEP(s0, s2, i);
       GSI_OUT_STEP(s1, s0, i + 1);
       GSI_OUT_STEP(s2, s1, i + 2);
+    }
+    if (nch3 < nch) {
+      GSI_OUT_STEP(s0, s2, nch3);
+      if (nch3 + 1 < nch) GSI_OUT_STEP(s1, s0, nch3 + 1);
     }
 #undef GSI_OUT_STEP
     __syncthreads();
@@ -378,6 +485,193 @@ __global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
           if (row < count && col < a.d_out) Y[(size_t)idx[row] * a.d_out + col] = f2bf(acc[m][c][i]);
         }
   }
+}
+
+// Both paths in one launch (blockIdx.y = path): a kernel boundary costs
+// microseconds even when the kernel has nothing to do.
+__global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
+  __shared__ __align__(16) OutLds L;
+  if (blockIdx.y == 0)
+    bout_path<0>(a, L);
+  else
+    bout_path<1>(a, L);
+}
+
+// ---------------------------------------------------------------------------
+// Outputs of a path with at most kThin tokens: streaming the matrix by rows.
+//
+// With few tokens the output GEMM is a stream of W (slow) or M (fast) and is
+// bound by HBM.  A workgroup owns 16 output rows; its four wavefronts take a
+// quarter of K each and meet in LDS at the end, so there is no barrier in the
+// K loop.  v_mfma_f32_16x16x32_bf16 with A = 16 matrix rows and B = 16 tokens
+// (kThin tokens are two B groups).
+//
+// In the MFMA operand layout the 16 lanes of a quarter-wave hold 16 different
+// rows, so loading W rows or token rows in that layout touches 16 cache lines
+// per quarter-wave and the address unit, not HBM, sets the pace.  Each
+// wavefront therefore loads a stage (4 k-steps = 128 columns of K) with
+// row-contiguous 16-byte pieces (16 lanes cover 256 bytes of one row), writes
+// it to its own LDS region and reads it back in operand layout.  The image M
+// is stored in operand order already (64 rows x 16 bytes contiguous) and is
+// read directly.  One stage is in flight in registers while the previous one
+// goes through LDS and the matrix cores.
+// ---------------------------------------------------------------------------
+template <int PATH>
+struct ThinStage {
+  static constexpr int NB = PATH == 0 ? 2 : 1;  // B matrices: (g hi, g lo) or (x)
+  u32x4_t A[4];      // slow: piece i * 64 + lane of the 16 x 256-byte W tile; fast: k-step i of M
+  u32x4_t B[NB][8];  // piece i * 64 + lane of the 32 x 256-byte token tile
+};
+
+template <int PATH>
+struct ThinLds {
+  static constexpr int NB = ThinStage<PATH>::NB;
+  static constexpr int kRowA = PATH == 1 ? 16 : 0;
+  // pieces of 16 bytes, rows padded by one piece so that the 16 rows read by a
+  // quarter-wave fall in different banks
+  static constexpr int kA = kRowA * 17;
+  static constexpr int kPieces = kA + NB * 32 * 17;
+};
+
+template <int PATH>
+__device__ __forceinline__ void thin_load(ThinStage<PATH> &st, const BArgs &a, int step0, int kend,
+                                          int r0, const int (&tk)[8], const u32x4_t *zero) {
+  const int lane = threadIdx.x & 63;
+  if (PATH == 0) {
+    const int q = lane >> 4, row = r0 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kg = (step0 + j) * 32 + 8 * q;
+      const bool ok = kg < kend && row < a.d_out;
+      const u32x4_t *p = static_cast<const u32x4_t *>(a.M) +
+                         ((size_t)(row / 64) * (a.k / 8) + kg / 8) * 64 + (row & 63);
+      st.A[j] = *(ok ? p : zero);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = i * 64 + lane;
+      const int row = r0 + (pc >> 4), kg = step0 * 32 + (pc & 15) * 8;
+      const bool ok = kg < kend && row < a.d_out;
+      const u32x4_t *p =
+          reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.W) + (size_t)row * a.d + kg);
+      st.A[i] = *(ok ? p : zero);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tok = tk[i], kg = step0 * 32 + (lane & 15) * 8;
+    const bool ok = kg < kend && tok >= 0;
+    if (PATH == 0) {
+      const size_t off = (size_t)tok * a.kpad + kg;
+      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.ghi + off) : zero);
+      st.B[ThinStage<PATH>::NB - 1][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.glo + off) : zero);
+    } else {
+      const size_t off = (size_t)tok * a.d + kg;
+      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) + off) : zero);
+    }
+  }
+}
+
+template <int PATH>
+__device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t *lds, f32x4_t (&acc)[2]) {
+  constexpr int NB = ThinStage<PATH>::NB;
+  constexpr int kA = ThinLds<PATH>::kA;
+  const int lane = threadIdx.x & 63;
+  wave_lds_fence();  // the previous stage's reads are done before it is overwritten
+  if (PATH == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = i * 64 + lane;
+      lds[(pc >> 4) * 17 + (pc & 15)] = st.A[i];
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = i * 64 + lane;
+      lds[kA + b * 32 * 17 + (pc >> 4) * 17 + (pc & 15)] = st.B[b][i];
+    }
+  wave_lds_fence();
+  const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t A = PATH == 1 ? lds[r * 17 + 4 * j + q] : st.A[j];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t B = lds[kA + b * 32 * 17 + (16 * g + r) * 17 + 4 * j + q];
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(B), acc[g], 0, 0, 0);
+      }
+  }
+}
+
+constexpr int kThinPieces = ThinLds<0>::kPieces > ThinLds<1>::kPieces ? ThinLds<0>::kPieces : ThinLds<1>::kPieces;
+static_assert(kThinPieces * 16 >= 2 * 4 * 64 * 4, "the final sums reuse a wavefront's region");
+
+template <int PATH>
+__device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], int *toks) {
+  const int count = a.ctl[1 + PATH];
+  if (count == 0 || count > kThin) return;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r0 = blockIdx.x * 16;
+  if (tid < kThin) toks[tid] = tid < count ? a.list[PATH * a.n + tid] : -1;
+  __syncthreads();
+  // one zero piece per lane (a uniform fallback address becomes a branch)
+  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
+  const int K = PATH == 0 ? a.kpad : a.d;
+  const int steps = (K + 31) / 32;  // k-steps of 32
+  const int per = (steps + kWaves - 1) / kWaves;
+  const int s0 = wave * per;
+  const int s_end = min(steps, s0 + per);
+  const int kend = min(s_end * 32, PATH == 0 ? a.k : a.d);  // this wavefront's K ends here
+
+  int tk[8];  // token of each of this lane's 16-byte pieces of the token tile
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tk[i] = toks[(i * 64 + lane) >> 4];
+
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  ThinStage<PATH> sa, sb;
+  thin_load<PATH>(sa, a, s0, kend, r0, tk, zero);
+  for (int st = s0; st < s_end; st += 8) {
+    thin_load<PATH>(sb, a, st + 4, kend, r0, tk, zero);
+    thin_consume<PATH>(sa, lds[wave], acc);
+    thin_load<PATH>(sa, a, st + 8, kend, r0, tk, zero);
+    thin_consume<PATH>(sb, lds[wave], acc);
+  }
+  // partial sums of the four K quarters, through each wavefront's own region
+  wave_lds_fence();
+  float *red = reinterpret_cast<float *>(lds[wave]);
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(g * 4 + i) * 64 + lane] = acc[g][i];
+  __syncthreads();
+  uint16_t *Y = static_cast<uint16_t *>(a.y);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = tid + h * kBlock;  // (group, element, lane)
+    const int g = e >> 8, i = (e >> 6) & 3, l = e & 63;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float *>(lds[w])[(g * 4 + i) * 64 + l];
+    const int t = toks[g * 16 + (l & 15)];
+    const int r = r0 + 4 * (l >> 4) + i;
+    if (t >= 0 && r < a.d_out) Y[(size_t)t * a.d_out + r] = f2bf(v);
+  }
+}
+
+// Both paths in one launch (blockIdx.y = path).
+__global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
+  __shared__ u32x4_t lds[kWaves][kThinPieces];
+  __shared__ int toks[kThin];
+  if (blockIdx.y == 0)
+    bthin_path<0>(a, lds, toks);
+  else
+    bthin_path<1>(a, lds, toks);
 }
 
 // ---------------------------------------------------------------------------
@@ -453,9 +747,11 @@ hipError_t launch_batched(const BArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(bgate_kernel<2>, gg, dim3(kBlock), 0, s, a);
   else
     hipLaunchKernelGGL(bgate_kernel<0>, gg, dim3(kBlock), 0, s, a);
-  const dim3 go((a.d_out + 63) / 64);
-  hipLaunchKernelGGL((bout_kernel<0>), go, dim3(kBlock), 0, s, a);
-  hipLaunchKernelGGL((bout_kernel<1>), go, dim3(kBlock), 0, s, a);
+  // Each path has a wide kernel (more than kThin tokens) and a row-streaming
+  // one (at most kThin); the one that does not apply returns at once.
+  // One launch holds the wide kernels of both paths, one the row-streaming ones.
+  hipLaunchKernelGGL(bout_kernel, dim3((a.d_out + 63) / 64, 2), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(bthin_kernel, dim3((a.d_out + 15) / 16, 2), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

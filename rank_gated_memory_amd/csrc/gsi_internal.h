@@ -98,66 +98,6 @@ struct KArgs {
   float *wsf;
 };
 
-// ---- batched bf16 path (many tokens through one map) ----
-constexpr int kBatchKc = 256;   // rows of V_k per split of the projection GEMM (multiple of 32)
-constexpr int kMaxBatch = 4096; // tokens per batched launch (compaction list in LDS)
-
-struct BArgs {
-  const void *W, *V, *M, *x;
-  void *y;
-  float *rho;
-  uint8_t *slow;
-  int32_t n, d, d_out, k;
-  int32_t kpad;    // k rounded up to 16 (MFMA K granularity)
-  int32_t kc;      // rows of V_k per split
-  int32_t splits;  // number of splits
-  int32_t mode;
-  float eps;
-  int32_t pad_;
-  float *part;     // [splits][n][k] partial g
-  float *xxp;      // [splits][n] partial ||x||^2
-  uint16_t *ghi;   // [n][kpad] bf16(g)
-  uint16_t *glo;   // [n][kpad] bf16(g - hi)
-  int32_t *flags;  // [n] 1 = slow
-  const void *zeros;  // 256 bytes of the workspace that stay zero
-};
-
-struct BatchShape {
-  int32_t kpad, kc, splits;
-  uint64_t zeros_off, part_off, xxp_off, ghi_off, glo_off, flags_off, total;
-};
-
-inline BatchShape batch_shape(int n, int d, int k) {
-  BatchShape b{};
-  b.kpad = (k + 15) / 16 * 16;
-  const int tiles = ((n + 63) / 64) * ((k + 63) / 64);
-  int s = (d + kBatchKc - 1) / kBatchKc;
-  const int want = (512 + tiles - 1) / tiles;
-  if (want > s) s = want;
-  const int smax = (d + 31) / 32;
-  if (s > smax) s = smax;
-  int kc = (d + s - 1) / s;
-  kc = (kc + 31) / 32 * 32;
-  if (kc > kBatchKc) kc = kBatchKc;
-  b.kc = kc;
-  b.splits = (d + kc - 1) / kc;
-  uint64_t off = 0;
-  b.zeros_off = off;  // never written: zero since the caller zero-filled the workspace
-  off += 256;
-  b.part_off = off;
-  off = align_up(off + (uint64_t)b.splits * n * k * 4, 256);
-  b.xxp_off = off;
-  off = align_up(off + (uint64_t)b.splits * n * 4, 256);
-  b.ghi_off = off;
-  off = align_up(off + (uint64_t)n * b.kpad * 2, 256);
-  b.glo_off = off;
-  off = align_up(off + (uint64_t)n * b.kpad * 2, 256);
-  b.flags_off = off;
-  off = align_up(off + (uint64_t)n * 4, 256);
-  b.total = off;
-  return b;
-}
-
 // Unit sizing shared by the stack plan and the single-map path.
 struct UnitShape {
   int32_t a_units, a_rows, fast_units, fast_tiles, slow_units, slow_rows;

@@ -355,3 +355,25 @@ def test_batched_many_tokens_multiple_launches():
     sel = np.r_[0:30, 4080:4110, 4470:4500]
     compare_tokens(f64(W), f64(V), f64(X)[sel], 0.05, f64(y)[sel], slow.cpu().numpy()[sel],
                    f64(rho)[sel], torch.bfloat16, what="batched T=4500")
+
+
+@pytest.mark.parametrize("T,n_slow", [(65, 32), (65, 33), (33, 0), (33, 33), (32, 32), (1, 1)])
+def test_batched_thin_and_wide_kernels(T, n_slow):
+    """A path with at most 32 tokens streams its matrix by rows, a larger one
+    runs the wide kernel: both sides of that boundary, for both paths, with
+    d_out not a multiple of 16 and k not a multiple of 32."""
+    d, d_out, k = 1024, 200, 40
+    W = synth.gaussian_weight(d_out, d, (97, T, n_slow, 0), dtype=torch.bfloat16)
+    v, u = synth.orthonormal_frame(d, k, 16, (97, T, n_slow, 1))
+    g = torch.Generator().manual_seed(97 * T + n_slow)
+    mask = torch.zeros(T, dtype=torch.bool)
+    mask[torch.randperm(T, generator=g)[:n_slow]] = True
+    X, _ = synth.tokens(v, u, mask, (97, T, n_slow))
+    X = X.to(torch.bfloat16)
+    V = v.to(torch.bfloat16)
+    m = new_map(W, V)
+    y, rho, slow = gsi.gsi_linear(m, X.to(DEV), 0.05)
+    sync()
+    assert torch.equal(slow.bool().cpu(), mask)
+    compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y), slow.cpu().numpy(), f64(rho),
+                   torch.bfloat16, rho_tol=2e-2, what=f"batched T={T} slow={n_slow}")
