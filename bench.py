@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=512)
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default="gptj6b-28L",
-                   choices=["gptj6b-28L", "llama13b-40L", "batched-t256"])
+                   choices=["gptj6b-28L", "llama13b-40L", "batched-t256", "sweep"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -225,6 +225,102 @@ def bench_batched(args):
     }), flush=True)
 
 
+def bench_sweep(args):
+    """Operating points: basis size k, threshold eps and the forced modes on spectral tokens.
+
+    GPT-J-shaped maps (28 layers by default) whose tokens have a power-law
+    spectrum, so that the fast share follows from k and eps.  For each k
+    (fc_out takes 2k, as in the GPT-J shapes) and each of gated eps = 0.05,
+    gated eps = 0.10, static projection (every token fast) and dense (every
+    token slow), one batch-1 decode pass over the workload's steps through
+    gsi_stack: fast share, algorithmic bytes and GB/s, tokens/s, parameters
+    read per token, and the output error against the dense outputs.
+    """
+    import numpy as np
+    import torch
+
+    from rank_gated_memory_amd import accounting as acc
+    from rank_gated_memory_amd import gsi, synth
+
+    dev = torch.device("cuda:0")
+    layers = args.layers or 28
+    steps = 128
+    t0 = time.perf_counter()
+    data = synth.sweep_config(layers, steps, device=dev)
+    torch.cuda.synchronize()
+    log(f"sweep inputs drawn in {time.perf_counter() - t0:.1f}s")
+    params = sum(e["d"] * e["d_out"] for row in data for e in row)
+    cells = []
+    for kk in (128, 256):
+        ks = [[2 * kk if e["name"] == "fc_out" else kk for e in row] for row in data]
+        maps = [[gsi.Map(e["W"], e["V64"][:, :k].to(torch.bfloat16).contiguous()) for e, k in zip(row, krow)]
+                for row, krow in zip(data, ks)]
+        for row in maps:
+            for m in row:
+                gsi.gsi_prepare(m)
+        outs = [[(torch.empty((steps, e["d_out"]), dtype=torch.bfloat16, device=dev),
+                  torch.empty(steps, dtype=torch.float32, device=dev),
+                  torch.zeros(steps, dtype=torch.uint8, device=dev)) for e in row] for row in data]
+        flat = [(e, m, o, k) for row, mrow, orow, krow in zip(data, maps, outs, ks)
+                for e, m, o, k in zip(row, mrow, orow, krow)]
+
+        def plans_for(eps):
+            return [gsi.Stack([(m, e["X"][s], Y[s], eps, R[s:s + 1], S[s:s + 1])
+                               for e, m, (Y, R, S), _ in flat], device=dev) for s in range(steps)]
+
+        plans = {0.05: plans_for(0.05), 0.10: plans_for(0.10)}
+        ws = gsi.workspace(max(p.ws_bytes for p in plans[0.05]), dev)
+
+        def run(mode, eps):
+            for i in range(4):
+                gsi.gsi_stack(plans[eps][i], mode, ws)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(steps):
+                gsi.gsi_stack(plans[eps][i], mode, ws)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t
+
+        run(gsi.FORCE_SLOW, 0.05)
+        dense_y = [Y.clone() for _, _, (Y, _, _), _ in flat]
+        for label, mode, eps in (("gated", gsi.GATED, 0.05), ("gated", gsi.GATED, 0.10),
+                                 ("static projection", gsi.FORCE_FAST, 0.05),
+                                 ("dense", gsi.FORCE_SLOW, 0.05)):
+            wall = run(mode, eps)
+            slow = torch.stack([S for _, _, (_, _, S), _ in flat], dim=1).cpu().numpy().astype(bool)
+            byts = sum(acc.token_bytes(e["d"], e["d_out"], k, 2, bool(slow[s, j]))
+                       for s in range(steps) for j, (e, _, _, k) in enumerate(flat))
+            read = sum((e["d"] * k + (e["d_out"] * e["d"] if slow[s, j] else e["d_out"] * k))
+                       for s in range(steps) for j, (e, _, _, k) in enumerate(flat)) / steps
+            errs = []
+            for (_, _, (Y, _, _), _), Yd in zip(flat, dense_y):
+                yd = Yd.float()
+                errs.append(((Y.float() - yd).norm(dim=1) / yd.norm(dim=1)).cpu())
+            err = torch.cat(errs).numpy()
+            cell = {"k": kk, "k_fc_out": 2 * kk, "mode": label, "eps": eps if mode == gsi.GATED else None,
+                    "fast_share": float(1.0 - slow.mean()), "tokens_per_s": steps / wall,
+                    "us_per_step": wall / steps * 1e6, "gbytes_per_step": byts / steps / 1e9,
+                    "gbps": byts / wall / 1e9, "params_read_per_token_M": read / 1e6,
+                    "params_k_over_d_M": params * kk / 4096 / 1e6,
+                    "rel_err_vs_dense_mean": float(err.mean()), "rel_err_vs_dense_p99": float(np.quantile(err, 0.99)),
+                    "rel_err_vs_dense_max": float(err.max())}
+            cells.append(cell)
+            log(f"k={kk} {label} eps={cell['eps']}: fast {cell['fast_share']:.3f}, {cell['tokens_per_s']:.0f} tok/s, "
+                f"{cell['gbps']:.0f} GB/s, err mean {cell['rel_err_vs_dense_mean']:.2e} max {cell['rel_err_vs_dense_max']:.2e}")
+        del maps, outs, flat, plans, ws, dense_y
+        torch.cuda.empty_cache()
+    head = [c for c in cells if c["k"] == 256 and c["mode"] == "gated" and c["eps"] == 0.05][0]
+    print(json.dumps({
+        "metric": "GSI operating points: tokens/s at batch 1 vs fast share, bytes and error",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 4,
+        "ms_per_step": head["us_per_step"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"sweep: {layers} layers x 4 GPT-J-shaped maps, power-law (alpha 1.1) "
+                               f"spectral tokens with 5% outliers, {steps} decode steps; value at k=256, eps=0.05",
+                   "params": params, "cells": cells},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +329,9 @@ def main():
         sys.exit(2)
     if args.workload == "batched-t256":
         bench_batched(args)
+        return
+    if args.workload == "sweep":
+        bench_sweep(args)
         return
     import numpy as np
     import torch

@@ -36,7 +36,7 @@ import torch
 ROOT_SEED = 20260506
 
 # purpose codes (last element of a spawn key)
-P_WEIGHT, P_BASIS, P_Z, P_NOISE, P_RESID, P_RHO, P_PICK, P_CASCADE = range(8)
+P_WEIGHT, P_BASIS, P_Z, P_NOISE, P_RESID, P_RHO, P_PICK, P_CASCADE, P_OUTLIER = range(9)
 
 # Map roles of the two transformer shapes (d -> d_out, k).
 GPTJ_MAPS = (
@@ -167,6 +167,38 @@ def tokens(v: torch.Tensor, u: torch.Tensor, slow_mask: torch.Tensor, key,
     return x, rho_built
 
 
+def spectral_tokens(v: torch.Tensor, u: torch.Tensor, n: int, key, alpha: float = 1.1,
+                    outlier_rate: float = 0.05, outlier_scale=(4.0, 10.0)):
+    """fp64 tokens [n][d] whose energy along the directions [v | u] decays as a power law.
+
+    With K = v.shape[1] head directions and m = u.shape[1] tail directions
+    (jointly orthonormal), x = v (s * z) + f u (t * w), z ~ N(0, I_K),
+    w ~ N(0, I_m), where s_i = i^-alpha (i = 1..K) and t_j = s_{K+j} scaled so
+    that the m tail directions carry the whole tail mass sum_{i>K}^{d} s_i^2.
+    f = 1, except for a seeded share of outlier tokens with f ~ U(outlier_scale).
+    A basis made of the first k columns of v then sees a residual ratio that
+    falls as k grows, so the share of fast tokens depends on k and on the
+    threshold instead of being prescribed.  Returns (X, outlier mask).
+    """
+    device = v.device
+    d, K = v.shape
+    m = u.shape[1]
+    i = torch.arange(1, d + 1, dtype=torch.float64, device=device)
+    s = i.pow(-alpha)
+    head = s[:K]
+    tail = s[K:K + m] * torch.sqrt((s[K:] ** 2).sum() / (s[K:K + m] ** 2).sum())
+    gz = generator(device, *tuple(key), P_Z)
+    gw = generator(device, *tuple(key), P_NOISE)
+    go = generator(device, *tuple(key), P_OUTLIER)
+    z = torch.randn((n, K), generator=gz, device=device, dtype=torch.float64) * head
+    w = torch.randn((n, m), generator=gw, device=device, dtype=torch.float64) * tail
+    out = torch.rand(n, generator=go, device=device, dtype=torch.float64) < outlier_rate
+    f = outlier_scale[0] + (outlier_scale[1] - outlier_scale[0]) * torch.rand(
+        n, generator=go, device=device, dtype=torch.float64)
+    w = w * torch.where(out, f, torch.ones_like(f))[:, None]
+    return z @ v.T + w @ u.T, out
+
+
 # --------------------------------------------------------------------------
 # Workload builders.  Each returns plain tensors in the storage dtype; the
 # oracle receives their exact fp64 upcast.
@@ -244,6 +276,30 @@ def stack_config(cfg: int, layers: int, maps, steps: int, slow_rate: float,
                                   keep_fp64=keep_fp64))
             if cascade and not keep_fp64:
                 frames[ridx][layer] = None
+        out.append(row)
+    return out
+
+
+def sweep_config(layers: int = 28, steps: int = 128, head: int = 1024, tail: int = 512,
+                 alpha: float = 1.1, device="cpu"):
+    """Operating-point workload: GPT-J-shaped maps whose tokens have a power-law spectrum.
+
+    Per layer and map role: W, a frame of `head` nested basis directions plus
+    `tail` complement directions, and `steps` spectral tokens.  A basis of
+    size k is the first k columns of the frame (nested in k).  Returns a list
+    over layers of lists over roles of dicts with W, the fp64 frame head V64
+    [d][head] and the tokens X [steps][d] in bf16.
+    """
+    cfg = 6
+    out = []
+    for layer in range(layers):
+        row = []
+        for ridx, (name, d, d_out, k) in enumerate(GPTJ_MAPS):
+            W = gaussian_weight(d_out, d, (cfg, layer, ridx, P_WEIGHT), device, torch.bfloat16)
+            v, u = orthonormal_frame(d, head, tail, (cfg, layer, ridx, P_BASIS), device)
+            x, outl = spectral_tokens(v, u, steps, (cfg, layer, ridx), alpha)
+            row.append({"name": name, "d": d, "d_out": d_out, "k_ref": k, "W": W, "V64": v,
+                        "X": x.to(torch.bfloat16), "outliers": outl})
         out.append(row)
     return out
 

@@ -299,8 +299,29 @@ def pin_norm_identity(orc):
         _close(orc.rho_from_norms(X[t], res["g"][t]), res["rho"][t], 1e-10, 0, "pythagorean rho")
 
 
+def pin_nested_bases(orc):
+    """Growing a basis by more orthonormal columns never raises rho: with
+    nested bases V_1 in V_2 in V_3, rho_3 <= rho_2 <= rho_1 for every token;
+    a token inside span(V_2) has rho_2 = rho_3 = 0, and its rho_1 equals the
+    norm of its coordinates on the columns V_2 adds, over ||x||."""
+    rng = _rng(25)
+    d = 48
+    Q = _orthonormal(rng, d, 24)
+    bases = [Q[:, :6], Q[:, :12], Q[:, :24]]
+    X = rng.standard_normal((6, d))
+    rhos = [[orc.residual_ratio(x, orc.residual(V, x, orc.project(V, x))) for x in X] for V in bases]
+    for a, b in zip(rhos[:-1], rhos[1:]):
+        assert all(rb <= ra + 1e-12 for ra, rb in zip(a, b)), "rho grew with the basis"
+    c = rng.standard_normal(12)
+    x = Q[:, :12] @ c
+    r1 = orc.residual_ratio(x, orc.residual(bases[0], x, orc.project(bases[0], x)))
+    _close(r1, np.linalg.norm(c[6:]) / np.linalg.norm(c), 1e-12, 0, "nested rho_1")
+    for V in bases[1:]:
+        assert orc.residual_ratio(x, orc.residual(V, x, orc.project(V, x))) < 1e-12
+
+
 ALL_PINS = [
     pin_identity_basis, pin_full_rank, pin_in_span_and_orthogonal, pin_construction,
     pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
-    pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity,
+    pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity, pin_nested_bases,
 ]

@@ -377,3 +377,38 @@ def test_batched_thin_and_wide_kernels(T, n_slow):
     assert torch.equal(slow.bool().cpu(), mask)
     compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y), slow.cpu().numpy(), f64(rho),
                    torch.bfloat16, rho_tol=2e-2, what=f"batched T={T} slow={n_slow}")
+
+
+@pytest.mark.parametrize("k", [128, 256])
+@pytest.mark.parametrize("eps", [0.05, 0.10])
+def test_spectral_tokens_operating_points(k, eps):
+    """Power-law spectral tokens (the operating-point workload), nested bases:
+    the gate is decided by the tokens' own residuals, many of them near eps.
+    Batch-1 stack calls and the batched path, against the oracle."""
+    d, d_out, T = 4096, 1000, 48
+    v, u = synth.orthonormal_frame(d, 512, 256, (98, 0, 0, 1))
+    X, _ = synth.spectral_tokens(v, u, T, (98, 0, 0))
+    W = synth.gaussian_weight(d_out, d, (98, 0, 0, 0), dtype=torch.bfloat16)
+    V = v[:, :k].to(torch.bfloat16)
+    Xb = X.to(torch.bfloat16)
+    m = new_map(W, V)
+    Wf, Vf, Xf = f64(W), f64(V), f64(Xb)
+    M = orc.prepare(Wf, Vf)
+    # batched path
+    y, rho, slow = gsi.gsi_linear(m, Xb.to(DEV), eps)
+    sync()
+    compare_tokens(Wf, Vf, Xf, eps, f64(y), slow.cpu().numpy(), f64(rho), torch.bfloat16, M=M,
+                   rho_tol=2e-2, what=f"spectral batched k={k} eps={eps}")
+    # batch-1: one stack of T single-token calls
+    Xd = Xb.to(DEV)
+    ys = torch.empty((T, d_out), dtype=torch.bfloat16, device=DEV)
+    rs = torch.empty(T, dtype=torch.float32, device=DEV)
+    ss = torch.empty(T, dtype=torch.uint8, device=DEV)
+    st = gsi.Stack([(m, Xd[t], ys[t], eps, rs[t:t + 1], ss[t:t + 1]) for t in range(T)], device=DEV)
+    st.run()
+    sync()
+    compare_tokens(Wf, Vf, Xf, eps, f64(ys), ss.cpu().numpy(), f64(rs), torch.bfloat16, M=M,
+                   rho_tol=2e-2, what=f"spectral stack k={k} eps={eps}")
+    share = 1.0 - float(ss.float().mean())
+    print(f"k={k} eps={eps}: fast share {share:.2f}")
+    assert 0.0 < share < 1.0 or eps == 0.10

@@ -57,3 +57,24 @@ def test_cascade_coherence_at_full_width():
         fr = synth.cascade_frames(d, k, 64, 2, (3, 0, 9, synth.P_CASCADE))
         c = synth.mean_principal_cosine(fr[0][0], fr[1][0])
         assert 0.90 < c < 0.99, c
+
+
+def test_spectral_tokens_follow_the_power_law():
+    """Energy of the spectral tokens along the frame: E[(v_i^T x)^2] = i^-2 alpha on
+    the head directions, the tail directions carry the remaining mass, and the
+    outlier share is near the requested rate."""
+    d, K, m, n, alpha = 512, 64, 64, 6000, 1.1
+    v, u = synth.orthonormal_frame(d, K, m, (97, 1, 2, 3))
+    X, out = synth.spectral_tokens(v, u, n, (97, 1, 2), alpha=alpha)
+    assert X.shape == (n, d) and X.dtype == torch.float64
+    assert abs(float(out.double().mean()) - 0.05) < 0.015
+    keep = ~out
+    head = ((X[keep] @ v) ** 2).mean(0)
+    want = torch.arange(1, K + 1, dtype=torch.float64).pow(-2 * alpha)
+    assert torch.allclose(head, want, rtol=0.12)
+    tail = ((X[keep] @ u) ** 2).sum(1).mean()
+    want_tail = torch.arange(K + 1, d + 1, dtype=torch.float64).pow(-2 * alpha).sum()
+    assert abs(float(tail / want_tail) - 1.0) < 0.05
+    # the part outside span([v | u]) is empty
+    resid = X - (X @ v) @ v.T - (X @ u) @ u.T
+    assert float(resid.norm() / X.norm()) < 1e-12
