@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GSI_ABI_VERSION 1
+#define GSI_ABI_VERSION 2
 
 typedef enum {
   GSI_OK = 0,
@@ -80,13 +80,15 @@ typedef struct gsi_map {
 } gsi_map;
 
 /* One batch-1 call of a stack: one token x [d] -> y [d_out] through `map`.
- * rho (one float) and slow (one byte, 1 = slow path taken) may be NULL. */
+ * rho (one float) and slow (one byte, 1 = slow path taken) may be NULL.
+ * wave: calls of a stack run in waves (see gsi_stack); 0 for a stack of
+ * independent calls. */
 typedef struct gsi_call {
   gsi_map map;
   const void *x;
   void *y;
   float eps;
-  int32_t reserved;
+  int32_t wave;
   float *rho;
   uint8_t *slow;
 } gsi_call;
@@ -125,11 +127,21 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
                       int32_t mode, float *rho, uint8_t *slow, void *ws, size_t ws_bytes,
                       void *stream);
 
-/* ---- stacks: many independent batch-1 calls in one pass (GSI-TS §3) ----
+/* ---- stacks: every linear map of a decode step in one launch (GSI-TS §3) ----
  * A stack plan is built once on the host from an array of calls and copied
- * by the caller to device memory; running the plan then needs no host work
- * beyond two kernel launches.  Calls of one stack must share one dtype and
- * must be independent (no call's x may alias another call's y). */
+ * by the caller to device memory; running the plan is one kernel launch.
+ * Calls of one stack share one dtype.
+ *
+ * Waves: calls carry a wave number, nondecreasing along the array.  The
+ * calls of one wave run concurrently and must be independent: no call of a
+ * wave may write bytes that another call of the same wave reads (x) or
+ * writes (y) -- gsi_stack_plan rejects such overlaps with GSI_E_ARG.  A
+ * wave starts only after every call of the previous wave has written its y,
+ * so a call may read as its x the y of any call of an earlier wave (a
+ * dependency-chained stack such as the layers of a decoder: the QKV and
+ * fc_in maps of a GPT-J block in one wave, out and fc_out in the next).
+ * The barriers between waves are kept on the device (no host round trip).
+ * With every wave number equal, all calls are independent. */
 
 /* Bytes of the host plan for these n calls (0 if n < 0 or n > 4096, or if
  * a call is invalid; gsi_stack_plan reports which check failed). */
@@ -146,12 +158,26 @@ size_t gsi_stack_workspace(const void *plan_host);
 
 /* Run every call of a plan: plan_host is the host buffer gsi_stack_plan
  * filled, plan_dev a byte-identical device copy of it.  Same workspace
- * rules as gsi_linear.  Equivalent to gsi_linear(T = 1) on each call. */
+ * rules as gsi_linear.  Equivalent to gsi_linear(T = 1) on each call, in
+ * array order; the results are bitwise identical to the two-phase form
+ * below for the same plan.  One persistent launch: the output work of a
+ * call starts as soon as its own gate is decided, while other calls are
+ * still projecting.
+ * Every device-side wait of the launch is bounded; if a bound ever ran out
+ * (a library fault, never expected) the launch still ends, the outputs of
+ * that run are incomplete and a nonzero code is left in the 32-bit status
+ * word at byte gsi_stack_status_offset(plan_host) of the workspace.  The
+ * word stays set until the caller clears it; other runs leave it alone. */
 gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, void *ws,
                      size_t ws_bytes, void *stream);
 
-/* The two phases of gsi_stack, for callers that interleave other work
- * between them or time them separately.
+/* Byte offset in the workspace of the status word described above (0 if
+ * the plan is invalid or empty). */
+size_t gsi_stack_status_offset(const void *plan_host);
+
+/* The two phases of a stack as two launches, for callers that interleave
+ * other work between them or time them separately.  Only for plans of one
+ * wave (GSI_E_ARG otherwise).
  *   GSI_PHASE_PROJECT : g = V_k^T x, ||x||, rho and the gate of every call
  *                       (GSI-TS §2.1-§2.2); writes rho/slow of each call;
  *   GSI_PHASE_APPLY   : every call's output through the path its gate chose

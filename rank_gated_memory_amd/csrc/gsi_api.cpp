@@ -6,7 +6,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "../../include/gsi.h"
@@ -17,6 +19,7 @@ namespace gsi {
 hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int d, int d_out,
                           int k, hipStream_t s);
 hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s);
+hipError_t launch_stack(int dtype, const FArgs &a, int mode, int max_groups, hipStream_t s);
 hipError_t launch_batched(const BArgs &a, hipStream_t s);
 }  // namespace gsi
 
@@ -80,16 +83,18 @@ int64_t proj_target_bytes(int64_t total_v_bytes) {
 }
 
 struct WsLayout {
-  uint64_t gate_off, need_off, pref_off, float_off, total;
+  uint64_t gate_off, need_off, pref_off, float_off, ctl_off, total;
 };
 
-WsLayout ws_layout(int64_t n, int64_t floats) {
+// ctl: control words of the single-launch stack kernel (0 for gsi_linear)
+WsLayout ws_layout(int64_t n, int64_t floats, int64_t ctl = 0) {
   WsLayout w;
   w.gate_off = align_up((uint64_t)(n + 1) * 4, 256);
   w.need_off = align_up(w.gate_off + (uint64_t)n * 16, 256);
   w.pref_off = align_up(w.need_off + (uint64_t)n * 4, 256);
   w.float_off = align_up(w.pref_off + (uint64_t)(n + 1) * 4, 256);
-  w.total = align_up(w.float_off + (uint64_t)floats * 4, 256);
+  w.ctl_off = align_up(w.float_off + (uint64_t)floats * 4, 256);
+  w.total = align_up(w.ctl_off + (uint64_t)ctl * 4, 256);
   return w;
 }
 
@@ -289,18 +294,74 @@ static gsi_status check_call(const gsi_call &c, int32_t dtype) {
   return GSI_OK;
 }
 
+// Byte ranges [lo, hi) of one call's x and y.
+struct Span {
+  uintptr_t lo, hi;
+  int32_t call;
+};
+
+// Calls of one wave may not write what another call of the same wave reads
+// or writes (they run concurrently); across waves anything goes, because a
+// wave starts only after the previous one has finished.
+static gsi_status check_wave_aliasing(const gsi_call *calls, int32_t b, int32_t e) {
+  const int es = esize_of(calls[b].map.dtype);
+  std::vector<Span> ys;
+  ys.reserve(e - b);
+  for (int32_t i = b; i < e; ++i) {
+    const uintptr_t y = reinterpret_cast<uintptr_t>(calls[i].y);
+    ys.push_back({y, y + (uintptr_t)calls[i].map.d_out * es, i});
+  }
+  std::sort(ys.begin(), ys.end(), [](const Span &p, const Span &q) { return p.lo < q.lo; });
+  for (size_t i = 1; i < ys.size(); ++i)
+    if (ys[i].lo < ys[i - 1].hi) return GSI_E_ARG;  // two outputs overlap
+  // outputs are now disjoint and sorted by start (and end): for each input,
+  // the last output starting below its end is the only candidate overlap
+  for (int32_t i = b; i < e; ++i) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(calls[i].x);
+    const uintptr_t hi = lo + (uintptr_t)calls[i].map.d * es;
+    auto it = std::lower_bound(ys.begin(), ys.end(), hi,
+                               [](const Span &p, uintptr_t v) { return p.lo < v; });
+    if (it != ys.begin() && std::prev(it)->hi > lo) return GSI_E_ARG;
+  }
+  return GSI_OK;
+}
+
+// Bytes of V_k per projection unit of a stack plan: small enough that the
+// gates of a step open progressively (output work overlaps projection in
+// the single launch), large enough to amortise a unit's partial hand-off.
+#ifndef GSI_PLAN_PROJ_UNIT_KB
+#define GSI_PLAN_PROJ_UNIT_KB 384
+#endif
+static int64_t plan_proj_target(int64_t total_v_bytes) {
+  int64_t t = total_v_bytes / (256 * 4);
+  if (t < 16 * 1024) t = 16 * 1024;
+  if (t > GSI_PLAN_PROJ_UNIT_KB * 1024) t = GSI_PLAN_PROJ_UNIT_KB * 1024;
+  return t;
+}
+
 static gsi_status plan_sizes(const gsi_call *calls, int32_t n, int64_t *units_a,
-                             int64_t *target, size_t *bytes) {
+                             int64_t *target, size_t *bytes, int32_t *n_waves) {
   if (n < 0 || n > kMaxCalls) return GSI_E_SHAPE;
   if (n > 0 && !calls) return GSI_E_NULL;
   const int32_t dtype = n > 0 ? calls[0].map.dtype : GSI_BF16;
   int64_t vbytes = 0;
+  int32_t waves = 0;
   for (int32_t i = 0; i < n; ++i) {
     const gsi_status s = check_call(calls[i], dtype);
     if (s != GSI_OK) return s;
+    if (calls[i].wave < 0 || (i > 0 && calls[i].wave < calls[i - 1].wave)) return GSI_E_ARG;
+    if (i == 0 || calls[i].wave != calls[i - 1].wave) ++waves;
     vbytes += (int64_t)calls[i].map.d * calls[i].map.k * esize_of(dtype);
   }
-  const int64_t t = proj_target_bytes(vbytes);
+  for (int32_t b = 0; b < n;) {
+    int32_t e = b + 1;
+    while (e < n && calls[e].wave == calls[b].wave) ++e;
+    const gsi_status s = check_wave_aliasing(calls, b, e);
+    if (s != GSI_OK) return s;
+    b = e;
+  }
+  *n_waves = waves;
+  const int64_t t = plan_proj_target(vbytes);
   int64_t ua = 0;
   for (int32_t i = 0; i < n; ++i) {
     const UnitShape us =
@@ -311,21 +372,24 @@ static gsi_status plan_sizes(const gsi_call *calls, int32_t n, int64_t *units_a,
   *target = t;
   const uint64_t desc_off = align_up(sizeof(PlanHeader), 128);
   const uint64_t unit_off = desc_off + (uint64_t)n * sizeof(CallDesc);
-  *bytes = (size_t)align_up(unit_off + (uint64_t)ua * 4, 256);
+  const uint64_t order_off = align_up(unit_off + (uint64_t)ua * 4, 16);
+  *bytes = (size_t)align_up(order_off + (uint64_t)(n + 2 * (waves + 1)) * 4, 256);
   return GSI_OK;
 }
 
 size_t gsi_stack_plan_bytes(const gsi_call *calls, int32_t n) {
   int64_t ua = 0, t = 0;
   size_t bytes = 0;
-  if (plan_sizes(calls, n, &ua, &t, &bytes) != GSI_OK) return 0;
+  int32_t waves = 0;
+  if (plan_sizes(calls, n, &ua, &t, &bytes, &waves) != GSI_OK) return 0;
   return bytes;
 }
 
 gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t plan_bytes) {
   int64_t ua = 0, target = 0;
   size_t bytes = 0;
-  const gsi_status s = plan_sizes(calls, n, &ua, &target, &bytes);
+  int32_t n_waves = 0;
+  const gsi_status s = plan_sizes(calls, n, &ua, &target, &bytes, &n_waves);
   if (s != GSI_OK) return s;
   if (!plan) return GSI_E_NULL;
   if (!aligned(plan, 16)) return GSI_E_ALIGN;
@@ -345,15 +409,24 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   // float offsets: g of every call first, then the partials
   int64_t g_total = 0;
   for (int32_t i = 0; i < n; ++i) g_total += (calls[i].map.k + 3) / 4 * 4;
-  // Projection units of the calls with the most units go first: their
-  // final reductions are the longest and should not be the launch's tail.
+  // Wave by wave, the projection units of the calls with the most units go
+  // first: their final reductions are the longest and should not be the
+  // tail.  Outputs are handed out in the same call order, which is the order
+  // in which the gates are expected to open.
+  std::vector<int32_t> wave_of(n);
+  for (int32_t i = 0, w = -1; i < n; ++i) {
+    if (i == 0 || calls[i].wave != calls[i - 1].wave) ++w;
+    wave_of[i] = w;
+  }
   std::vector<int32_t> order(n);
   for (int32_t i = 0; i < n; ++i) order[i] = i;
   std::vector<int32_t> nunits(n);
   for (int32_t i = 0; i < n; ++i)
     nunits[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, target).a_units;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t x, int32_t y) { return nunits[x] > nunits[y]; });
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    if (wave_of[x] != wave_of[y]) return wave_of[x] < wave_of[y];
+    return nunits[x] > nunits[y];
+  });
   std::vector<int32_t> first_unit(n);
   {
     int64_t u = 0;
@@ -363,7 +436,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     }
   }
   int64_t g_off = 0, part_off = g_total, a_begin = 0, units_b = 0;
-  int32_t max_k = 8, max_d = 8;
+  int32_t max_k = 8, max_d = 8, units_max = 1;
   for (int32_t i = 0; i < n; ++i) {
     const gsi_call &c = calls[i];
     const UnitShape us = unit_shape(c.map.d, c.map.d_out, c.map.k, es, target);
@@ -390,10 +463,15 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.g_off = g_off;
     o.part_off = part_off;
     o.gate_off = i;
+    o.wave = wave_of[i];
+    o.flags = (o.wave > 0 ? kCallXCoherent : 0) | (o.wave + 1 < n_waves ? kCallYCoherent : 0);
     for (int32_t q = 0; q < us.a_units; ++q) unit_call[a_begin + q] = i;
     g_off += us.g_floats;
     part_off += us.part_floats;
-    units_b += us.fast_units > us.slow_units ? us.fast_units : us.slow_units;
+    const int32_t ub = us.fast_units > us.slow_units ? us.fast_units : us.slow_units;
+    if (ub >= kMaxUnitsPerCall) return GSI_E_SHAPE;
+    units_b += ub;
+    if (ub > units_max) units_max = ub;
     if (c.map.k > max_k) max_k = c.map.k;
     if (c.map.d > max_d) max_d = c.map.d;
   }
@@ -403,14 +481,28 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     h->units_a = (int32_t)ua;
   }
   h->units_b = (int32_t)units_b;
+  h->units_max = units_max;
   h->max_k = max_k;
   h->max_d = max_d;
-  const WsLayout wl = ws_layout(n, part_off);
+  h->n_waves = n_waves;
+  // output order and the per-wave tables of the single-launch kernel
+  h->order_off = align_up(h->unit_off + (uint64_t)h->units_a * 4, 16);
+  auto *a_order = reinterpret_cast<int32_t *>(static_cast<char *>(plan) + h->order_off);
+  int32_t *wave_tab = a_order + n;
+  for (int32_t i = 0; i < n; ++i) a_order[i] = order[i];
+  for (int32_t w = 0, i = 0; w <= n_waves; ++w) {
+    while (i < n && wave_of[order[i]] < w) ++i;
+    wave_tab[w] = i < n ? first_unit[order[i]] : h->units_a;  // first projection unit
+    wave_tab[n_waves + 1 + w] = i;                               // first output slot
+  }
+  h->ctl_words = (int32_t)ctl_words(n, n_waves);
+  const WsLayout wl = ws_layout(n, part_off, h->ctl_words);
   h->ws_bytes = n > 0 ? wl.total : 0;
   h->ws_gate_off = wl.gate_off;
   h->ws_need_off = wl.need_off;
   h->ws_pref_off = wl.pref_off;
   h->ws_float_off = wl.float_off;
+  h->ws_ctl_off = wl.ctl_off;
   return GSI_OK;
 }
 
@@ -421,24 +513,73 @@ size_t gsi_stack_workspace(const void *plan_host) {
   return (size_t)h->ws_bytes;
 }
 
+size_t gsi_stack_status_offset(const void *plan_host) {
+  if (!plan_host) return 0;
+  const auto *h = static_cast<const PlanHeader *>(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->n <= 0) return 0;
+  return (size_t)(h->ws_ctl_off + 4 * kCtlStatus);
+}
+
+// Bound of every device-side wait of the single-launch kernel, in polls of
+// a few hundred ns: far beyond any legitimate wait.  GSI_SPIN_LIMIT
+// overrides it (tests force the bound to run out).
+static int32_t spin_limit() {
+  const char *e = std::getenv("GSI_SPIN_LIMIT");
+  if (e && *e) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 0 && v < (1L << 30)) return (int32_t)v;
+  }
+  return 1 << 22;
+}
+
+static gsi_status check_plan_run(const PlanHeader *h, const void *plan_dev, int32_t mode, void *ws,
+                                 size_t ws_bytes) {
+  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->n < 0 || h->n > kMaxCalls)
+    return GSI_E_ARG;
+  if (mode < GSI_GATED || mode > GSI_FORCE_SLOW) return GSI_E_ARG;
+  if (h->n == 0) return GSI_OK;
+  if (!plan_dev || !ws) return GSI_E_NULL;
+  if (!aligned(plan_dev, 16) || !aligned(ws, 256)) return GSI_E_ALIGN;
+  if (ws_bytes < h->ws_bytes) return GSI_E_WORKSPACE;
+  return GSI_OK;
+}
+
 gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, void *ws,
                      size_t ws_bytes, void *stream) {
-  return gsi_stack_phase(plan_host, plan_dev, mode, GSI_PHASE_PROJECT | GSI_PHASE_APPLY, ws,
-                         ws_bytes, stream);
+  if (!plan_host) return GSI_E_NULL;
+  const auto *h = static_cast<const PlanHeader *>(plan_host);
+  const gsi_status s = check_plan_run(h, plan_dev, mode, ws, ws_bytes);
+  if (s != GSI_OK || h->n == 0) return s;
+  const char *pd = static_cast<const char *>(plan_dev);
+  char *w = static_cast<char *>(ws);
+  FArgs a{};
+  a.table = reinterpret_cast<const CallDesc *>(pd + h->desc_off);
+  a.unit_call = reinterpret_cast<const int32_t *>(pd + h->unit_off);
+  a.a_order = reinterpret_cast<const int32_t *>(pd + h->order_off);
+  a.wave_tab = a.a_order + h->n;
+  a.ctl = reinterpret_cast<uint32_t *>(w + h->ws_ctl_off);
+  a.entries = reinterpret_cast<uint64_t *>(a.ctl + kCtlWave0 + kCtlWaveWords * h->n_waves);
+  a.counters = reinterpret_cast<uint32_t *>(w);
+  a.gate = w + h->ws_gate_off;
+  a.wsf = reinterpret_cast<float *>(w + h->ws_float_off);
+  a.n = h->n;
+  a.n_waves = h->n_waves;
+  a.max_k = h->max_k;
+  a.max_d = h->max_d;
+  a.spin_limit = spin_limit();
+  const hipError_t e = launch_stack(h->dtype, a, mode, h->units_a + h->units_b,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }
 
 gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t mode,
                            int32_t phase, void *ws, size_t ws_bytes, void *stream) {
   if (!plan_host) return GSI_E_NULL;
   const auto *h = static_cast<const PlanHeader *>(plan_host);
-  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->n < 0 || h->n > kMaxCalls)
-    return GSI_E_ARG;
-  if (mode < GSI_GATED || mode > GSI_FORCE_SLOW) return GSI_E_ARG;
   if (phase < 1 || phase > 3) return GSI_E_ARG;
-  if (h->n == 0) return GSI_OK;
-  if (!plan_dev || !ws) return GSI_E_NULL;
-  if (!aligned(plan_dev, 16) || !aligned(ws, 256)) return GSI_E_ALIGN;
-  if (ws_bytes < h->ws_bytes) return GSI_E_WORKSPACE;
+  const gsi_status s = check_plan_run(h, plan_dev, mode, ws, ws_bytes);
+  if (s != GSI_OK || h->n == 0) return s;
+  if (h->n_waves > 1) return GSI_E_ARG;  // the two-launch form has no wave barriers
   KArgs a{};
   a.table = reinterpret_cast<const CallDesc *>(static_cast<const char *>(plan_dev) + h->desc_off);
   a.unit_call =

@@ -8,7 +8,7 @@
 namespace gsi {
 
 constexpr uint32_t kPlanMagic = 0x50495347u;  // "GSIP"
-constexpr uint32_t kPlanVersion = 1;
+constexpr uint32_t kPlanVersion = 2;
 constexpr int kBlock = 256;          // threads per workgroup of every kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kTileRows = 64;        // image rows per tile (one per lane)
@@ -38,9 +38,17 @@ struct alignas(16) CallDesc {
   int64_t g_off;       // float offset in the workspace of g [k]
   int32_t gate_off;    // index of this call's gate record / counter
   int32_t fast_tiles;  // 64-row image tiles per fast output unit (multiple of kWaves)
-  int32_t pad_[2];
+  int32_t flags;       // kCallXCoherent | kCallYCoherent
+  int32_t wave;        // wave of the call in a stack (0 for independent calls)
 };
 static_assert(sizeof(CallDesc) == 128, "CallDesc layout");
+
+// CallDesc::flags.  In a stack of several waves, x of a later wave may be
+// the y of an earlier one, written inside the same launch by a workgroup on
+// another XCD: such x is read, and such y written, with agent-coherent
+// accesses (the eight XCD L2s are not coherent with each other).
+constexpr int32_t kCallXCoherent = 1;
+constexpr int32_t kCallYCoherent = 2;
 
 // Header of a stack plan (host buffer, copied verbatim to the device).
 struct alignas(16) PlanHeader {
@@ -60,8 +68,36 @@ struct alignas(16) PlanHeader {
   uint64_t ws_need_off;
   uint64_t ws_pref_off;
   uint64_t ws_float_off;
+  uint64_t ws_ctl_off;   // control words of the single-launch stack kernel
+  uint64_t order_off;    // int32 a_order[n], then int32 wave_tab[2 (n_waves + 1)]
+  int32_t n_waves;
+  int32_t ctl_words;
+  int32_t units_max;     // largest per-call max(fast_units, slow_units)
+  int32_t pad_;
 };
-static_assert(sizeof(PlanHeader) == 96, "PlanHeader layout");
+static_assert(sizeof(PlanHeader) == 128, "PlanHeader layout");
+
+// Control words of the single-launch stack kernel (uint32, zero between
+// launches except the status word).  Hot words sit on separate 128-byte
+// lines.
+constexpr int kCtlStatus = 0;       // sticky: nonzero once a device-side wait ran out
+constexpr int kCtlExit = 32;        // workgroups that have left the work loop
+constexpr int kCtlSeg = 64;         // first work segment not known to be exhausted
+constexpr int kCtlWave0 = 96;       // per wave: kCtlWaveWords words, then the open lists
+constexpr int kCtlWaveWords = 128;  // four lines per wave:
+constexpr int kWvProj = 0;          //   projection tickets taken
+constexpr int kWvOut = 32;          //   output tickets taken
+constexpr int kWvOpen = 64;         //   open word (64-bit): calls open << 40 | their output units
+constexpr int kWvDone = 96;         //   output units finished (waves with a successor)
+// After the wave blocks: the open list, one 64-bit entry per call, indexed by
+// the wave's first a_order slot plus the order in which the call's gate
+// opened: base | need << 32 | slow << 50 | (call + 1) << 51, where base is
+// the wave's output ticket of the call's first unit and need its unit count.
+constexpr int kEntryNeedBits = 18;
+constexpr int64_t kMaxUnitsPerCall = (int64_t)1 << kEntryNeedBits;
+inline int64_t ctl_words(int64_t n, int64_t n_waves) {
+  return kCtlWave0 + kCtlWaveWords * n_waves + 2 * n;
+}
 
 // Workspace regions (byte offsets from the workspace base):
 //   [0, 4(n+1))         uint32 counters: one per call, then one for the whole
@@ -96,6 +132,29 @@ struct KArgs {
   int32_t *need;
   int32_t *pref;
   float *wsf;
+};
+
+// Arguments of the single-launch stack kernel.  Work is a sequence of
+// segments: the projection units of wave 0, the output units of wave 0, the
+// projection units of wave 1, ...  Workgroups take tickets segment by
+// segment; see stack_kernel.
+struct FArgs {
+  const CallDesc *table;
+  const int32_t *unit_call;  // projection unit -> call, wave-major
+  const int32_t *a_order;    // calls in output order, wave-major
+  const int32_t *wave_tab;   // [n_waves + 1] first projection unit of each wave,
+                             // then [n_waves + 1] first a_order slot of each wave
+  uint32_t *ctl;             // control words (kCtl*)
+  uint64_t *entries;         // open lists: ctl + kCtlWave0 + kCtlWaveWords * n_waves
+  uint32_t *counters;        // per-call projection counters
+  void *gate;                // float4 records
+  float *wsf;
+  int32_t n;
+  int32_t n_waves;
+  int32_t max_k;
+  int32_t max_d;
+  int32_t spin_limit;        // bound of every device-side wait (polls)
+  int32_t pad_;
 };
 
 // Unit sizing shared by the stack plan and the single-map path.

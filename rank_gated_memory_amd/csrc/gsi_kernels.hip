@@ -74,6 +74,14 @@ struct Vec<float> {
   __device__ __forceinline__ static void store1(void *p, size_t i, float v) {
     static_cast<float *>(p)[i] = v;
   }
+  // agent-coherent forms (data handed between waves of one launch)
+  __device__ __forceinline__ static float load1c(const void *p, size_t i) {
+    return __hip_atomic_load(const_cast<float *>(static_cast<const float *>(p)) + i,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ static void store1c(void *p, size_t i, float v) {
+    __hip_atomic_store(static_cast<float *>(p) + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 };
 
 template <>
@@ -96,7 +104,25 @@ struct Vec<bf16_t> {
   __device__ __forceinline__ static void store1(void *p, size_t i, float v) {
     static_cast<uint16_t *>(p)[i] = float_to_bf16(v);
   }
+  __device__ __forceinline__ static float load1c(const void *p, size_t i) {
+    const uint16_t b = __hip_atomic_load(const_cast<uint16_t *>(static_cast<const uint16_t *>(p)) + i,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __uint_as_float((uint32_t)b << 16);
+  }
+  __device__ __forceinline__ static void store1c(void *p, size_t i, float v) {
+    __hip_atomic_store(static_cast<uint16_t *>(p) + i, float_to_bf16(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 };
+
+// One element of y: agent-coherent when a later wave of the same launch reads it.
+template <typename T>
+__device__ __forceinline__ void store_y(const CallDesc &cd, int i, float v) {
+  if (cd.flags & kCallYCoherent)
+    Vec<T>::store1c(cd.y, i, v);
+  else
+    Vec<T>::store1(cd.y, i, v);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
   // Butterfly: every lane ends with the same, order-fixed sum.
@@ -189,19 +215,14 @@ __device__ void launch_prefix(const KArgs &a, int *sh_int) {
   if (tid == kBlock - 1) a.pref[n] = sh_int[kBlock - 1];
 }
 
-template <typename T, int UNROLL, int MODE>
-__global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
+// Partial g = V_k^T x and ||x||^2 over projection unit q of a call (a chunk
+// of a_rows rows of V_k), written to `part` ([k] then ||x||^2) with
+// agent-coherent stores.  XC: x is read with agent-coherent loads.
+template <typename T, int UNROLL, bool XC>
+__device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *part, float *red,
+                                             float *sh) {
   constexpr int VW = Vec<T>::VW;
-  __shared__ float red[kBlock * VW];
-  __shared__ float sh[kWaves];
-  __shared__ int sh_int[kBlock];
-  __shared__ int s_last;
-
   const int tid = threadIdx.x;
-  const int u = blockIdx.x;
-  const int c = a.table ? a.unit_call[u] : (u / a.one.a_units);
-  const CallDesc cd = load_call(a, c);
-  const int q = u - cd.a_begin;
   const int row0 = q * cd.a_rows;
   const int rows = min(cd.a_rows, cd.d - row0);
   const int k = cd.k;
@@ -229,7 +250,7 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         v[j] = vp[(size_t)(r + j * rpp) * tpr];
-        xv[j] = Vec<T>::load1(xp, r + j * rpp);
+        xv[j] = XC ? Vec<T>::load1c(xp, r + j * rpp) : Vec<T>::load1(xp, r + j * rpp);
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
@@ -243,7 +264,7 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
     // remainder rows of the last chunk of a call
     for (; r < rows; r += rpp) {
       const uint4 v = vp[(size_t)r * tpr];
-      const float xv = Vec<T>::load1(xp, r);
+      const float xv = XC ? Vec<T>::load1c(xp, r) : Vec<T>::load1(xp, r);
       float f[VW];
       Vec<T>::unpack(v, f);
 #pragma unroll
@@ -255,28 +276,26 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   }
   xx = block_sum(xx, sh);  // also publishes red to the workgroup
 
-  const int stride = k + 4;
-  float *part = a.wsf + cd.part_off + (int64_t)q * stride;
   for (int j = tid; j < k; j += kBlock) {
     float s = 0.f;
     for (int sl = 0; sl < rpp; ++sl) s += red[sl * k + j];
     store_coherent(part + j, s);
   }
   if (tid == 0) store_coherent(part + k, xx);
+}
 
-  // Hand the partials over (see the header); the last chunk finishes the gate.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(cd.a_units - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  const float *p0 = a.wsf + cd.part_off;
-  float *g = a.wsf + cd.g_off;
+// Run by the workgroup that wrote a call's last partial: sums the partials
+// in a fixed order (bitwise deterministic), forms ||g||^2, rho and the gate
+// (GSI-TS §2.2), writes g (agent-coherent stores when GC), the gate record
+// and the caller's rho / slow, and clears the call's counter.  Returns the
+// slow flag (valid on thread 0).
+template <int MODE, bool GC>
+__device__ __forceinline__ int finish_gate(const CallDesc &cd, const float *wsf, float *gw,
+                                           void *gate, uint32_t *counters, float *sh) {
+  const int tid = threadIdx.x;
+  const int k = cd.k;
+  const int stride = k + 4;
+  const float *p0 = wsf + cd.part_off;
   float gg = 0.f;
   for (int j = tid; j < k; j += kBlock) {
     float s = 0.f;
@@ -296,23 +315,56 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
       for (int i = 0; i < 8; ++i) s += t[i];
     }
     for (; qq < cd.a_units; ++qq) s += load_coherent(p0 + (int64_t)qq * stride + j);
-    g[j] = s;
+    if (GC)
+      store_coherent(gw + j, s);
+    else
+      gw[j] = s;
     gg = fmaf(s, s, gg);
   }
   float xp = 0.f;
   for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += load_coherent(p0 + (int64_t)qq * stride + k);
   gg = block_sum(gg, sh);
   const float xxt = block_sum(xp, sh);
+  int slow = 0;
   if (tid == 0) {
     const float rho = rho_from_norms(xxt, gg);
-    const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < cd.eps));
-    reinterpret_cast<float4 *>(a.gate)[cd.gate_off] =
-        make_float4(rho, __int_as_float(slow), xxt, gg);
+    slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < cd.eps));
+    reinterpret_cast<float4 *>(gate)[cd.gate_off] = make_float4(rho, __int_as_float(slow), xxt, gg);
     if (cd.rho) *cd.rho = rho;
     if (cd.slow) *cd.slow = (uint8_t)slow;
-    a.counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
-    store_coherent_i(a.need + c, slow ? cd.slow_units : cd.fast_units);
+    counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
   }
+  return slow;
+}
+
+template <typename T, int UNROLL, int MODE>
+__global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
+  constexpr int VW = Vec<T>::VW;
+  __shared__ float red[kBlock * VW];
+  __shared__ float sh[kWaves];
+  __shared__ int sh_int[kBlock];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int c = a.table ? a.unit_call[u] : (u / a.one.a_units);
+  const CallDesc cd = load_call(a, c);
+  const int q = u - cd.a_begin;
+  proj_partial<T, UNROLL, false>(cd, q, a.wsf + cd.part_off + (int64_t)q * (cd.k + 4), red, sh);
+
+  // Hand the partials over (see the header); the last chunk finishes the gate.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (unsigned)(cd.a_units - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  const int slow = finish_gate<MODE, false>(cd, a.wsf, a.wsf + cd.g_off, a.gate, a.counters, sh);
+  if (tid == 0) store_coherent_i(a.need + c, slow ? cd.slow_units : cd.fast_units);
 
   // The last call to finish writes the launch-wide prefix of output units.
   __builtin_amdgcn_s_waitcnt(0);
@@ -373,9 +425,9 @@ __device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const f
       }
     }
     const int oa = tile * kTileRows + lane;
-    if (oa < cd.d_out) Vec<T>::store1(cd.y, oa, a0 + a1);
+    if (oa < cd.d_out) store_y<T>(cd, oa, a0 + a1);
     const int ob = (tile + kWaves) * kTileRows + lane;
-    if (two && ob < cd.d_out) Vec<T>::store1(cd.y, ob, b0 + b1);
+    if (two && ob < cd.d_out) store_y<T>(cd, ob, b0 + b1);
   }
 }
 
@@ -423,8 +475,8 @@ __device__ __forceinline__ void slow_unit(const CallDesc &cd, int local, const u
     const float sa = wave_sum(a0 + a1);
     const float sb = wave_sum(b0 + b1);
     if (lane == 0) {
-      Vec<T>::store1(cd.y, r, sa);
-      if (two) Vec<T>::store1(cd.y, r + kWaves, sb);
+      store_y<T>(cd, r, sa);
+      if (two) store_y<T>(cd, r + kWaves, sb);
     }
   }
 }
@@ -487,6 +539,376 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
       slow_unit<T, UNROLL>(cd, local, xs);
     else
       fast_unit<T, UNROLL>(cd, local, gs);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch stack: projection, gate and output of every call of a plan
+// in one persistent launch.
+//
+// Waves run one after the other.  Within wave w there are projection units
+// (a fixed count, one ticket counter) and output units (a count known per
+// call once its gate is decided).  The workgroup that decides a call's gate
+// opens it by appending the call to the wave's open list: one 64-bit
+// fetch-add on the wave's open word (open calls << 40 | their output units)
+// returns both the call's slot and the output ticket of its first unit, so
+// output tickets number the units of the open calls in the order their
+// gates opened.  Each workgroup holds one projection ticket and one output
+// ticket of its wave.  It runs the output unit as soon as the open units
+// cover its output ticket (finding the covering call by scanning the open
+// list 64 slots at a time with the lanes of wavefront 0), otherwise a
+// projection unit, and fetches the next ticket of the kind it used while the
+// unit runs.  No workgroup walks calls or polls a single call's word, which
+// keeps the control traffic off any one memory channel.
+//
+// A workgroup waits only (a) when its wave has no projection ticket left and
+// its output ticket is not covered yet: every gate it can wait for belongs
+// to a call whose projection units are all held by running workgroups,
+// which never wait inside the wave; or (b) on entering wave w+1, which it
+// does only once wave w has no ticket left: every unit of wave w is then
+// held by a running workgroup that waits on nothing later.  By induction
+// over waves every wait ends, whatever the number of resident workgroups.
+// Each wait is also bounded (spin_limit polls); if one ever runs out the
+// workgroup sets the sticky status word and leaves, so the launch always
+// drains.
+//
+// Within a wave, a call's output work starts as soon as its own gate opens,
+// overlapping the projection of other calls, and no launch boundary
+// separates the phases.
+//
+// Cross-workgroup data (partials, g, control words, and activations handed
+// between waves) moves with agent-coherent accesses only, as in
+// proj_kernel; s_waitcnt 0 before a barrier orders a workgroup's stores
+// before the control word that publishes them.
+// ---------------------------------------------------------------------------
+enum { kJobDone = 0, kJobProj = 1, kJobOut = 2 };
+
+// Rows of V_k in flight per thread in a projection unit of the single-launch
+// kernel.
+#ifndef GSI_STACK_PROJ_UNROLL
+#define GSI_STACK_PROJ_UNROLL 8
+#endif
+
+__device__ __forceinline__ uint32_t ctl_load(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ctl_load64(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctl_add(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ctl_add64(uint64_t *p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctl_max(uint32_t *p, uint32_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctl_store(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctl_store64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The scheduler runs on the 64 lanes of wavefront 0.  Control words are
+// touched by lane 0 only and broadcast; the open-list scan uses every lane.
+__device__ __forceinline__ uint32_t bcast(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t bcast64(uint64_t v) {
+  return ((uint64_t)bcast((uint32_t)(v >> 32)) << 32) | bcast((uint32_t)v);
+}
+
+constexpr uint64_t kLow40 = ((uint64_t)1 << 40) - 1;
+
+// Scheduler state of one workgroup (uniform over wavefront 0; the tickets
+// live in lane 0 between a fetch and their next use).
+struct Sched {
+  int w;          // current wave
+  int entered;    // first tickets of wave w taken
+  int p_out;      // projection tickets of wave w known exhausted
+  int p_held;     // st.tp holds a projection ticket not yet run
+  int last_out;   // the last job was an output unit
+  int pf;         // ticket to fetch while the job runs: 1 projection, 2 output
+  int slot;       // first open-list slot that may hold the output ticket
+  uint32_t tp;    // projection ticket held
+  uint32_t to;    // output ticket held
+  uint64_t open;  // last open word seen for wave w
+};
+
+__device__ __forceinline__ uint32_t *wave_ctl(const FArgs &a, int w) {
+  return a.ctl + kCtlWave0 + w * kCtlWaveWords;
+}
+
+__device__ __forceinline__ void set_job(int *job, int kind, int c, int u, int slow) {
+  if (threadIdx.x == 0) {
+    job[0] = kind;
+    job[1] = c;
+    job[2] = u;
+    job[3] = slow;
+  }
+}
+
+__device__ __forceinline__ void sched_fail(const FArgs &a, int code, int *job) {
+  if (threadIdx.x == 0) ctl_max(a.ctl + kCtlStatus, (uint32_t)code);
+  set_job(job, kJobDone, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint64_t load_open(const FArgs &a, int w) {
+  uint64_t ow = 0;
+  if (threadIdx.x == 0) ow = ctl_load64(reinterpret_cast<const uint64_t *>(wave_ctl(a, w) + kWvOpen));
+  return bcast64(ow);
+}
+
+// Picks the next job of this workgroup (wavefront 0): job = {kind, call,
+// unit, slow} in LDS.  Within a wave a workgroup holds one output ticket
+// and at most one projection ticket.  It runs its output unit as soon as
+// the open units cover the ticket, otherwise a projection unit; a
+// projection ticket fetched during a projection unit is run right after at
+// most one output unit, so no ticket that gates other work is held for
+// long.  It waits only when the wave has no projection ticket left, and
+// leaves the wave once every gate is open and its output ticket lies beyond
+// the last unit.  The first ticket of each kind in a wave is the workgroup's
+// own index (no atomic); the counters hand out the tickets from the grid
+// size on.
+__device__ void next_job(const FArgs &a, Sched &st, int *job) {
+  const int lane = threadIdx.x;
+  st.pf = 0;
+  int polls = 0;
+  for (;;) {
+    if (st.w >= a.n_waves) break;
+    const int w = st.w;
+    uint32_t *wv = wave_ctl(a, w);
+    if (!st.entered) {
+      if (w > 0) {
+        // x of this wave may be y of the previous one: wait for its outputs
+        // (every unit of that wave is held by a running workgroup).
+        const uint32_t *pv = wave_ctl(a, w - 1);
+        const uint32_t pcalls = (uint32_t)(a.wave_tab[a.n_waves + 1 + w] - a.wave_tab[a.n_waves + w]);
+        for (int s = 0;; ++s) {
+          uint32_t ok = 0;
+          if (lane == 0) {
+            const uint64_t ow = ctl_load64(reinterpret_cast<const uint64_t *>(pv + kWvOpen));
+            ok = (ow >> 40) == pcalls && ctl_load(pv + kWvDone) == (uint32_t)(ow & kLow40);
+          }
+          if (bcast(ok)) break;
+          if (s >= a.spin_limit) return sched_fail(a, 1, job);
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      st.to = blockIdx.x;
+      st.tp = blockIdx.x;
+      st.entered = 1;
+      st.p_out = 0;
+      st.p_held = 1;
+      st.last_out = 0;
+      st.slot = 0;
+      st.open = 0;
+    }
+    const int p0 = a.wave_tab[w];
+    const int np = a.wave_tab[w + 1] - p0;
+    if (st.p_held && st.last_out) {
+      // a projection ticket waited through one output unit: run it now
+      const uint32_t tp = bcast(st.tp);
+      st.p_held = 0;
+      if ((int)tp < np) {
+        set_job(job, kJobProj, a.unit_call[p0 + tp], p0 + (int)tp, 0);
+        st.last_out = 0;
+        st.pf = 1;
+        return;
+      }
+      st.p_out = 1;
+    }
+    const uint32_t to = bcast(st.to);
+    const int q0 = a.wave_tab[a.n_waves + 1 + w];
+    const uint32_t ncalls = (uint32_t)(a.wave_tab[a.n_waves + 2 + w] - q0);
+    if (to >= (uint32_t)(st.open & kLow40)) st.open = load_open(a, w);
+    if (to < (uint32_t)(st.open & kLow40)) {
+      // ---- output unit: find the open call that covers ticket `to` ----
+      const int nopen = (int)(st.open >> 40);
+      for (int base_slot = st.slot;; base_slot += 64) {
+        const int idx = base_slot + lane;
+        uint64_t e = 0;
+        int stuck = 0;
+        if (idx < nopen) {
+          e = ctl_load64(a.entries + q0 + idx);
+          for (int s = 0; e == 0; ++s) {  // opened a moment ago, entry not yet stored
+            if (s >= a.spin_limit) {
+              stuck = 1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            e = ctl_load64(a.entries + q0 + idx);
+          }
+        }
+        if (__ballot(stuck)) return sched_fail(a, 3, job);
+        const uint32_t eb = (uint32_t)e;
+        const uint32_t en = (uint32_t)(e >> 32) & ((1u << kEntryNeedBits) - 1);
+        const uint64_t hit = __ballot(idx < nopen && to >= eb && to - eb < en);
+        if (hit) {
+          const int l = __ffsll((unsigned long long)hit) - 1;
+          const uint64_t he =
+              ((uint64_t)(uint32_t)__shfl((int)(e >> 32), l, 64) << 32) | (uint32_t)__shfl((int)eb, l, 64);
+          st.slot = base_slot + l;
+          set_job(job, kJobOut, (int)(he >> 51) - 1, (int)(to - (uint32_t)he), (int)((he >> 50) & 1));
+          st.last_out = 1;
+          st.pf = 2;
+          return;
+        }
+        if (base_slot + 64 >= nopen) return sched_fail(a, 4, job);  // cannot happen: to < open units
+      }
+    }
+    if (!st.p_out) {
+      // ---- projection unit ----
+      if (!st.p_held) {
+        uint32_t t = 0;
+        if (lane == 0) t = gridDim.x + ctl_add(wv + kWvProj, 1u);
+        st.tp = t;
+      }
+      const uint32_t tp = bcast(st.tp);
+      st.p_held = 0;
+      if ((int)tp < np) {
+        set_job(job, kJobProj, a.unit_call[p0 + tp], p0 + (int)tp, 0);
+        st.last_out = 0;
+        st.pf = 1;
+        return;
+      }
+      st.p_out = 1;
+    }
+    if ((uint32_t)(st.open >> 40) == ncalls) {  // every gate open and `to` beyond the last unit
+      st.w += 1;
+      st.entered = 0;
+      continue;
+    }
+    // nothing to do until another gate of this wave opens
+    if (++polls > a.spin_limit) return sched_fail(a, 2, job);
+    __builtin_amdgcn_s_sleep(8);
+  }
+  set_job(job, kJobDone, 0, 0, 0);
+}
+
+// Fetches the ticket of the kind the job used up (wavefront 0, right after
+// the job was handed out; lane 0 takes the ticket, which the next call of
+// next_job reads; the state flags stay uniform over the wavefront).
+__device__ __forceinline__ void sched_prefetch(const FArgs &a, Sched &st) {
+  if (st.pf == 1) {
+    if (threadIdx.x == 0) st.tp = gridDim.x + ctl_add(wave_ctl(a, st.w) + kWvProj, 1u);
+    st.p_held = 1;
+  } else if (st.pf == 2) {
+    if (threadIdx.x == 0) st.to = gridDim.x + ctl_add(wave_ctl(a, st.w) + kWvOut, 1u);
+  }
+}
+
+// Two workgroups of four wavefronts per CU (see launch_stack_mode): the
+// register budget of two wavefronts per SIMD lets the compiler keep every
+// streaming load of a unit in flight (measured 290 -> 238 us per 112-map
+// step against the default budget).
+#ifndef GSI_STACK_WAVES_PER_EU
+#define GSI_STACK_WAVES_PER_EU 2
+#endif
+#define GSI_STACK_ATTR __attribute__((amdgpu_waves_per_eu(1, GSI_STACK_WAVES_PER_EU)))
+
+template <typename T, int UNROLL, int MODE>
+__global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
+  constexpr int VW = Vec<T>::VW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float sh[kWaves];
+  __shared__ int s_job[4];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  // Output units use x (slow) or g (fast) staged at the start of the LDS
+  // block; projection units use it for their column partials.
+  uint4 *xs = reinterpret_cast<uint4 *>(smem);
+  float *gs = reinterpret_cast<float *>(smem + align_up((uint64_t)a.max_d * sizeof(T), 16));
+  float *red = reinterpret_cast<float *>(smem);
+
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
+  int cur = -1, cur_slow = 0;
+  for (;;) {
+    if (tid < 64) next_job(a, st, s_job);
+    __syncthreads();
+    const int kind = s_job[0];
+    const int c = __builtin_amdgcn_readfirstlane(s_job[1]);
+    const int u = s_job[2];
+    const int slow = s_job[3];
+    __syncthreads();  // s_job is rewritten only after every thread has read it
+    if (kind == kJobDone) break;
+    if (tid < 64) sched_prefetch(a, st);
+    const CallDesc cd = a.table[c];
+    if (kind == kJobProj) {
+      cur = -1;  // the partials overwrite staged x / g
+      const int q = u - cd.a_begin;
+      float *part = a.wsf + cd.part_off + (int64_t)q * (cd.k + 4);
+      if (cd.flags & kCallXCoherent)
+        proj_partial<T, GSI_STACK_PROJ_UNROLL, true>(cd, q, part, red, sh);
+      else
+        proj_partial<T, GSI_STACK_PROJ_UNROLL, false>(cd, q, part, red, sh);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        s_flag = ctl_add(a.counters + c, 1u) == (uint32_t)(cd.a_units - 1) ? 1 : 0;
+      __syncthreads();
+      if (s_flag) {
+        const int sl = finish_gate<MODE, true>(cd, a.wsf, a.wsf + cd.g_off, a.gate, a.counters, sh);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // g of every thread is stored before the gate opens
+        if (tid == 0) {
+          // open the gate: append the call to its wave's open list
+          const uint64_t need = (uint64_t)(sl ? cd.slow_units : cd.fast_units);
+          uint32_t *wv = wave_ctl(a, cd.wave);
+          const uint64_t old = ctl_add64(reinterpret_cast<uint64_t *>(wv + kWvOpen), ((uint64_t)1 << 40) | need);
+          const uint64_t slot = old >> 40;
+          ctl_store64(a.entries + a.wave_tab[a.n_waves + 1 + cd.wave] + slot,
+                      (old & kLow40) | (need << 32) | ((uint64_t)sl << 50) | ((uint64_t)(c + 1) << 51));
+        }
+      }
+    } else {
+      if (c != cur || slow != cur_slow) {
+        if (slow) {
+          const int nv = cd.d / VW;
+          const uint4 *xp = static_cast<const uint4 *>(cd.x);
+          if (cd.flags & kCallXCoherent) {
+            const uint32_t *xw = static_cast<const uint32_t *>(cd.x);
+            for (int i = tid; i < nv; i += kBlock)
+              xs[i] = make_uint4(ctl_load(xw + 4 * i), ctl_load(xw + 4 * i + 1),
+                                 ctl_load(xw + 4 * i + 2), ctl_load(xw + 4 * i + 3));
+          } else {
+            for (int i = tid; i < nv; i += kBlock) xs[i] = xp[i];
+          }
+        } else {
+          for (int j = tid; j < cd.k; j += kBlock) gs[j] = load_coherent(a.wsf + cd.g_off + j);
+        }
+        __syncthreads();
+        cur = c;
+        cur_slow = slow;
+      }
+      if (slow)
+        slow_unit<T, UNROLL>(cd, u, xs);
+      else
+        fast_unit<T, UNROLL>(cd, u, gs);
+      if (cd.wave + 1 < a.n_waves) {
+        // a later wave may read this y: count the unit once its stores landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) ctl_add(wave_ctl(a, cd.wave) + kWvDone, 1u);
+      }
+    }
+  }
+
+  // The last workgroup to leave clears the control words (all but the status
+  // word) and the projection counters for the next launch on this workspace.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_flag = ctl_add(a.ctl + kCtlExit, 1u) == gridDim.x - 1 ? 1 : 0;
+  __syncthreads();
+  if (!s_flag) return;
+  for (int i = tid; i < a.n_waves * kCtlWaveWords; i += kBlock) ctl_store(a.ctl + kCtlWave0 + i, 0u);
+  for (int i = tid; i < a.n; i += kBlock) {
+    ctl_store64(a.entries + i, 0u);
+    ctl_store(a.counters + i, 0u);
+  }
+  if (tid == 0) {
+    ctl_store(a.ctl + kCtlSeg, 0u);
+    ctl_store(a.ctl + kCtlExit, 0u);
   }
 }
 
@@ -587,6 +1009,54 @@ void launch_typed(const KArgs &a, int grid_b, int phases, size_t lds, hipStream_
     launch_modes<T, 2>(a, grid_b, phases, lds, s);
   else
     launch_modes<T, 0>(a, grid_b, phases, lds, s);
+}
+
+size_t stack_lds_bytes(int max_d, int max_k, int esize) {
+  const size_t out = align_up((uint64_t)max_d * esize, 16) + align_up((uint64_t)max_k * 4, 16);
+  const size_t proj = (size_t)kBlock * (16 / esize) * 4;
+  return out > proj ? out : proj;
+}
+
+#ifndef GSI_STACK_GROUPS_PER_CU
+#define GSI_STACK_GROUPS_PER_CU 2
+#endif
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+template <typename T, int MODE>
+hipError_t launch_stack_mode(const FArgs &a, int max_groups, hipStream_t s) {
+  constexpr int U = 8;
+  // Fewer concurrent streams than the registers allow read HBM faster
+  // (512 workgroups beat 768 on the 112-map step), and they must be spread
+  // evenly over the CUs: the LDS request is raised so that at most
+  // GSI_STACK_GROUPS_PER_CU workgroups fit on one CU.
+  size_t lds = stack_lds_bytes(a.max_d, a.max_k, (int)sizeof(T));
+  const size_t spread = kLdsPerCu / (GSI_STACK_GROUPS_PER_CU + 1) + 1024;
+  if (lds < spread && spread * GSI_STACK_GROUPS_PER_CU <= kLdsPerCu) lds = spread;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, stack_kernel<T, U, MODE>, kBlock, lds) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  int grid = occ * cus;
+  if (max_groups > 0 && grid > max_groups) grid = max_groups;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((stack_kernel<T, U, MODE>), dim3(grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_stack_typed(const FArgs &a, int mode, int max_groups, hipStream_t s) {
+  if (mode == 1) return launch_stack_mode<T, 1>(a, max_groups, s);
+  if (mode == 2) return launch_stack_mode<T, 2>(a, max_groups, s);
+  return launch_stack_mode<T, 0>(a, max_groups, s);
+}
+
+hipError_t launch_stack(int dtype, const FArgs &a, int mode, int max_groups, hipStream_t s) {
+  if (dtype == 0) return launch_stack_typed<float>(a, mode, max_groups, s);
+  return launch_stack_typed<bf16_t>(a, mode, max_groups, s);
 }
 
 hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s) {

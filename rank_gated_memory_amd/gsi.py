@@ -35,7 +35,7 @@ class GsiMapStruct(ctypes.Structure):
 
 class GsiCallStruct(ctypes.Structure):
     _fields_ = [("map", GsiMapStruct), ("x", c_void_p), ("y", c_void_p), ("eps", c_float),
-                ("reserved", c_int32), ("rho", c_void_p), ("slow", c_void_p)]
+                ("wave", c_int32), ("rho", c_void_p), ("slow", c_void_p)]
 
 
 _lib = None
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.gsi_stack_workspace.argtypes = [c_void_p]
         L.gsi_stack.restype = c_int32
         L.gsi_stack.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+        L.gsi_stack_status_offset.restype = c_size_t
+        L.gsi_stack_status_offset.argtypes = [c_void_p]
         L.gsi_stack_phase.restype = c_int32
         L.gsi_stack_phase.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
                                       c_void_p]
@@ -180,18 +182,22 @@ def gsi_linear(m: Map, x: torch.Tensor, eps: float, mode: int = GATED, y=None, r
 
 
 class Stack:
-    """A stack plan over independent batch-1 calls, with its device copy.
+    """A stack plan over batch-1 calls, with its device copy.
 
     calls: list of (Map, x [d], y [d_out], eps, rho (1 float) or None,
-    slow (1 byte) or None).  Tensors must stay alive as long as the plan.
+    slow (1 byte) or None[, wave]).  Calls of one wave are independent; a
+    call may read the y of a call of an earlier wave.  Tensors must stay
+    alive as long as the plan.
     """
 
     def __init__(self, calls, device=None):
         self._keep = calls
         n = len(calls)
         arr = (GsiCallStruct * max(n, 1))()
-        for i, (m, x, y, eps, rho, slow) in enumerate(calls):
-            arr[i] = GsiCallStruct(m.struct, _ptr(x), _ptr(y), float(eps), 0, _ptr(rho), _ptr(slow))
+        for i, call in enumerate(calls):
+            m, x, y, eps, rho, slow = call[:6]
+            wave = int(call[6]) if len(call) > 6 else 0
+            arr[i] = GsiCallStruct(m.struct, _ptr(x), _ptr(y), float(eps), wave, _ptr(rho), _ptr(slow))
         self._arr = arr
         nbytes = int(lib().gsi_stack_plan_bytes(arr, n))
         if n > 0 and nbytes == 0:
@@ -204,6 +210,12 @@ class Stack:
         self.ws_bytes = int(lib().gsi_stack_workspace(_ptr(self.host)))
         dev = device if device is not None else (calls[0][1].device if n else "cpu")
         self.dev = self.host.to(dev) if n else None
+        self.status_offset = int(lib().gsi_stack_status_offset(_ptr(self.host)))
+
+    def status(self, ws: torch.Tensor) -> int:
+        """The device status word of this plan's runs in `ws` (0 = every run completed)."""
+        o = self.status_offset
+        return int(ws[o:o + 4].cpu().view(torch.int32)[0])
 
     def run(self, mode: int = GATED, ws=None, stream=None):
         if ws is None:

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gsi.gsi_abi_version() == 1
+    assert gsi.gsi_abi_version() == 2
     m = re.search(r"#define GSI_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == gsi.gsi_abi_version()
     assert gsi.status_str(0) == "GSI_OK"
@@ -105,12 +105,14 @@ def test_linear_workspace_grows_with_tokens():
     assert L.gsi_linear_workspace(ctypes.byref(m), 0) == 0
 
 
-def calls_array(specs):
-    arr = (gsi.GsiCallStruct * len(specs))()
+def calls_array(specs, waves=None, xy=None):
+    """specs: (d, d_out, k, dtype) per call; waves: wave per call; xy: (x, y) addresses per call."""
+    arr = (gsi.GsiCallStruct * max(len(specs), 1))()
     base = FAKE
     for i, (d, d_out, k, dt) in enumerate(specs):
         mp = gsi.GsiMapStruct(d, d_out, k, dt, base, base + 0x1000000, base + 0x2000000)
-        arr[i] = gsi.GsiCallStruct(mp, base + 0x3000000, base + 0x4000000, 0.05, 0, 0, 0)
+        x, y = xy[i] if xy else (base + 0x3000000, base + 0x4000000)
+        arr[i] = gsi.GsiCallStruct(mp, x, y, 0.05, waves[i] if waves else 0, 0, 0)
         base += 0x10000000
     return arr
 
@@ -119,12 +121,22 @@ PLAN_HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("n", "<i4"), ("dtype
                      ("units_a", "<i4"), ("units_b", "<i4"), ("max_k", "<i4"), ("max_d", "<i4"),
                      ("ws_bytes", "<u8"), ("desc_off", "<u8"), ("unit_off", "<u8"),
                      ("total_bytes", "<u8"), ("ws_gate_off", "<u8"), ("ws_need_off", "<u8"),
-                     ("ws_pref_off", "<u8"), ("ws_float_off", "<u8")])
+                     ("ws_pref_off", "<u8"), ("ws_float_off", "<u8"), ("ws_ctl_off", "<u8"),
+                     ("order_off", "<u8"), ("n_waves", "<i4"), ("ctl_words", "<i4"),
+                     ("units_max", "<i4"), ("pad", "<i4")])
+DESC = np.dtype([("ptrs", "<u8", 7), ("d", "<i4"), ("d_out", "<i4"), ("k", "<i4"), ("eps", "<f4"),
+                 ("a_begin", "<i4"), ("a_units", "<i4"), ("a_rows", "<i4"), ("fast_units", "<i4"),
+                 ("slow_units", "<i4"), ("slow_rows", "<i4"), ("part_off", "<i8"), ("g_off", "<i8"),
+                 ("gate_off", "<i4"), ("fast_tiles", "<i4"), ("flags", "<i4"), ("wave", "<i4")])
 
 
-def build_plan(specs):
+def header(plan):
+    return np.frombuffer(plan[:PLAN_HDR.itemsize].tobytes(), dtype=PLAN_HDR)[0]
+
+
+def build_plan(specs, waves=None, xy=None):
     L = gsi.lib()
-    arr = calls_array(specs)
+    arr = calls_array(specs, waves, xy)
     nb = L.gsi_stack_plan_bytes(arr, len(specs))
     buf = np.zeros(nb + 64, dtype=np.uint8)
     off = (-buf.ctypes.data) % 16
@@ -138,8 +150,10 @@ def test_stack_plan_layout():
              (16384, 4096, 512, 1)] * 3
     st, plan, nb = build_plan(specs)
     assert st == GSI_OK
-    h = np.frombuffer(plan[:PLAN_HDR.itemsize].tobytes(), dtype=PLAN_HDR)[0]
-    assert h["magic"] == 0x50495347 and h["n"] == 12 and h["dtype"] == 1
+    h = header(plan)
+    assert PLAN_HDR.itemsize == 128 and DESC.itemsize == 128
+    assert h["magic"] == 0x50495347 and h["version"] == 2 and h["n"] == 12 and h["dtype"] == 1
+    assert h["n_waves"] == 1
     assert h["total_bytes"] == nb and h["max_k"] == 512 and h["max_d"] == 16384
     uo, ua = int(h["unit_off"]), int(h["units_a"])
     unit_call = np.frombuffer(plan[uo:uo + 4 * ua].tobytes(), "<i4")
@@ -182,3 +196,78 @@ def test_stack_rejects_before_launch():
     st0, plan0, _ = build_plan([])
     assert st0 == GSI_OK
     assert L.gsi_stack(plan0.ctypes.data, 0, 0, 0, 0, None) == GSI_OK
+
+
+def plan_tables(plan):
+    h = header(plan)
+    n, W = int(h["n"]), int(h["n_waves"])
+    desc = np.frombuffer(plan[int(h["desc_off"]):int(h["desc_off"]) + n * 128].tobytes(), DESC)
+    uo, ua = int(h["unit_off"]), int(h["units_a"])
+    unit_call = np.frombuffer(plan[uo:uo + 4 * ua].tobytes(), "<i4")
+    oo = int(h["order_off"])
+    tab = np.frombuffer(plan[oo:oo + 4 * (n + 2 * (W + 1))].tobytes(), "<i4")
+    return h, desc, unit_call, tab[:n], tab[n:n + W + 1], tab[n + W + 1:]
+
+
+def test_stack_plan_waves():
+    # two GPT-J-shaped layers as four waves: (qkv, fc_in), (out, fc_out), ...
+    specs = [(4096, 12288, 256, 1), (4096, 16384, 256, 1), (4096, 4096, 256, 1),
+             (16384, 4096, 512, 1)] * 2
+    waves = [0, 0, 1, 1, 2, 2, 3, 3]
+    st, plan, _ = build_plan(specs, waves)
+    assert st == GSI_OK
+    h, desc, unit_call, order, p_begin, o_begin = plan_tables(plan)
+    assert h["n_waves"] == 4
+    assert list(desc["wave"]) == waves
+    # agent-coherent x from wave 1 on, coherent y up to the last wave but one
+    assert list(desc["flags"] & 1) == [0, 0, 1, 1, 1, 1, 1, 1]
+    assert list(desc["flags"] & 2) == [2, 2, 2, 2, 2, 2, 0, 0]
+    # output order is wave-major and holds every call once
+    assert sorted(order) == list(range(8))
+    assert [waves[c] for c in order] == sorted(waves)
+    assert list(o_begin) == [0, 2, 4, 6, 8]
+    # projection units are wave-major; each wave's range holds exactly its calls' units
+    assert p_begin[0] == 0 and p_begin[-1] == h["units_a"]
+    for w in range(4):
+        calls = set(unit_call[p_begin[w]:p_begin[w + 1]].tolist())
+        assert calls == {i for i in range(8) if waves[i] == w}
+        assert p_begin[w + 1] - p_begin[w] == sum(desc["a_units"][i] for i in calls)
+    for i in range(8):
+        assert list(unit_call[desc["a_begin"][i]:desc["a_begin"][i] + desc["a_units"][i]]) == [i] * desc["a_units"][i]
+    # control words: header, one block per wave, one open-list entry per call
+    assert h["ctl_words"] == 96 + 128 * 4 + 2 * 8
+    assert h["ws_ctl_off"] + 4 * h["ctl_words"] <= h["ws_bytes"]
+    assert gsi.lib().gsi_stack_status_offset(plan.ctypes.data) == h["ws_ctl_off"]
+
+
+def test_stack_plan_wave_numbers_may_skip():
+    st, plan, _ = build_plan([(256, 512, 16, 0)] * 3, waves=[0, 5, 5])
+    assert st == GSI_OK
+    h, desc, *_ = plan_tables(plan)
+    assert h["n_waves"] == 2 and list(desc["wave"]) == [0, 1, 1]
+
+
+def test_stack_plan_rejects_bad_waves_and_aliasing():
+    spec = [(256, 512, 16, 0)] * 2
+    assert build_plan(spec, waves=[1, 0])[0] == E_ARG       # decreasing
+    assert build_plan(spec, waves=[-1, 0])[0] == E_ARG      # negative
+    X, Y = FAKE + 0x3000000, FAKE + 0x4000000
+    # same wave: y of one call overlaps y of another, or the x of another
+    assert build_plan(spec, xy=[(X, Y), (X + 0x10000, Y + 1024)])[0] == E_ARG
+    assert build_plan(spec, xy=[(X, Y), (Y + 2032, Y + 0x10000)])[0] == E_ARG
+    # x ranges may overlap (reads only), and touching ranges do not overlap
+    assert build_plan(spec, xy=[(X, Y), (X + 16, Y + 2048)])[0] == GSI_OK
+    assert build_plan(spec, xy=[(X, Y), (Y + 2048, Y + 0x10000)])[0] == GSI_OK
+    # across waves, x may be the y of an earlier call (a chain)
+    assert build_plan(spec, waves=[0, 1], xy=[(X, Y), (Y, Y + 0x10000)])[0] == GSI_OK
+    chain = [(256, 256, 16, 0)] * 3
+    assert build_plan(chain, waves=[0, 1, 2], xy=[(X, Y), (Y, X), (X, Y)])[0] == GSI_OK
+    assert build_plan(chain, waves=[0, 1, 1], xy=[(X, Y), (Y, X), (X, Y)])[0] == E_ARG
+
+
+def test_stack_phase_rejects_multi_wave_plans():
+    L = gsi.lib()
+    st, plan, _ = build_plan([(256, 512, 16, 0)] * 2, waves=[0, 1])
+    assert st == GSI_OK
+    need = L.gsi_stack_workspace(plan.ctypes.data)
+    assert L.gsi_stack_phase(plan.ctypes.data, FAKE, 0, 1, FAKE, need, None) == E_ARG

@@ -412,3 +412,34 @@ def test_spectral_tokens_operating_points(k, eps):
     share = 1.0 - float(ss.float().mean())
     print(f"k={k} eps={eps}: fast share {share:.2f}")
     assert 0.0 < share < 1.0 or eps == 0.10
+
+
+# ------------------------------------------------ single launch vs phases ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_stack_single_launch_matches_two_phases(dtype):
+    """gsi_stack (one persistent launch) gives the same bits as the two-launch form."""
+    items = ragged_stack_inputs(dtype, 2) * 3
+    calls, outs = [], []
+    for W, V, X in items:
+        m = new_map(W, V)
+        y = torch.empty(W.shape[0], dtype=dtype, device=DEV)
+        r = torch.empty(1, dtype=torch.float32, device=DEV)
+        s = torch.empty(1, dtype=torch.uint8, device=DEV)
+        calls.append((m, X[0].to(DEV), y, 0.05, r, s))
+        outs.append((y, r, s))
+    st = gsi.Stack(calls)
+    ws = gsi.workspace(st.ws_bytes, DEV)
+    for mode in (gsi.GATED, gsi.FORCE_FAST, gsi.FORCE_SLOW):
+        gsi.gsi_stack_phase(st, mode, gsi.PHASE_PROJECT, ws)
+        gsi.gsi_stack_phase(st, mode, gsi.PHASE_APPLY, ws)
+        sync()
+        ref = [tuple(t.clone() for t in o) for o in outs]
+        for o in outs:
+            o[0].fill_(7)
+        for _ in range(3):
+            gsi.gsi_stack(st, mode, ws)
+            sync()
+            for (y, r, s), (y0, r0, s0) in zip(outs, ref):
+                assert torch.equal(y, y0) and torch.equal(r, r0) and torch.equal(s, s0)
+    assert st.status(ws) == 0
