@@ -32,6 +32,10 @@ Readings where the pages are silent (each is listed in the design notes):
     exact arithmetic, see the decomposition pin);
   * eps <= 0 or eps > 1 is applied literally.
 
+Readings for chains of calls (an input read from an earlier output):
+  * the input is the earlier output as stored, i.e. rounded to nearest-even
+    in the storage type, not the exact value.
+
 Every function here is pinned by tests that check it against closed forms,
 special cases, identities, invariances or brute force (see tests/).
 """
@@ -139,6 +143,57 @@ def linear_rows(W_rows, V, x, eps: float, mode: int = GATED) -> dict:
     else:
         y = fast_output(prepare(W_rows, V), g)
     return {"g": g, "rho": rho, "slow": slow, "y": y}
+
+
+def to_storage(y, dtype: str) -> np.ndarray:
+    """The value a stored output holds: y rounded to nearest, ties to even, in
+    the storage type ("fp32" or "bf16").
+
+    bf16 keeps 8 significant bits and fp32's exponent range: normal values
+    are rounded to 8 bits, values below 2**-126 to the subnormal grid of
+    spacing 2**-133, and values that round to 2**128 or beyond overflow to
+    infinity.  NaN and infinities are kept.
+    """
+    y = _f64(y)
+    if dtype == "fp32":
+        return y.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(f"unknown storage type {dtype!r}")
+    with np.errstate(invalid="ignore", over="ignore"):
+        m, e = np.frexp(y)  # y = m 2**e with 0.5 <= |m| < 1
+        normal = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+        sub = np.ldexp(np.rint(np.ldexp(y, 133)), -133)
+        out = np.where(np.abs(y) < 2.0 ** -126, sub, normal)
+        out = np.where(np.abs(out) >= 2.0 ** 128, np.copysign(np.inf, y), out)
+    return np.where(np.isfinite(y), out, y)
+
+
+def chain(calls, dtype: str, mode: int = GATED) -> list:
+    """Gated calls evaluated in order, where a call may read the output of an
+    earlier one (the maps of consecutive transformer layers, GSI-TS §2.3 and
+    §3: the gate is applied to every linear map, each fed by the ones before).
+
+    Each call is a dict with W, V, M, eps and either "x" (its own token) or
+    "src" = (j, offset): its input is the stored output of call j < i, i.e.
+    to_storage(y_j, dtype), from element `offset` on, d elements long.
+    Returns, per call, the linear_token result plus "x" (the input used).
+    """
+    out = []
+    for i, c in enumerate(calls):
+        if "src" in c:
+            j, off = c["src"]
+            if not 0 <= j < i:
+                raise ValueError(f"call {i} reads call {j}, which does not come before it")
+            d = _f64(c["V"]).shape[0]
+            x = to_storage(out[j]["y"], dtype)[off:off + d]
+            if x.shape[0] != d:
+                raise ValueError(f"call {i}: slice [{off}, {off + d}) beyond the output of call {j}")
+        else:
+            x = _f64(c["x"])
+        r = linear_token(c["W"], c["V"], c["M"], x, c["eps"], mode)
+        r["x"] = x
+        out.append(r)
+    return out
 
 
 def stack(calls, mode: int = GATED) -> list:

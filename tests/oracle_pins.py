@@ -320,8 +320,89 @@ def pin_nested_bases(orc):
         assert orc.residual_ratio(x, orc.residual(V, x, orc.project(V, x))) < 1e-12
 
 
+def pin_storage_rounding(orc):
+    """Rounding into the storage type: torch's float32 -> bfloat16 conversion
+    (round to nearest even) on float32 values across the whole exponent
+    range, closed-form ties, subnormals, overflow and non-finite values."""
+    rng = _rng(26)
+    x = rng.standard_normal(20000) * np.exp(rng.uniform(-88.0, 88.0, 20000))
+    x = np.concatenate([x, rng.standard_normal(2000) * 2.0 ** -128])  # bf16 subnormal range
+    x = x.astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    got = orc.to_storage(x, "bf16")
+    assert np.array_equal(got, want), f"bf16: {np.sum(got != want)} values differ from torch"
+    u = 2.0 ** -7  # spacing of bf16 in [1, 2)
+    ties = {1 + u / 2: 1.0, 1 + 3 * u / 2: 1 + 2 * u, -(1 + u / 2): -1.0, 2.0 ** -133 * 1.5: 2.0 ** -132,
+            2.0 ** -133 * 0.5: 0.0, (2 - u) * 2.0 ** 127: (2 - u) * 2.0 ** 127,
+            (2 - u / 2) * 2.0 ** 127: np.inf, 1 + u / 4: 1.0, 1 + 3 * u / 4: 1 + u}
+    for v, w in ties.items():
+        assert orc.to_storage(np.array([v]), "bf16")[0] == w, f"bf16({v!r}) != {w!r}"
+    sp = orc.to_storage(np.array([np.nan, np.inf, -np.inf, 0.0]), "bf16")
+    assert np.isnan(sp[0]) and sp[1] == np.inf and sp[2] == -np.inf and sp[3] == 0.0
+    y = rng.standard_normal(1000)
+    assert np.array_equal(orc.to_storage(y, "fp32"), y.astype(np.float32).astype(np.float64))
+
+
+def pin_chain(orc):
+    """Calls reading earlier stored outputs (GSI-TS §2.3, §3).
+
+    With k = d the gate is always fast and M g = W V V^T x = W x, so each
+    output has the closed form W x with x the stored (rounded) slice of the
+    producer's output; with the identity basis the gate of a chained call
+    is decided by the tail of its stored input, rho = ||x[k:]|| / ||x||.
+    """
+    rng = _rng(27)
+    d = 32
+    for dt in ("fp32", "bf16"):
+        W = [rng.standard_normal((2 * d, d)), rng.standard_normal((d, d)), rng.standard_normal((3 * d, d)),
+             rng.standard_normal((d, d))]
+        V = [_orthonormal(rng, d, d) for _ in W]
+        x0 = rng.standard_normal(d)
+        calls = [{"W": W[0], "V": V[0], "M": orc.prepare(W[0], V[0]), "eps": 0.05, "x": x0},
+                 {"W": W[1], "V": V[1], "M": orc.prepare(W[1], V[1]), "eps": 0.05, "src": (0, d)},
+                 {"W": W[2], "V": V[2], "M": orc.prepare(W[2], V[2]), "eps": 0.05, "src": (1, 0)},
+                 {"W": W[3], "V": V[3], "M": orc.prepare(W[3], V[3]), "eps": 0.05, "src": (0, 0)}]
+        res = orc.chain(calls, dt)
+        y0 = W[0] @ x0
+        x1 = orc.to_storage(y0, dt)[d:]
+        y1 = W[1] @ x1
+        x2 = orc.to_storage(y1, dt)
+        y2 = W[2] @ x2
+        x3 = orc.to_storage(y0, dt)[:d]
+        y3 = W[3] @ x3
+        for r, x, y, i in zip(res, (x0, x1, x2, x3), (y0, y1, y2, y3), range(4)):
+            assert not r["slow"], f"{dt} call {i}: full-rank basis must take the fast path"
+            assert np.array_equal(r["x"], x), f"{dt} call {i}: wrong input"
+            _close(r["y"], y, 1e-12, 1e-12, f"{dt} chain call {i}")
+        # identity basis: the chained call's gate follows the tail of its stored input
+        k = d // 2
+        E = np.eye(d)[:, :k]
+        A = rng.standard_normal((d, d))
+        B = rng.standard_normal((d, d))
+        xa = np.concatenate([rng.standard_normal(k), 0.5 * rng.standard_normal(d - k)])
+        cc = [{"W": A, "V": E, "M": orc.prepare(A, E), "eps": 0.05, "x": xa},
+              {"W": B, "V": E, "M": orc.prepare(B, E), "eps": 0.05, "src": (0, 0)}]
+        ra, rb = orc.chain(cc, dt)
+        assert ra["slow"]
+        _close(ra["y"], A @ xa, 1e-12, 1e-12, "slow producer")
+        xb = orc.to_storage(A @ xa, dt)
+        rho_b = np.linalg.norm(xb[k:]) / np.linalg.norm(xb)
+        _close(rb["rho"], rho_b, 1e-12, 0, "chained rho")
+        assert rb["slow"] == (not rho_b < 0.05)
+        _close(rb["y"], B @ xb if rb["slow"] else B[:, :k] @ xb[:k], 1e-12, 1e-12, "chained output")
+    for bad in ({"src": (1, 0)}, {"src": (0, 3 * d)}):
+        c = [calls[0], dict(calls[1], **bad)]
+        c[1].pop("x", None)
+        try:
+            orc.chain(c, "fp32")
+        except ValueError:
+            continue
+        raise AssertionError(f"chain accepted {bad}")
+
+
 ALL_PINS = [
     pin_identity_basis, pin_full_rank, pin_in_span_and_orthogonal, pin_construction,
     pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
     pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity, pin_nested_bases,
+    pin_storage_rounding, pin_chain,
 ]

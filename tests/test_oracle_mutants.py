@@ -48,7 +48,56 @@ MUTANTS = {
     "slow_drop_term": ("slow_output", lambda W, x: f64(W)[:, :-1] @ f64(x)[:-1]),
     "slow_uses_image": ("linear_token", None),
     "batch_drops_token": ("linear", None),
+    # storage rounding: truncation, ties away from zero, bf16 kept as fp32
+    "storage_truncates": ("to_storage", None),
+    "storage_ties_away": ("to_storage", None),
+    "storage_bf16_as_fp32": ("to_storage", None),
+    # chains: exact instead of stored input, offset ignored, wrong producer
+    "chain_unrounded_input": ("chain", None),
+    "chain_ignores_offset": ("chain", None),
+    "chain_reads_previous_call": ("chain", None),
 }
+
+
+def _mutant_to_storage(mod, how):
+    orig = mod.to_storage
+
+    def to_storage(y, dtype):
+        y = f64(y)
+        if dtype != "bf16" or how == "as_fp32":
+            return y.astype(np.float32).astype(np.float64)
+        m, e = np.frexp(y)
+        t = np.ldexp(m, 8)
+        r = np.trunc(t) if how == "trunc" else np.sign(t) * np.floor(np.abs(t) + 0.5)
+        out = np.ldexp(r, e - 8)
+        return np.where(np.isfinite(y), out, orig(y, dtype))
+    return to_storage
+
+
+def _mutant_chain(mod, how):
+    def chain(calls, dtype, mode=0):
+        out = []
+        for i, c in enumerate(calls):
+            if "src" in c:
+                j, off = c["src"]
+                if not 0 <= j < i:
+                    raise ValueError("bad producer")
+                if how == "previous":
+                    j = i - 1
+                if how == "no_offset":
+                    off = 0
+                d = f64(c["V"]).shape[0]
+                y = out[j]["y"] if how == "unrounded" else mod.to_storage(out[j]["y"], dtype)
+                x = y[off:off + d]
+                if x.shape[0] != d:
+                    raise ValueError("slice")
+            else:
+                x = f64(c["x"])
+            r = mod.linear_token(c["W"], c["V"], c["M"], x, c["eps"], mode)
+            r["x"] = x
+            out.append(r)
+        return out
+    return chain
 
 
 def _mutant_linear_token(mod):
@@ -79,6 +128,12 @@ def test_pins_catch_mutant(name):
         fn = _mutant_linear_token(mod)
     elif name == "batch_drops_token":
         fn = _mutant_linear(mod, mod.linear)
+    elif name.startswith("storage_"):
+        fn = _mutant_to_storage(mod, {"storage_truncates": "trunc", "storage_ties_away": "away",
+                                      "storage_bf16_as_fp32": "as_fp32"}[name])
+    elif name.startswith("chain_"):
+        fn = _mutant_chain(mod, {"chain_unrounded_input": "unrounded", "chain_ignores_offset": "no_offset",
+                                 "chain_reads_previous_call": "previous"}[name])
     setattr(mod, attr, fn)
     caught = []
     with np.errstate(all="ignore"):

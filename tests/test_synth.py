@@ -78,3 +78,21 @@ def test_spectral_tokens_follow_the_power_law():
     # the part outside span([v | u]) is empty
     resid = X - (X @ v) @ v.T - (X @ u) @ u.T
     assert float(resid.norm() / X.norm()) < 1e-12
+
+
+def test_subspace_map_carries_subspace_and_keeps_ratio():
+    d_in, d_out, k_in, k_out = 256, 384, 16, 24
+    v_in, u_in = synth.orthonormal_frame(d_in, k_in, 64, (8, 0, 0, 1))
+    v_out, _ = synth.orthonormal_frame(d_out, k_out, 0, (8, 0, 0, 2))
+    W = synth.subspace_map(v_in, v_out, (8, 0, 0, 3), dtype=torch.float32).double()
+    # the basis of the input lands inside the basis of the output
+    img = W @ v_in
+    assert torch.linalg.matrix_norm(img - v_out @ (v_out.T @ img)) < 1e-5 * torch.linalg.matrix_norm(img)
+    # tokens keep their residual ratio approximately
+    mask = torch.tensor([False] * 20 + [True] * 20)
+    X, rho_built = synth.tokens(v_in, u_in, mask, (8, 0, 0))
+    Y = X @ W.T
+    rho_in = torch.linalg.vector_norm(X - (X @ v_in) @ v_in.T, dim=1) / torch.linalg.vector_norm(X, dim=1)
+    rho_out = torch.linalg.vector_norm(Y - (Y @ v_out) @ v_out.T, dim=1) / torch.linalg.vector_norm(Y, dim=1)
+    ratio = rho_out / rho_in
+    assert float(ratio.min()) > 0.5 and float(ratio.max()) < 2.0, ratio
