@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=512)
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default="gptj6b-28L",
-                   choices=["gptj6b-28L", "llama13b-40L", "batched-t256", "sweep"])
+                   choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -90,6 +90,68 @@ def build_workload(name, layers_override, dev):
                 outs=outs, plans=plans)
 
 
+class _Shape:
+    """d, d_out, k of one call, for byte accounting."""
+
+    def __init__(self, d, d_out, k):
+        self.d, self.d_out, self.k = d, d_out, k
+
+
+def build_chained_workload(layers_override, dev):
+    """GPT-J-shaped layers whose maps feed each other: one decode step is one
+    token through 28 parallel blocks as 56 waves (qkv and fc_in on the layer
+    input; out on the value third of qkv's output, fc_out on fc_in's output,
+    which is the next layer's input), one gsi_stack launch with device-side
+    barriers between the waves.  Weights carry each layer's input subspace to
+    the next (synth.subspace_map), so the slow share set at the first layer
+    (5% of the steps) carries down the stack."""
+    import torch
+
+    from rank_gated_memory_amd import gsi, synth
+
+    layers = layers_override or 28
+    steps, rate = 512, 0.05
+    d, k, f, kf = 4096, 256, 16384, 512
+    t0 = time.perf_counter()
+    cfg, (vh0, uh0) = synth.chain_config(d, k, f, kf, layers, (6, 0), device=dev, dtype=torch.bfloat16)
+    mask = synth.pick_slow(steps, int(round(rate * steps)), (6, 0, 0, synth.P_PICK), dev)
+    X0, _ = synth.tokens(vh0, uh0, mask, (6, 0, 0))
+    X0 = X0.to(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"chained inputs drawn in {time.perf_counter() - t0:.1f}s")
+    roles = (("qkv", d, 3 * d, k), ("out", d, d, k), ("fc_in", d, f, k), ("fc_out", f, d, kf))
+    maps = [{r: gsi.Map(*layer.maps[r]) for r, *_ in roles} for layer in cfg]
+    for row in maps:
+        for m in row.values():
+            gsi.gsi_prepare(m)
+    outs = [{r: (torch.empty((steps, m.d_out), dtype=torch.bfloat16, device=dev),
+                 torch.empty(steps, dtype=torch.float32, device=dev),
+                 torch.zeros(steps, dtype=torch.uint8, device=dev)) for r, m in row.items()} for row in maps]
+    plans = []
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        calls, h = [], X0[s_]
+        for l in range(layers):
+            mp, o = maps[l], outs[l]
+            for r in ("qkv", "fc_in"):
+                Y, R, S = o[r]
+                calls.append((mp[r], h, Y[s_], 0.05, R[s_:s_ + 1], S[s_:s_ + 1], 2 * l))
+            Y, R, S = o["out"]
+            calls.append((mp["out"], o["qkv"][0][s_, 2 * d:3 * d], Y[s_], 0.05, R[s_:s_ + 1], S[s_:s_ + 1], 2 * l + 1))
+            Y, R, S = o["fc_out"]
+            calls.append((mp["fc_out"], o["fc_in"][0][s_], Y[s_], 0.05, R[s_:s_ + 1], S[s_:s_ + 1], 2 * l + 1))
+            h = Y[s_]
+        plans.append(gsi.Stack(calls, device=dev))
+    torch.cuda.synchronize()
+    log(f"{steps} chained plans of {len(plans[0]._keep)} calls built in {time.perf_counter() - t0:.2f}s")
+    order = ("qkv", "fc_in", "out", "fc_out")  # the call order inside a layer of a plan
+    dims = {r: (dd, do, kk) for r, dd, do, kk in roles}
+    data = [[_Shape(*dims[r]) for r in order] for _ in range(layers)]
+    flat_outs = [[outs[l][r] for r in order] for l in range(layers)]
+    return dict(cfg=6, layers=layers, roles=[(r, *dims[r]) for r in order], steps=steps, rate=rate,
+                data=data, maps=maps, outs=flat_outs, plans=plans, chained=True, host_cfg=cfg, X0=X0)
+
+
 def step_bytes(wl, step_slow):
     """Algorithmic bytes of one step split by phase, given its gate per map."""
     from rank_gated_memory_amd import accounting as acc
@@ -103,6 +165,66 @@ def step_bytes(wl, step_slow):
             apply += acc.apply_bytes(mi.d, mi.d_out, mi.k, 2, slow)
             i += 1
     return proj, apply
+
+
+def cpu_baseline_chained(wl, seconds):
+    """The fp64 oracle chain on a bounded sample: the first two layers (8
+    chained calls) of each step, steps in order, time scaled to all layers."""
+    import numpy as np
+    import torch
+
+    from oracle import gsi_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    d = 4096
+    host = []
+    for l in range(2):
+        mp = {}
+        for r, (W, V) in wl["host_cfg"][l].maps.items():
+            Wf = W.to("cpu", torch.float64).numpy()
+            Vf = V.to("cpu", torch.float64).numpy()
+            mp[r] = (Wf, Vf, orc.prepare(Wf, Vf))
+        host.append(mp)
+    X0 = wl["X0"].to("cpu", torch.float64).numpy()
+
+    def calls_for(s_):
+        cs = []
+        h_src = None  # index of the call whose output is the layer input
+        for l in range(2):
+            idx = {}
+            for r in ("qkv", "fc_in"):
+                W, V, M = host[l][r]
+                c = {"W": W, "V": V, "M": M, "eps": 0.05}
+                if h_src is None:
+                    c["x"] = X0[s_]
+                else:
+                    c["src"] = (h_src, 0)
+                idx[r] = len(cs)
+                cs.append(c)
+            W, V, M = host[l]["out"]
+            cs.append({"W": W, "V": V, "M": M, "eps": 0.05, "src": (idx["qkv"], 2 * d)})
+            W, V, M = host[l]["fc_out"]
+            h_src = len(cs)
+            cs.append({"W": W, "V": V, "M": M, "eps": 0.05, "src": (idx["fc_in"], 0)})
+        return cs
+
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        orc.chain(calls_for(done % wl["steps"]), "bf16")
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    maps_total = sum(len(r) for r in wl["data"])
+    per_step = el / done * (maps_total / 8)
+    return {"value": 1.0 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} decode steps (in order) through the first 2 of {wl['layers']} chained layers "
+                      f"(8 of {maps_total} maps), fp64 numpy, {el:.1f}s; step time scaled by {maps_total}/8 maps"}
 
 
 def cpu_baseline(wl, seconds):
@@ -342,7 +464,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     gsi.lib()
-    wl = build_workload(args.workload, args.layers, dev)
+    if args.workload == "gptj6b-28L-chained":
+        wl = build_chained_workload(args.layers, dev)
+    else:
+        wl = build_workload(args.workload, args.layers, dev)
+    chained = bool(wl.get("chained"))
     plans = wl["plans"]
     S = wl["steps"]
     ws = gsi.workspace(max(p.ws_bytes for p in plans), dev)
@@ -385,23 +511,41 @@ def main():
     total_bytes = float((proj_b[idx] + apply_b[idx]).sum())
     step_gbps = total_bytes / wall / 1e9
 
-    # ---- per-kernel pass: HIP events around each phase on the launch stream ----
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # ---- per-launch pass: HIP events around each gsi_stack on the launch stream ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
-        p = plans[i % S]
         evs[i][0].record(stream)
-        gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_PROJECT, ws)
+        gsi.gsi_stack(plans[i % S], gsi.GATED, ws)
         evs[i][1].record(stream)
-        gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_APPLY, ws)
-        evs[i][2].record(stream)
     torch.cuda.synchronize()
-    t_proj = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_apply = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    proj_gbps = float(proj_b[idx].sum() / t_proj.sum() / 1e9)
-    apply_gbps = float(apply_b[idx].sum() / t_apply.sum() / 1e9)
-    log(f"proj_kernel  mean {t_proj.mean() * 1e6:.1f} us, {proj_gbps:.0f} GB/s")
-    log(f"apply_kernel mean {t_apply.mean() * 1e6:.1f} us, {apply_gbps:.0f} GB/s")
+    t_stack = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    step_b = proj_b[idx] + apply_b[idx]
+    stack_gbps = float(step_b.sum() / t_stack.sum() / 1e9)
+    log(f"stack_kernel mean {t_stack.mean() * 1e6:.1f} us, {stack_gbps:.0f} GB/s")
+    two_launch = None
+    if not chained:
+        # the same steps as two launches (projection, then outputs): context
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            p = plans[i % S]
+            evs[i][0].record(stream)
+            gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_PROJECT, ws)
+            evs[i][1].record(stream)
+            gsi.gsi_stack_phase(p, gsi.GATED, gsi.PHASE_APPLY, ws)
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        t_proj = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+        t_apply = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+        two_launch = {
+            "us_per_step": float((t_proj + t_apply).mean() * 1e6),
+            "proj_kernel": {"gbps": float(proj_b[idx].sum() / t_proj.sum() / 1e9),
+                            "mean_us": float(t_proj.mean() * 1e6), "bytes_per_launch": float(proj_b[idx].mean())},
+            "apply_kernel": {"gbps": float(apply_b[idx].sum() / t_apply.sum() / 1e9),
+                             "mean_us": float(t_apply.mean() * 1e6), "bytes_per_launch": float(apply_b[idx].mean())},
+        }
+        log(f"two launches: {two_launch['us_per_step']:.1f} us per step (proj {t_proj.mean() * 1e6:.1f}, "
+            f"apply {t_apply.mean() * 1e6:.1f})")
 
     # ---- dense baseline (same kernels, every token slow) and static projection ----
     D = max(1, args.dense_steps)
@@ -430,7 +574,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = (cpu_baseline_chained if chained else cpu_baseline)(wl, args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
 
     maps_per_step = sum(len(r) for r in wl["data"])
@@ -449,8 +593,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {wl['layers']} layers x {len(wl['roles'])} maps "
-                        f"({maps_per_step} gated batch-1 calls per step), "
-                        f"{wl['rate'] * 100:.0f}% slow tokens per map, eps=0.05",
+                        f"({maps_per_step} gated batch-1 calls per step"
+                        + (f" in {2 * wl['layers']} dependent waves" if chained else "") + "), "
+                        f"{wl['rate'] * 100:.0f}% slow tokens" + (" at the first layer" if chained else " per map")
+                        + ", eps=0.05",
             "layers": wl["layers"],
             "maps": [[n, d, o, k] for n, d, o, k in wl["roles"]],
             "distinct_steps": S,
@@ -461,21 +607,16 @@ def main():
         "bytes_per_step": total_bytes / K,
         "roofline": {
             "bound": "hbm",
-            "kernel": "apply_kernel",
-            "achieved": apply_gbps,
+            "kernel": "stack_kernel",
+            "achieved": stack_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": apply_gbps / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(args.workload, "apply_kernel"),
-            "bytes_per_launch": float(apply_b[idx].mean()),
-            "mean_launch_us": float(t_apply.mean() * 1e6),
+            "frac": stack_gbps / PEAK_HBM_GBPS,
+            "traffic": measured_traffic(args.workload, "stack_kernel"),
+            "bytes_per_launch": float(step_b.mean()),
+            "mean_launch_us": float(t_stack.mean() * 1e6),
         },
-        "kernels": {
-            "proj_kernel": {"gbps": proj_gbps, "mean_us": float(t_proj.mean() * 1e6),
-                            "bytes_per_launch": float(proj_b[idx].mean())},
-            "apply_kernel": {"gbps": apply_gbps, "mean_us": float(t_apply.mean() * 1e6),
-                             "bytes_per_launch": float(apply_b[idx].mean())},
-        },
+        "two_launch": two_launch,
         "dense_tokens_per_s": dense_tok_s,
         "speedup_vs_dense": tok_s / dense_tok_s,
         "all_fast_tokens_per_s": K / fast_wall,
