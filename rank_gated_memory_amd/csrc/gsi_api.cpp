@@ -339,6 +339,40 @@ static int64_t plan_proj_target(int64_t total_v_bytes) {
   return t;
 }
 
+// Unit shapes of every call of a (validated) plan, chosen wave by wave.
+// A wave's projection units aim at (its V_k bytes) / 1024, clamped to
+// [16 KiB, GSI_PLAN_PROJ_UNIT_KB], and at most kMaxPartials per call (the
+// final sum of a call's partials is then one round of loads).  A wave whose fast
+// outputs make fewer than kFineUnits ordinary units is latency-bound (the
+// waves of a dependency-chained stack): it takes the smallest output units.
+constexpr int64_t kFineUnits = 1024;
+#ifndef GSI_PLAN_MAX_PARTIALS
+#define GSI_PLAN_MAX_PARTIALS 64
+#endif
+constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
+
+static std::vector<UnitShape> call_shapes(const gsi_call *calls, int32_t n, int es) {
+  std::vector<UnitShape> shapes(n);
+  for (int32_t b = 0; b < n;) {
+    int32_t e = b + 1;
+    while (e < n && calls[e].wave == calls[b].wave) ++e;
+    int64_t vbytes = 0, fast_units = 0;
+    for (int32_t i = b; i < e; ++i) {
+      vbytes += (int64_t)calls[i].map.d * calls[i].map.k * es;
+      fast_units += unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, 1 << 20).fast_units;
+    }
+    const int64_t t = plan_proj_target(vbytes);
+    const bool fine = fast_units < kFineUnits;
+    for (int32_t i = b; i < e; ++i) {
+      const int64_t vi = (int64_t)calls[i].map.d * calls[i].map.k * es;
+      const int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
+      shapes[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, ti, fine);
+    }
+    b = e;
+  }
+  return shapes;
+}
+
 static gsi_status plan_sizes(const gsi_call *calls, int32_t n, int64_t *units_a,
                              int64_t *target, size_t *bytes, int32_t *n_waves) {
   if (n < 0 || n > kMaxCalls) return GSI_E_SHAPE;
@@ -361,15 +395,10 @@ static gsi_status plan_sizes(const gsi_call *calls, int32_t n, int64_t *units_a,
     b = e;
   }
   *n_waves = waves;
-  const int64_t t = plan_proj_target(vbytes);
   int64_t ua = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const UnitShape us =
-        unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, esize_of(dtype), t);
-    ua += us.a_units;
-  }
+  for (const UnitShape &us : call_shapes(calls, n, esize_of(dtype))) ua += us.a_units;
   *units_a = ua;
-  *target = t;
+  *target = plan_proj_target(vbytes);
   const uint64_t desc_off = align_up(sizeof(PlanHeader), 128);
   const uint64_t unit_off = desc_off + (uint64_t)n * sizeof(CallDesc);
   const uint64_t order_off = align_up(unit_off + (uint64_t)ua * 4, 16);
@@ -420,9 +449,9 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   }
   std::vector<int32_t> order(n);
   for (int32_t i = 0; i < n; ++i) order[i] = i;
+  const std::vector<UnitShape> shapes = call_shapes(calls, n, es);
   std::vector<int32_t> nunits(n);
-  for (int32_t i = 0; i < n; ++i)
-    nunits[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, target).a_units;
+  for (int32_t i = 0; i < n; ++i) nunits[i] = shapes[i].a_units;
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
     if (wave_of[x] != wave_of[y]) return wave_of[x] < wave_of[y];
     return nunits[x] > nunits[y];
@@ -439,7 +468,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   int32_t max_k = 8, max_d = 8, units_max = 1;
   for (int32_t i = 0; i < n; ++i) {
     const gsi_call &c = calls[i];
-    const UnitShape us = unit_shape(c.map.d, c.map.d_out, c.map.k, es, target);
+    const UnitShape &us = shapes[i];
     a_begin = first_unit[i];
     CallDesc &o = desc[i];
     o.W = c.map.W;

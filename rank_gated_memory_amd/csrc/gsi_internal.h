@@ -37,7 +37,8 @@ struct alignas(16) CallDesc {
   int64_t part_off;    // float offset in the workspace of the partials [a_units][k + 4]
   int64_t g_off;       // float offset in the workspace of g [k]
   int32_t gate_off;    // index of this call's gate record / counter
-  int32_t fast_tiles;  // 64-row image tiles per fast output unit (multiple of kWaves)
+  int32_t fast_tiles;  // 64-row image tiles per fast output unit (multiple of kWaves, or 1:
+                       // one tile whose columns are split over the wavefronts)
   int32_t flags;       // kCallXCoherent | kCallYCoherent
   int32_t wave;        // wave of the call in a stack (0 for independent calls)
 };
@@ -84,11 +85,15 @@ constexpr int kCtlStatus = 0;       // sticky: nonzero once a device-side wait r
 constexpr int kCtlExit = 32;        // workgroups that have left the work loop
 constexpr int kCtlSeg = 64;         // first work segment not known to be exhausted
 constexpr int kCtlWave0 = 96;       // per wave: kCtlWaveWords words, then the open lists
-constexpr int kCtlWaveWords = 128;  // four lines per wave:
-constexpr int kWvProj = 0;          //   projection tickets taken
-constexpr int kWvOut = 32;          //   output tickets taken
-constexpr int kWvOpen = 64;         //   open word (64-bit): calls open << 40 | their output units
-constexpr int kWvDone = 96;         //   output units finished (waves with a successor)
+// Ticket and completion counters are split into kGroups copies, one per
+// group of workgroups (blockIdx % kGroups), each on its own line: one
+// address taking every workgroup's atomics serialises them (~13 ns each).
+constexpr int kGroups = 8;
+constexpr int kCtlWaveWords = (3 * kGroups + 1) * 32;
+constexpr int kWvProj = 0;               // + 32 g: projection tickets taken by group g
+constexpr int kWvOut = 32 * kGroups;     // + 32 g: output tickets taken by group g
+constexpr int kWvDone = 64 * kGroups;    // + 32 g: output units finished by group g
+constexpr int kWvOpen = 96 * kGroups;    // open word (64-bit): calls open << 40 | their output units
 // After the wave blocks: the open list, one 64-bit entry per call, indexed by
 // the wave's first a_order slot plus the order in which the call's gate
 // opened: base | need << 32 | slow << 50 | (call + 1) << 51, where base is
@@ -171,7 +176,13 @@ struct UnitShape {
 #endif
 constexpr int64_t kApplyUnitBytes = GSI_APPLY_UNIT_KB * 1024;
 
-inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_proj_bytes) {
+// fine: latency-bound waves (few bytes per wave) take the smallest fast
+// output units, one 64-row image tile whose columns are split over the
+// wavefronts of a workgroup, so that every workgroup of the launch gets a
+// share of a small wave.  Slow units keep their size: a slow call reads all
+// of W and is bandwidth-bound even alone.
+inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_proj_bytes,
+                            bool fine = false) {
   UnitShape s{};
   const int64_t row_bytes = (int64_t)k * esize;
   int64_t rows = target_proj_bytes / row_bytes;
@@ -186,6 +197,7 @@ inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_p
   ft = (ft + kWaves - 1) / kWaves * kWaves;
   if (ft < kWaves) ft = kWaves;
   if (ft > 8 * kWaves) ft = 8 * kWaves;
+  if (fine) ft = 1;
   s.fast_tiles = (int32_t)ft;
   s.fast_units = (int32_t)((tiles + ft - 1) / ft);
   int64_t srows = kApplyUnitBytes / ((int64_t)d * esize);

@@ -300,6 +300,13 @@ __device__ __forceinline__ int finish_gate(const CallDesc &cd, const float *wsf,
   for (int j = tid; j < k; j += kBlock) {
     float s = 0.f;
     int qq = 0;
+    for (; qq + 64 <= cd.a_units; qq += 64) {
+      float t[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s += t[i];
+    }
     for (; qq + 32 <= cd.a_units; qq += 32) {
       float t[32];
 #pragma unroll
@@ -383,8 +390,59 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 // Output: fast units (y = M g) and slow units (y = W x) of the chosen paths.
 // ---------------------------------------------------------------------------
+// Fast unit of one 64-row tile: wavefront w takes the 16-byte column
+// vectors w, w + kWaves, ... of every row (one row per lane) and the four
+// partial sums meet in LDS (`scr`, kWaves x 64 floats), added in wavefront
+// order.  Used by latency-bound waves, where a unit must be small.
 template <typename T, int UNROLL>
-__device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const float *gs) {
+__device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, const float *gs,
+                                                float *scr) {
+  constexpr int VW = Vec<T>::VW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int kv = cd.k / VW;
+  const uint4 *m = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * kTileRows * kv + lane;
+  float a0 = 0.f, a1 = 0.f;
+  for (int cg0 = wave; cg0 < kv; cg0 += kWaves * UNROLL) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int cg = cg0 + j * kWaves;
+      v[j] = cg < kv ? m[(size_t)cg * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int cg = cg0 + j * kWaves;
+      if (cg < kv) {
+        float f[VW];
+        Vec<T>::unpack(v[j], f);
+        const float *gp = gs + cg * VW;
+#pragma unroll
+        for (int e = 0; e < VW; e += 2) {
+          a0 = fmaf(f[e], gp[e], a0);
+          a1 = fmaf(f[e + 1], gp[e + 1], a1);
+        }
+      }
+    }
+  }
+  scr[wave * 64 + lane] = a0 + a1;
+  __syncthreads();
+  if (wave == 0) {
+    float t = scr[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += scr[w * 64 + lane];
+    const int o = tile * kTileRows + lane;
+    if (o < cd.d_out) store_y<T>(cd, o, t);
+  }
+  __syncthreads();  // scr is free again
+}
+
+template <typename T, int UNROLL>
+__device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const float *gs, float *scr) {
+  if (cd.fast_tiles == 1) {
+    fast_tile_split<T, UNROLL>(cd, local, gs, scr);
+    return;
+  }
   constexpr int VW = Vec<T>::VW;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -491,6 +549,8 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
   int *pref = reinterpret_cast<int *>(smem);
   float *gs = reinterpret_cast<float *>(smem + pref_bytes);
   uint4 *xs = reinterpret_cast<uint4 *>(smem + pref_bytes + g_bytes);
+  float *scr = reinterpret_cast<float *>(smem + pref_bytes + g_bytes +
+                                         align_up((uint64_t)a.max_d * sizeof(T), 16));
 
   // Prefix over calls of the units their chosen path needs (written by the
   // projection launch).
@@ -538,7 +598,7 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
     if (slow)
       slow_unit<T, UNROLL>(cd, local, xs);
     else
-      fast_unit<T, UNROLL>(cd, local, gs);
+      fast_unit<T, UNROLL>(cd, local, gs, scr);
   }
 }
 
@@ -630,10 +690,21 @@ struct Sched {
   int last_out;   // the last job was an output unit
   int pf;         // ticket to fetch while the job runs: 1 projection, 2 output
   int slot;       // first open-list slot that may hold the output ticket
+  int done;       // output units of wave w finished by this workgroup, not yet reported
   uint32_t tp;    // projection ticket held
   uint32_t to;    // output ticket held
   uint64_t open;  // last open word seen for wave w
 };
+
+// Tickets of a wave: the first of each kind is the workgroup's index; the
+// later ones of group g = blockIdx % kGroups are gridDim + kGroups * j + g
+// for j = 0, 1, ... taken from group g's counter.  Every ticket from the
+// grid size on belongs to exactly one group, whose workgroups take its
+// tickets in order until they pass the wave's count.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr0) {
+  const uint32_t g = blockIdx.x % kGroups;
+  return gridDim.x + kGroups * ctl_add(ctr0 + 32 * g, 1u) + g;
+}
 
 __device__ __forceinline__ uint32_t *wave_ctl(const FArgs &a, int w) {
   return a.ctl + kCtlWave0 + w * kCtlWaveWords;
@@ -688,7 +759,10 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
           uint32_t ok = 0;
           if (lane == 0) {
             const uint64_t ow = ctl_load64(reinterpret_cast<const uint64_t *>(pv + kWvOpen));
-            ok = (ow >> 40) == pcalls && ctl_load(pv + kWvDone) == (uint32_t)(ow & kLow40);
+            uint32_t fin = 0;
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) fin += ctl_load(pv + kWvDone + 32 * g);
+            ok = (ow >> 40) == pcalls && fin == (uint32_t)(ow & kLow40);
           }
           if (bcast(ok)) break;
           if (s >= a.spin_limit) return sched_fail(a, 1, job);
@@ -757,11 +831,17 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
         if (base_slot + 64 >= nopen) return sched_fail(a, 4, job);  // cannot happen: to < open units
       }
     }
+    if ((uint32_t)(st.open >> 40) == ncalls && !(st.p_held && (int)bcast(st.tp) < np)) {
+      // every gate of the wave is open, so every projection unit is done
+      // and no projection ticket need be taken
+      st.p_out = 1;
+      st.p_held = 0;
+    }
     if (!st.p_out) {
       // ---- projection unit ----
       if (!st.p_held) {
         uint32_t t = 0;
-        if (lane == 0) t = gridDim.x + ctl_add(wv + kWvProj, 1u);
+        if (lane == 0) t = take_ticket(wv + kWvProj);
         st.tp = t;
       }
       const uint32_t tp = bcast(st.tp);
@@ -775,6 +855,11 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
       st.p_out = 1;
     }
     if ((uint32_t)(st.open >> 40) == ncalls) {  // every gate open and `to` beyond the last unit
+      // the outputs this workgroup wrote in the wave have landed (each
+      // output unit of a wave with a successor ends with s_waitcnt 0 and a
+      // barrier): count them for the next wave's entry
+      if (lane == 0 && st.done) ctl_add(wv + kWvDone + 32 * (blockIdx.x % kGroups), (uint32_t)st.done);
+      st.done = 0;
       st.w += 1;
       st.entered = 0;
       continue;
@@ -791,10 +876,10 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
 // next_job reads; the state flags stay uniform over the wavefront).
 __device__ __forceinline__ void sched_prefetch(const FArgs &a, Sched &st) {
   if (st.pf == 1) {
-    if (threadIdx.x == 0) st.tp = gridDim.x + ctl_add(wave_ctl(a, st.w) + kWvProj, 1u);
+    if (threadIdx.x == 0) st.tp = take_ticket(wave_ctl(a, st.w) + kWvProj);
     st.p_held = 1;
   } else if (st.pf == 2) {
-    if (threadIdx.x == 0) st.to = gridDim.x + ctl_add(wave_ctl(a, st.w) + kWvOut, 1u);
+    if (threadIdx.x == 0) st.to = take_ticket(wave_ctl(a, st.w) + kWvOut);
   }
 }
 
@@ -819,9 +904,10 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   // block; projection units use it for their column partials.
   uint4 *xs = reinterpret_cast<uint4 *>(smem);
   float *gs = reinterpret_cast<float *>(smem + align_up((uint64_t)a.max_d * sizeof(T), 16));
+  float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
   int cur = -1, cur_slow = 0;
   for (;;) {
     if (tid < 64) next_job(a, st, s_job);
@@ -884,12 +970,13 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
       if (slow)
         slow_unit<T, UNROLL>(cd, u, xs);
       else
-        fast_unit<T, UNROLL>(cd, u, gs);
+        fast_unit<T, UNROLL>(cd, u, gs, scr);
       if (cd.wave + 1 < a.n_waves) {
-        // a later wave may read this y: count the unit once its stores landed
+        // a later wave may read this y: the unit counts once its stores
+        // landed (reported when the workgroup leaves the wave)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) ctl_add(wave_ctl(a, cd.wave) + kWvDone, 1u);
+        st.done += 1;
       }
     }
   }
@@ -984,7 +1071,7 @@ hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int 
 
 size_t apply_lds_bytes(const KArgs &a, int esize) {
   return align_up((uint64_t)(a.n + 1) * 4, 16) + align_up((uint64_t)a.max_k * 4, 16) +
-         align_up((uint64_t)a.max_d * esize, 16);
+         align_up((uint64_t)a.max_d * esize, 16) + kWaves * 64 * 4;
 }
 
 #ifndef GSI_PROJ_UNROLL
@@ -1012,7 +1099,8 @@ void launch_typed(const KArgs &a, int grid_b, int phases, size_t lds, hipStream_
 }
 
 size_t stack_lds_bytes(int max_d, int max_k, int esize) {
-  const size_t out = align_up((uint64_t)max_d * esize, 16) + align_up((uint64_t)max_k * 4, 16);
+  const size_t out = align_up((uint64_t)max_d * esize, 16) + align_up((uint64_t)max_k * 4, 16) +
+                     kWaves * 64 * 4;
   const size_t proj = (size_t)kBlock * (16 / esize) * 4;
   return out > proj ? out : proj;
 }
