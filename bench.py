@@ -43,13 +43,16 @@ def parse():
     p.add_argument("--workload", default="gptj6b-28L",
                    choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--shared-bases", action="store_true",
+                   help="maps that read one input (GPT-J qkv and fc_in, LLaMA gate and up) share "
+                        "its tokens and basis, hence one projection")
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     return p.parse_args()
 
 
-def build_workload(name, layers_override, dev):
+def build_workload(name, layers_override, dev, shared=False):
     import torch
 
     from rank_gated_memory_amd import gsi, synth
@@ -58,7 +61,8 @@ def build_workload(name, layers_override, dev):
     if layers_override:
         layers = layers_override
     t0 = time.perf_counter()
-    data = synth.stack_config(cfg, layers, roles, steps, rate, device=dev, cascade=cascade)
+    data = synth.stack_config(cfg, layers, roles, steps, rate, device=dev, cascade=cascade,
+                              share=synth.SHARED_INPUTS[name] if shared else None)
     torch.cuda.synchronize()
     log(f"inputs drawn in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
@@ -91,10 +95,22 @@ def build_workload(name, layers_override, dev):
 
 
 class _Shape:
-    """d, d_out, k of one call, for byte accounting."""
+    """d, d_out, k of one call, for byte accounting; shared: the call reads
+    the projection of an earlier call with the same input and basis."""
 
-    def __init__(self, d, d_out, k):
-        self.d, self.d_out, self.k = d, d_out, k
+    def __init__(self, d, d_out, k, shared=False):
+        self.d, self.d_out, self.k, self.shared = d, d_out, k, shared
+
+
+def call_bytes(mi, slow):
+    """Algorithmic bytes of one call: V_k and x are not read again by a call
+    that shares an earlier call's projection."""
+    from rank_gated_memory_amd import accounting as acc
+
+    b = acc.token_bytes(mi.d, mi.d_out, mi.k, 2, slow)
+    if getattr(mi, "shared", False):
+        b -= acc.project_bytes(mi.d, mi.k, 2)
+    return b
 
 
 def build_chained_workload(layers_override, dev):
@@ -146,7 +162,8 @@ def build_chained_workload(layers_override, dev):
     log(f"{steps} chained plans of {len(plans[0]._keep)} calls built in {time.perf_counter() - t0:.2f}s")
     order = ("qkv", "fc_in", "out", "fc_out")  # the call order inside a layer of a plan
     dims = {r: (dd, do, kk) for r, dd, do, kk in roles}
-    data = [[_Shape(*dims[r]) for r in order] for _ in range(layers)]
+    # fc_in reads the same input with the same basis as qkv: one projection
+    data = [[_Shape(*dims[r], shared=(r == "fc_in")) for r in order] for _ in range(layers)]
     flat_outs = [[outs[l][r] for r in order] for l in range(layers)]
     return dict(cfg=6, layers=layers, roles=[(r, *dims[r]) for r in order], steps=steps, rate=rate,
                 data=data, maps=maps, outs=flat_outs, plans=plans, chained=True, host_cfg=cfg, X0=X0)
@@ -161,7 +178,8 @@ def step_bytes(wl, step_slow):
     for row in wl["data"]:
         for mi in row:
             slow = bool(step_slow[i])
-            proj += acc.project_bytes(mi.d, mi.k, 2)
+            if not getattr(mi, "shared", False):
+                proj += acc.project_bytes(mi.d, mi.k, 2)
             apply += acc.apply_bytes(mi.d, mi.d_out, mi.k, 2, slow)
             i += 1
     return proj, apply
@@ -467,7 +485,7 @@ def main():
     if args.workload == "gptj6b-28L-chained":
         wl = build_chained_workload(args.layers, dev)
     else:
-        wl = build_workload(args.workload, args.layers, dev)
+        wl = build_workload(args.workload, args.layers, dev, shared=args.shared_bases)
     chained = bool(wl.get("chained"))
     plans = wl["plans"]
     S = wl["steps"]
@@ -558,13 +576,13 @@ def main():
     torch.cuda.synchronize()
     dense_wall = time.perf_counter() - t0
     dense_tok_s = D / dense_wall
-    dense_bytes = sum(acc.token_bytes(mi.d, mi.d_out, mi.k, 2, True) for row in wl["data"] for mi in row)
+    dense_bytes = sum(call_bytes(mi, True) for row in wl["data"] for mi in row)
     t0 = time.perf_counter()
     for i in range(K):
         gsi.gsi_stack(plans[i % S], gsi.FORCE_FAST, ws)
     torch.cuda.synchronize()
     fast_wall = time.perf_counter() - t0
-    fast_bytes = sum(acc.token_bytes(mi.d, mi.d_out, mi.k, 2, False) for row in wl["data"] for mi in row)
+    fast_bytes = sum(call_bytes(mi, False) for row in wl["data"] for mi in row)
     # restore the gated outputs of the last steps (the forced runs overwrote them)
     for i in range(min(K, S)):
         gsi.gsi_stack(plans[i], gsi.GATED, ws)
@@ -592,7 +610,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {wl['layers']} layers x {len(wl['roles'])} maps "
+            "workload": f"{args.workload}{' (shared bases)' if args.shared_bases else ''}: "
+                        f"{wl['layers']} layers x {len(wl['roles'])} maps "
                         f"({maps_per_step} gated batch-1 calls per step"
                         + (f" in {2 * wl['layers']} dependent waves" if chained else "") + "), "
                         f"{wl['rate'] * 100:.0f}% slow tokens" + (" at the first layer" if chained else " per map")
@@ -612,7 +631,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": stack_gbps / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(args.workload, "stack_kernel"),
+            "traffic": measured_traffic(args.workload + ("-shared" if args.shared_bases else ""),
+                                        "stack_kernel"),
             "bytes_per_launch": float(step_b.mean()),
             "mean_launch_us": float(t_stack.mean() * 1e6),
         },

@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -351,14 +353,31 @@ constexpr int64_t kFineUnits = 1024;
 #endif
 constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
 
+// For each call, the earlier call of the same wave whose projection it
+// shares (same x, V_k, d and k: g, ||x|| and rho are then the same), or -1.
+static std::vector<int32_t> share_owners(const gsi_call *calls, int32_t n) {
+  std::vector<int32_t> owner(n, -1);
+  std::map<std::tuple<int32_t, const void *, const void *, int32_t, int32_t>, int32_t> first;
+  for (int32_t i = 0; i < n; ++i) {
+    const auto key = std::make_tuple(calls[i].wave, calls[i].x, calls[i].map.V, calls[i].map.d, calls[i].map.k);
+    const auto it = first.find(key);
+    if (it == first.end())
+      first.emplace(key, i);
+    else
+      owner[i] = it->second;
+  }
+  return owner;
+}
+
 static std::vector<UnitShape> call_shapes(const gsi_call *calls, int32_t n, int es) {
   std::vector<UnitShape> shapes(n);
+  const std::vector<int32_t> owner = share_owners(calls, n);
   for (int32_t b = 0; b < n;) {
     int32_t e = b + 1;
     while (e < n && calls[e].wave == calls[b].wave) ++e;
     int64_t vbytes = 0, fast_units = 0;
     for (int32_t i = b; i < e; ++i) {
-      vbytes += (int64_t)calls[i].map.d * calls[i].map.k * es;
+      if (owner[i] < 0) vbytes += (int64_t)calls[i].map.d * calls[i].map.k * es;
       fast_units += unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, 1 << 20).fast_units;
     }
     const int64_t t = plan_proj_target(vbytes);
@@ -367,6 +386,10 @@ static std::vector<UnitShape> call_shapes(const gsi_call *calls, int32_t n, int 
       const int64_t vi = (int64_t)calls[i].map.d * calls[i].map.k * es;
       const int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
       shapes[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, ti, fine);
+      if (owner[i] >= 0) {  // projected by its owner
+        shapes[i].a_units = 0;
+        shapes[i].part_floats = 0;
+      }
     }
     b = e;
   }
@@ -450,6 +473,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
   std::vector<int32_t> order(n);
   for (int32_t i = 0; i < n; ++i) order[i] = i;
   const std::vector<UnitShape> shapes = call_shapes(calls, n, es);
+  const std::vector<int32_t> owner = share_owners(calls, n);
   std::vector<int32_t> nunits(n);
   for (int32_t i = 0; i < n; ++i) nunits[i] = shapes[i].a_units;
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
@@ -489,13 +513,19 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.fast_tiles = us.fast_tiles;
     o.slow_units = us.slow_units;
     o.slow_rows = us.slow_rows;
-    o.g_off = g_off;
+    o.g_off = owner[i] < 0 ? g_off : desc[owner[i]].g_off;
     o.part_off = part_off;
     o.gate_off = i;
     o.wave = wave_of[i];
     o.flags = (o.wave > 0 ? kCallXCoherent : 0) | (o.wave + 1 < n_waves ? kCallYCoherent : 0);
     for (int32_t q = 0; q < us.a_units; ++q) unit_call[a_begin + q] = i;
-    g_off += us.g_floats;
+    if (owner[i] >= 0) {  // append to the owner's sharing list
+      int32_t last = owner[i];
+      while (desc[last].share_next) last = desc[last].share_next - 1;
+      desc[last].share_next = i + 1;
+    } else {
+      g_off += us.g_floats;
+    }
     part_off += us.part_floats;
     const int32_t ub = us.fast_units > us.slow_units ? us.fast_units : us.slow_units;
     if (ub >= kMaxUnitsPerCall) return GSI_E_SHAPE;

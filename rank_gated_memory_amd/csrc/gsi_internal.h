@@ -8,7 +8,7 @@
 namespace gsi {
 
 constexpr uint32_t kPlanMagic = 0x50495347u;  // "GSIP"
-constexpr uint32_t kPlanVersion = 2;
+constexpr uint32_t kPlanVersion = 3;
 constexpr int kBlock = 256;          // threads per workgroup of every kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kTileRows = 64;        // image rows per tile (one per lane)
@@ -41,8 +41,15 @@ struct alignas(16) CallDesc {
                        // one tile whose columns are split over the wavefronts)
   int32_t flags;       // kCallXCoherent | kCallYCoherent
   int32_t wave;        // wave of the call in a stack (0 for independent calls)
+  // Calls of one wave with the same x, V_k, d and k share one projection:
+  // the first of them (the owner) has the projection units; the others have
+  // none, read the owner's g, and have their gates decided by the owner's
+  // last projection unit.  share_next = 1 + the next call of the group
+  // (0: none), so a zero-filled descriptor shares nothing.
+  int32_t share_next;
+  int32_t pad_[3];
 };
-static_assert(sizeof(CallDesc) == 128, "CallDesc layout");
+static_assert(sizeof(CallDesc) == 144, "CallDesc layout");
 
 // CallDesc::flags.  In a stack of several waves, x of a later wave may be
 // the y of an earlier one, written inside the same launch by a workgroup on

@@ -285,13 +285,12 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
 }
 
 // Run by the workgroup that wrote a call's last partial: sums the partials
-// in a fixed order (bitwise deterministic), forms ||g||^2, rho and the gate
-// (GSI-TS §2.2), writes g (agent-coherent stores when GC), the gate record
-// and the caller's rho / slow, and clears the call's counter.  Returns the
-// slow flag (valid on thread 0).
-template <int MODE, bool GC>
-__device__ __forceinline__ int finish_gate(const CallDesc &cd, const float *wsf, float *gw,
-                                           void *gate, uint32_t *counters, float *sh) {
+// in a fixed order (bitwise deterministic), writes g (agent-coherent stores
+// when GC), forms ||x||^2, ||g||^2 and rho (GSI-TS §2.2), and clears the
+// call's counter.  Returns {rho, ||x||^2, ||g||^2} (valid on thread 0).
+template <bool GC>
+__device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const float *wsf, float *gw,
+                                                    uint32_t *counters, float *sh) {
   const int tid = threadIdx.x;
   const int k = cd.k;
   const int stride = k + 4;
@@ -332,15 +331,19 @@ __device__ __forceinline__ int finish_gate(const CallDesc &cd, const float *wsf,
   for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += load_coherent(p0 + (int64_t)qq * stride + k);
   gg = block_sum(gg, sh);
   const float xxt = block_sum(xp, sh);
-  int slow = 0;
-  if (tid == 0) {
-    const float rho = rho_from_norms(xxt, gg);
-    slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < cd.eps));
-    reinterpret_cast<float4 *>(gate)[cd.gate_off] = make_float4(rho, __int_as_float(slow), xxt, gg);
-    if (cd.rho) *cd.rho = rho;
-    if (cd.slow) *cd.slow = (uint8_t)slow;
-    counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
-  }
+  if (tid == 0) counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
+  return make_float3(rho_from_norms(xxt, gg), xxt, gg);
+}
+
+// The gate of one call from its residual ratio (GSI-TS §2.2): slow iff
+// !(rho < eps), unless the mode forces a path.  Writes the gate record and
+// the caller's rho / slow (thread 0 only) and returns the slow flag.
+template <int MODE>
+__device__ __forceinline__ int decide_gate(const CallDesc &m, float3 r, void *gate) {
+  const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(r.x < m.eps));
+  reinterpret_cast<float4 *>(gate)[m.gate_off] = make_float4(r.x, __int_as_float(slow), r.y, r.z);
+  if (m.rho) *m.rho = r.x;
+  if (m.slow) *m.slow = (uint8_t)slow;
   return slow;
 }
 
@@ -370,16 +373,29 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  const int slow = finish_gate<MODE, false>(cd, a.wsf, a.wsf + cd.g_off, a.gate, a.counters, sh);
-  if (tid == 0) store_coherent_i(a.need + c, slow ? cd.slow_units : cd.fast_units);
+  const float3 r = finish_projection<false>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh);
+  if (tid == 0) {
+    // the gates of this call and of every call sharing its projection
+    unsigned members = 0;
+    for (int m = c;;) {
+      const CallDesc md = m == c ? cd : load_call(a, m);
+      const int slow = decide_gate<MODE>(md, r, a.gate);
+      store_coherent_i(a.need + m, slow ? md.slow_units : md.fast_units);
+      ++members;
+      if (md.share_next == 0) break;
+      m = md.share_next - 1;
+    }
+    s_last = (int)members;
+  }
 
   // The last call to finish writes the launch-wide prefix of output units.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + a.n, 1u, __ATOMIC_RELAXED,
+    const unsigned members = (unsigned)s_last;
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + a.n, members, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(a.n - 1)) ? 1 : 0;
+    s_last = (prev + members == (unsigned)a.n) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
@@ -934,17 +950,23 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         s_flag = ctl_add(a.counters + c, 1u) == (uint32_t)(cd.a_units - 1) ? 1 : 0;
       __syncthreads();
       if (s_flag) {
-        const int sl = finish_gate<MODE, true>(cd, a.wsf, a.wsf + cd.g_off, a.gate, a.counters, sh);
+        const float3 r = finish_projection<true>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // g of every thread is stored before the gate opens
+        __syncthreads();  // g of every thread is stored before any gate opens
         if (tid == 0) {
-          // open the gate: append the call to its wave's open list
-          const uint64_t need = (uint64_t)(sl ? cd.slow_units : cd.fast_units);
+          // open the gates of this call and of every call sharing its
+          // projection: append each to its wave's open list
           uint32_t *wv = wave_ctl(a, cd.wave);
-          const uint64_t old = ctl_add64(reinterpret_cast<uint64_t *>(wv + kWvOpen), ((uint64_t)1 << 40) | need);
-          const uint64_t slot = old >> 40;
-          ctl_store64(a.entries + a.wave_tab[a.n_waves + 1 + cd.wave] + slot,
-                      (old & kLow40) | (need << 32) | ((uint64_t)sl << 50) | ((uint64_t)(c + 1) << 51));
+          for (int m = c;;) {
+            const CallDesc md = m == c ? cd : a.table[m];
+            const int sl = decide_gate<MODE>(md, r, a.gate);
+            const uint64_t need = (uint64_t)(sl ? md.slow_units : md.fast_units);
+            const uint64_t old = ctl_add64(reinterpret_cast<uint64_t *>(wv + kWvOpen), ((uint64_t)1 << 40) | need);
+            ctl_store64(a.entries + a.wave_tab[a.n_waves + 1 + md.wave] + (old >> 40),
+                        (old & kLow40) | (need << 32) | ((uint64_t)sl << 50) | ((uint64_t)(m + 1) << 51));
+            if (md.share_next == 0) break;
+            m = md.share_next - 1;
+          }
         }
       }
     } else {

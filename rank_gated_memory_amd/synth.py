@@ -323,13 +323,24 @@ def config5(k: int, slow_frac: float, T: int = 256, d: int = 4096, d_out: int = 
                       int(round(slow_frac * T)), torch.bfloat16, device, w_device)
 
 
+# Map roles that read the same input as an earlier role of the same layer
+# (follower index -> owner index): GPT-J's parallel block feeds qkv and
+# fc_in from one layer norm; LLaMA's gate and up read one MLP input.
+SHARED_INPUTS = {"gptj6b-28L": {2: 0}, "llama13b-40L": {3: 2}}
+
+
 def stack_config(cfg: int, layers: int, maps, steps: int, slow_rate: float,
-                 device="cpu", cascade: bool = True, extra_cols: int = 64, keep_fp64: bool = False):
+                 device="cpu", cascade: bool = True, extra_cols: int = 64, keep_fp64: bool = False,
+                 share=None):
     """Layer stack: per map role a (cascaded or independent) basis per layer.
 
     Returns a list over layers of lists over roles of MapInputs whose X holds
-    one token per decode step ([steps][d]).
+    one token per decode step ([steps][d]).  share (follower role index ->
+    owner role index): the follower reads the owner's tokens with the
+    owner's basis (the same tensors) through its own weight, and carries
+    shared=True.
     """
+    share = share or {}
     n_slow = int(round(slow_rate * steps))
     frames = {}
     for ridx, (name, d, d_out, k) in enumerate(maps):
@@ -339,6 +350,15 @@ def stack_config(cfg: int, layers: int, maps, steps: int, slow_rate: float,
     for layer in range(layers):
         row = []
         for ridx, (name, d, d_out, k) in enumerate(maps):
+            if ridx in share:
+                o = row[share[ridx]]
+                if (o.d, o.k) != (d, k):
+                    raise ValueError(f"{name} cannot share the input of {o.name}")
+                W = gaussian_weight(d_out, d, (cfg, layer, ridx, P_WEIGHT), device, torch.bfloat16)
+                mi = MapInputs(name, d, d_out, k, W, o.V, o.X, o.slow_mask, o.rho_built, extra=o.extra)
+                mi.shared = True
+                row.append(mi)
+                continue
             fr = frames[ridx][layer] if cascade else None
             row.append(single_map(cfg, layer, ridx, name, d, d_out, k, steps, n_slow,
                                   torch.bfloat16, device, device, extra_cols, frame=fr,

@@ -127,7 +127,8 @@ PLAN_HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("n", "<i4"), ("dtype
 DESC = np.dtype([("ptrs", "<u8", 7), ("d", "<i4"), ("d_out", "<i4"), ("k", "<i4"), ("eps", "<f4"),
                  ("a_begin", "<i4"), ("a_units", "<i4"), ("a_rows", "<i4"), ("fast_units", "<i4"),
                  ("slow_units", "<i4"), ("slow_rows", "<i4"), ("part_off", "<i8"), ("g_off", "<i8"),
-                 ("gate_off", "<i4"), ("fast_tiles", "<i4"), ("flags", "<i4"), ("wave", "<i4")])
+                 ("gate_off", "<i4"), ("fast_tiles", "<i4"), ("flags", "<i4"), ("wave", "<i4"),
+                 ("share_next", "<i4"), ("pad", "<i4", 3)])
 
 
 def header(plan):
@@ -151,8 +152,8 @@ def test_stack_plan_layout():
     st, plan, nb = build_plan(specs)
     assert st == GSI_OK
     h = header(plan)
-    assert PLAN_HDR.itemsize == 128 and DESC.itemsize == 128
-    assert h["magic"] == 0x50495347 and h["version"] == 2 and h["n"] == 12 and h["dtype"] == 1
+    assert PLAN_HDR.itemsize == 128 and DESC.itemsize == 144
+    assert h["magic"] == 0x50495347 and h["version"] == 3 and h["n"] == 12 and h["dtype"] == 1
     assert h["n_waves"] == 1
     assert h["total_bytes"] == nb and h["max_k"] == 512 and h["max_d"] == 16384
     uo, ua = int(h["unit_off"]), int(h["units_a"])
@@ -201,7 +202,7 @@ def test_stack_rejects_before_launch():
 def plan_tables(plan):
     h = header(plan)
     n, W = int(h["n"]), int(h["n_waves"])
-    desc = np.frombuffer(plan[int(h["desc_off"]):int(h["desc_off"]) + n * 128].tobytes(), DESC)
+    desc = np.frombuffer(plan[int(h["desc_off"]):int(h["desc_off"]) + n * DESC.itemsize].tobytes(), DESC)
     uo, ua = int(h["unit_off"]), int(h["units_a"])
     unit_call = np.frombuffer(plan[uo:uo + 4 * ua].tobytes(), "<i4")
     oo = int(h["order_off"])
@@ -271,3 +272,32 @@ def test_stack_phase_rejects_multi_wave_plans():
     assert st == GSI_OK
     need = L.gsi_stack_workspace(plan.ctypes.data)
     assert L.gsi_stack_phase(plan.ctypes.data, FAKE, 0, 1, FAKE, need, None) == E_ARG
+
+
+def test_stack_plan_shares_projections():
+    """Calls of one wave with the same x, V_k, d and k share one projection:
+    the first owns the units, the others link to it and read its g."""
+    X, Y = FAKE + 0x3000000, FAKE + 0x4000000
+    L = gsi.lib()
+    arr = (gsi.GsiCallStruct * 6)()
+    V = FAKE + 0x100000
+    specs = [  # (d, d_out, k, V, x, wave)
+        (4096, 12288, 256, V, X, 0), (4096, 16384, 256, V, X, 0), (4096, 4096, 256, V + 0x10000000, X, 0),
+        (4096, 4096, 256, V, X + 0x100000, 0), (4096, 12288, 256, V, X, 0), (4096, 4096, 256, V, X, 1)]
+    for i, (d, do, k, v, x, w) in enumerate(specs):
+        mp = gsi.GsiMapStruct(d, do, k, 1, FAKE + 0x20000000 * (i + 1), v, FAKE + 0x20000000 * (i + 1) + 0x10000000)
+        arr[i] = gsi.GsiCallStruct(mp, x, Y + 0x100000 * i, 0.05, w, 0, 0)
+    nb = L.gsi_stack_plan_bytes(arr, 6)
+    buf = np.zeros(nb + 64, dtype=np.uint8)
+    off = (-buf.ctypes.data) % 16
+    plan = buf[off:off + nb]
+    assert L.gsi_stack_plan(arr, 6, plan.ctypes.data, nb) == GSI_OK
+    h, desc, unit_call, *_ = plan_tables(plan)
+    # calls 0, 1 and 4 share (same x, V, d, k, wave); 2 (other V), 3 (other x), 5 (other wave) do not
+    assert list(desc["share_next"]) == [2, 5, 0, 0, 0, 0]
+    assert desc["a_units"][1] == 0 and desc["a_units"][4] == 0
+    assert all(desc["a_units"][i] > 0 for i in (0, 2, 3, 5))
+    assert desc["g_off"][1] == desc["g_off"][0] == desc["g_off"][4]
+    assert len(set(desc["g_off"][[0, 2, 3, 5]].tolist())) == 4
+    assert set(unit_call.tolist()) == {0, 2, 3, 5}
+    assert h["units_a"] == sum(desc["a_units"])

@@ -443,3 +443,51 @@ def test_stack_single_launch_matches_two_phases(dtype):
             for (y, r, s), (y0, r0, s0) in zip(outs, ref):
                 assert torch.equal(y, y0) and torch.equal(r, r0) and torch.equal(s, s0)
     assert st.status(ws) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_shared_projection_stack(dtype):
+    """Calls reading one x with one basis share a projection (one set of
+    projection units), yet each keeps its own threshold, gate and output:
+    with rho ~ 0.029, eps = 0.05 takes the fast path and eps = 0.02 the slow
+    one from the same rho.  Oracle parity, and the same bits as the
+    two-launch form."""
+    d, k = 512, 32
+    v, u = synth.orthonormal_frame(d, k, 64, (93, 0, 0, 1))
+    V = v.to(dtype).to(DEV).contiguous()
+    mask = torch.tensor([False, True, False, False])
+    X, _ = synth.tokens(v, u, mask, (93, 0, 0), rho_fast=0.03)
+    Xd = X.to(dtype).to(DEV)
+    outs_dims = (328, 200, 1000)
+    epss = (0.05, 0.02, 0.05)
+    maps = []
+    for i, do in enumerate(outs_dims):
+        W = synth.gaussian_weight(do, d, (93, 0, i, 2), dtype=dtype)
+        m = gsi.Map(W.to(DEV), V)
+        gsi.gsi_prepare(m)
+        maps.append((m, W))
+    calls, outs = [], []
+    for t in range(4):
+        for (m, W), eps in zip(maps, epss):
+            y = torch.empty(m.d_out, dtype=dtype, device=DEV)
+            r = torch.empty(1, dtype=torch.float32, device=DEV)
+            s = torch.empty(1, dtype=torch.uint8, device=DEV)
+            calls.append((m, Xd[t], y, eps, r, s))
+            outs.append((t, W, eps, y, r, s))
+    st = gsi.Stack(calls)
+    ws = st.run()
+    sync()
+    Vf = f64(V)
+    slow_seen = set()
+    for t, W, eps, y, r, s in outs:
+        compare_tokens(f64(W), Vf, f64(Xd[t:t + 1]), eps, f64(y)[None], np.array([int(s.item())]),
+                       np.array([float(r.item())]), dtype, rho_tol=2e-2, what=f"shared t{t} eps{eps}")
+        slow_seen.add((t, eps, int(s.item())))
+    # one rho, two thresholds, two paths
+    assert (0, 0.05, 0) in slow_seen and (0, 0.02, 1) in slow_seen
+    assert st.status(ws) == 0
+    ref = [o[3].clone() for o in outs]
+    gsi.gsi_stack_phase(st, gsi.GATED, gsi.PHASE_PROJECT, ws)
+    gsi.gsi_stack_phase(st, gsi.GATED, gsi.PHASE_APPLY, ws)
+    sync()
+    assert all(torch.equal(o[3], a) for o, a in zip(outs, ref))
