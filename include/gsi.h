@@ -22,11 +22,12 @@
  *     Accumulation is fp32 everywhere; g, norms and rho are fp32.
  *   - Shapes: d, d_out, k positive multiples of 8, k <= min(d, 1024),
  *     d * sizeof(element) <= 32 KiB (x is staged in LDS).
- *   - Alignment: W, V_k, M, x, y 16-byte aligned; rho 4-byte aligned.
+ *   - Alignment: W, V_k, M, G, x, y 16-byte aligned; rho 4-byte aligned.
  *   - Gate (GSI-TS §2.2): slow = !(rho < eps).  Ties go slow; ||x|| = 0
  *     gives rho = 0; a NaN/Inf token gives rho = NaN and goes slow.
  *     On the GPU rho is evaluated as sqrt(max(0, 1 - ||g||^2/||x||^2)),
- *     which equals ||x - V_k g|| / ||x|| for an orthonormal V_k.
+ *     which equals ||x - V_k g|| / ||x|| for an orthonormal V_k, or exactly
+ *     for the stored basis when the map carries E (gsi_map.G).
  */
 #ifndef GSI_H
 #define GSI_H
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GSI_ABI_VERSION 2
+#define GSI_ABI_VERSION 3
 
 typedef enum {
   GSI_OK = 0,
@@ -77,6 +78,14 @@ typedef struct gsi_map {
   const void *W;
   const void *V;
   void *M;
+  /* Optional (NULL for none): E = V_k^T V_k - I, [k][k] row-major in the
+   * storage dtype, gsi_gram_bytes() bytes, written by gsi_prepare.  With it
+   * every gate of the map uses the residual ratio exactly for the stored
+   * basis, rho = sqrt(max(0, ||x||^2 - ||g||^2 + g^T E g)) / ||x||, which is
+   * ||x - V_k g|| / ||x|| (GSI-TS §2.2) even where rounding has left V_k only
+   * nearly orthonormal; without it rho = sqrt(1 - ||g||^2/||x||^2), exact
+   * only for an orthonormal V_k.  Costs one read of E per gate. */
+  void *G;
 } gsi_map;
 
 /* One batch-1 call of a stack: one token x [d] -> y [d_out] through `map`.
@@ -103,10 +112,14 @@ const char *gsi_status_str(int32_t status);
  * or 0 for invalid arguments. */
 size_t gsi_image_bytes(int32_t d_out, int32_t k, int32_t dtype);
 
-/* Build the cached image M = W V_k (GSI-TS §2.1) into map->M.
- * fp32 accumulation, rounded to nearest-even into the storage dtype; the
- * padding rows of the last tile are written as zeros.  Runs once per map,
- * off the per-token path. */
+/* Bytes of E = V_k^T V_k - I of a map with k basis columns (see gsi_map.G),
+ * or 0 for invalid arguments. */
+size_t gsi_gram_bytes(int32_t k, int32_t dtype);
+
+/* Build the cached image M = W V_k (GSI-TS §2.1) into map->M, and, if
+ * map->G is set, E = V_k^T V_k - I into map->G.  fp32 accumulation, rounded
+ * to nearest-even into the storage dtype; the padding rows of the last tile
+ * of M are written as zeros.  Runs once per map, off the per-token path. */
 gsi_status gsi_prepare(const gsi_map *map, void *stream);
 
 /* Workspace bytes gsi_linear needs for T tokens of `map` (0 if T == 0). */

@@ -221,6 +221,13 @@ def spectral_norm(W) -> float:
     return float(np.linalg.norm(_f64(W), 2))
 
 
+def gram_deviation(V) -> np.ndarray:
+    """E = V_k^T V_k - I: how far the stored basis is from orthonormal (zero
+    for the orthonormal V_k of GSI-TS §2.1)."""
+    V = _f64(V)
+    return V.T @ V - np.eye(V.shape[1])
+
+
 def theorem4_bound(W, x, rho: float) -> float:
     """Fast-path error bound ||W||_2 * rho * ||x|| (GSI-TS §2.2, Theorem 4).
 

@@ -22,6 +22,7 @@ hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int 
                           int k, hipStream_t s);
 hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s);
 hipError_t launch_stack(int dtype, const FArgs &a, int mode, int max_groups, hipStream_t s);
+hipError_t launch_gram(int dtype, const void *V, void *E, int d, int k, hipStream_t s);
 hipError_t launch_batched(const BArgs &a, hipStream_t s);
 }  // namespace gsi
 
@@ -48,7 +49,8 @@ gsi_status check_map(const gsi_map *m) {
   const gsi_status s = check_shape(m->d, m->d_out, m->k, m->dtype);
   if (s != GSI_OK) return s;
   if (!m->W || !m->V || !m->M) return GSI_E_NULL;
-  if (!aligned(m->W, 16) || !aligned(m->V, 16) || !aligned(m->M, 16)) return GSI_E_ALIGN;
+  if (!aligned(m->W, 16) || !aligned(m->V, 16) || !aligned(m->M, 16) || !aligned(m->G, 16))
+    return GSI_E_ALIGN;
   return GSI_OK;
 }
 
@@ -144,11 +146,18 @@ size_t gsi_image_bytes(int32_t d_out, int32_t k, int32_t dtype) {
   return (size_t)(tiles * kTileRows * (int64_t)k * es);
 }
 
+size_t gsi_gram_bytes(int32_t k, int32_t dtype) {
+  const int es = esize_of(dtype);
+  if (es == 0 || k <= 0) return 0;
+  return (size_t)k * k * es;
+}
+
 gsi_status gsi_prepare(const gsi_map *map, void *stream) {
   const gsi_status s = check_map(map);
   if (s != GSI_OK) return s;
-  const hipError_t e = launch_prepare(map->dtype, map->W, map->V, map->M, map->d, map->d_out,
-                                      map->k, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prepare(map->dtype, map->W, map->V, map->M, map->d, map->d_out, map->k, st);
+  if (e == hipSuccess && map->G) e = launch_gram(map->dtype, map->V, map->G, map->d, map->k, st);
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }
 
@@ -194,6 +203,7 @@ static gsi_status linear_batched(const gsi_map *map, const void *x, void *y, int
     a.W = map->W;
     a.V = map->V;
     a.M = map->M;
+    a.G = map->G;
     a.x = static_cast<const char *>(x) + (int64_t)t0 * map->d * 2;
     a.y = static_cast<char *>(y) + (int64_t)t0 * map->d_out * 2;
     a.rho = rho ? rho + t0 : nullptr;
@@ -252,6 +262,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     o.W = map->W;
     o.V = map->V;
     o.M = map->M;
+    o.G = map->G;
     o.x = static_cast<const char *>(x) + (int64_t)t0 * map->d * es;
     o.y = static_cast<char *>(y) + (int64_t)t0 * map->d_out * es;
     o.rho = rho ? rho + t0 : nullptr;
@@ -354,12 +365,13 @@ constexpr int64_t kFineUnits = 1024;
 constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
 
 // For each call, the earlier call of the same wave whose projection it
-// shares (same x, V_k, d and k: g, ||x|| and rho are then the same), or -1.
+// shares (same x, V_k, E, d and k: g, ||x|| and rho are then the same), or -1.
 static std::vector<int32_t> share_owners(const gsi_call *calls, int32_t n) {
   std::vector<int32_t> owner(n, -1);
-  std::map<std::tuple<int32_t, const void *, const void *, int32_t, int32_t>, int32_t> first;
+  std::map<std::tuple<int32_t, const void *, const void *, const void *, int32_t, int32_t>, int32_t> first;
   for (int32_t i = 0; i < n; ++i) {
-    const auto key = std::make_tuple(calls[i].wave, calls[i].x, calls[i].map.V, calls[i].map.d, calls[i].map.k);
+    const auto key = std::make_tuple(calls[i].wave, calls[i].x, calls[i].map.V, (const void *)calls[i].map.G,
+                                     calls[i].map.d, calls[i].map.k);
     const auto it = first.find(key);
     if (it == first.end())
       first.emplace(key, i);
@@ -498,6 +510,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.W = c.map.W;
     o.V = c.map.V;
     o.M = c.map.M;
+    o.G = c.map.G;
     o.x = c.x;
     o.y = c.y;
     o.rho = c.rho;

@@ -22,6 +22,7 @@ struct BArgs {
   int32_t mode;
   float eps;
   int32_t pad_;
+  const void *G;   // E = V_k^T V_k - I [k][k] bf16 (exact rho), or null
   float *part;     // [splits][n][k] partial g
   float *xxp;      // [splits][n] partial ||x||^2
   uint16_t *ghi;   // [n][kpad] bf16(g)

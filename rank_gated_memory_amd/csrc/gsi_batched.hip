@@ -29,6 +29,7 @@
 #include <cfloat>
 
 #include "gsi_batched.h"
+#include "gsi_gram.h"
 
 namespace gsi {
 
@@ -224,6 +225,7 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
 template <int MODE>
 __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   __shared__ float sh[kWaves];
+  __shared__ float gl[1024];  // g of the token, for the exact rho
   __shared__ int2 scan[kBlock];
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -245,6 +247,7 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
       for (; s < a.splits; ++s) g += p[(size_t)s * stride];
     }
     gg = fmaf(g, g, gg);
+    if (a.G && j < a.k) gl[j] = g;
     const uint16_t hi = f2bf(g);
     const uint16_t lo = f2bf(g - bf2f(hi));
     a.ghi[(size_t)t * a.kpad + j] = hi;
@@ -266,8 +269,10 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   float xx = 0.f;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) xx += sh[i];
+  float q = 0.f;
+  if (a.G) q = gram_quadratic<2, kBlock>(a.G, a.k, gl, sh);
   if (tid == 0) {
-    const float rho = rho_of(xx, ggt);
+    const float rho = a.G ? rho_exact(xx, ggt, q) : rho_of(xx, ggt);
     const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < a.eps));
     store_flag(a.flags + t, slow);
     if (a.rho) a.rho[t] = rho;

@@ -47,7 +47,8 @@ struct alignas(16) CallDesc {
   // last projection unit.  share_next = 1 + the next call of the group
   // (0: none), so a zero-filled descriptor shares nothing.
   int32_t share_next;
-  int32_t pad_[3];
+  int32_t pad_;
+  const void *G;       // E = V_k^T V_k - I [k][k] (exact rho), or null (norm form)
 };
 static_assert(sizeof(CallDesc) == 144, "CallDesc layout");
 

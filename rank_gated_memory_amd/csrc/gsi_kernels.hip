@@ -40,6 +40,7 @@
 
 #include <cfloat>
 
+#include "gsi_gram.h"
 #include "gsi_internal.h"
 
 namespace gsi {
@@ -287,10 +288,12 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
 // Run by the workgroup that wrote a call's last partial: sums the partials
 // in a fixed order (bitwise deterministic), writes g (agent-coherent stores
 // when GC), forms ||x||^2, ||g||^2 and rho (GSI-TS §2.2), and clears the
-// call's counter.  Returns {rho, ||x||^2, ||g||^2} (valid on thread 0).
-template <bool GC>
+// call's counter.  With a cached E = V_k^T V_k - I, rho is exact for the
+// stored basis (g also goes to the LDS scratch gl, k floats).  Returns
+// {rho, ||x||^2, ||g||^2} (valid on thread 0).
+template <typename T, bool GC>
 __device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const float *wsf, float *gw,
-                                                    uint32_t *counters, float *sh) {
+                                                    uint32_t *counters, float *sh, float *gl) {
   const int tid = threadIdx.x;
   const int k = cd.k;
   const int stride = k + 4;
@@ -325,6 +328,7 @@ __device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const fl
       store_coherent(gw + j, s);
     else
       gw[j] = s;
+    if (cd.G) gl[j] = s;
     gg = fmaf(s, s, gg);
   }
   float xp = 0.f;
@@ -332,6 +336,10 @@ __device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const fl
   gg = block_sum(gg, sh);
   const float xxt = block_sum(xp, sh);
   if (tid == 0) counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
+  if (cd.G) {
+    const float q = gram_quadratic<sizeof(T), kBlock>(cd.G, k, gl, sh);
+    return make_float3(rho_exact(xxt, gg, q), xxt, gg);
+  }
   return make_float3(rho_from_norms(xxt, gg), xxt, gg);
 }
 
@@ -373,7 +381,7 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  const float3 r = finish_projection<false>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh);
+  const float3 r = finish_projection<T, false>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh, red);
   if (tid == 0) {
     // the gates of this call and of every call sharing its projection
     unsigned members = 0;
@@ -950,7 +958,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         s_flag = ctl_add(a.counters + c, 1u) == (uint32_t)(cd.a_units - 1) ? 1 : 0;
       __syncthreads();
       if (s_flag) {
-        const float3 r = finish_projection<true>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh);
+        const float3 r = finish_projection<T, true>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh, red);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // g of every thread is stored before any gate opens
         if (tid == 0) {
@@ -1071,6 +1079,61 @@ __global__ void __launch_bounds__(kBlock)
       Vec<T>::store1(M, idx, acc[j]);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// E = V_k^T V_k - I (k x k, row-major, storage dtype) for the exact residual
+// ratio: one 64 x 64 block of E per workgroup, fp64 FMA over the d rows of
+// V_k in chunks of 32 staged through LDS (the diagonal sums d squares to
+// nearly 1 before 1 is subtracted, which fp32 would leave ~4e-6 off).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(kBlock) gram_kernel(const T *__restrict__ V, T *__restrict__ E, int d, int k) {
+  constexpr int KC = 32;
+  __shared__ float Vi[KC][64];
+  __shared__ float Vj[KC][65];
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int ri = tid >> 2;          // row of the block (0..63)
+  const int cj = (tid & 3) * 16;    // first of 16 columns
+  double acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = 0.0;
+  for (int r0 = 0; r0 < d; r0 += KC) {
+    for (int e = tid; e < KC * 64; e += kBlock) {
+      const int r = e / 64, c = e % 64;
+      const bool ok = r0 + r < d;
+      Vi[r][c] = (ok && i0 + c < k) ? Vec<T>::load1(V, (size_t)(r0 + r) * k + i0 + c) : 0.f;
+      Vj[r][c] = (ok && j0 + c < k) ? Vec<T>::load1(V, (size_t)(r0 + r) * k + j0 + c) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < KC; ++r) {
+      const double a = Vi[r][ri];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = fma(a, (double)Vj[r][cj + c], acc[c]);
+    }
+    __syncthreads();
+  }
+  const int i = i0 + ri;
+  if (i < k) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int j = j0 + cj + c;
+      if (j < k) Vec<T>::store1(E, (size_t)i * k + j, (float)(acc[c] - (i == j ? 1.0 : 0.0)));
+    }
+  }
+}
+
+hipError_t launch_gram(int dtype, const void *V, void *E, int d, int k, hipStream_t s) {
+  const dim3 grid((k + 63) / 64, (k + 63) / 64);
+  if (dtype == 0)
+    hipLaunchKernelGGL(gram_kernel<float>, grid, dim3(kBlock), 0, s, static_cast<const float *>(V),
+                       static_cast<float *>(E), d, k);
+  else
+    hipLaunchKernelGGL(gram_kernel<bf16_t>, grid, dim3(kBlock), 0, s, static_cast<const bf16_t *>(V),
+                       static_cast<bf16_t *>(E), d, k);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

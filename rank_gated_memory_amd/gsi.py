@@ -30,7 +30,7 @@ class GsiError(RuntimeError):
 
 class GsiMapStruct(ctypes.Structure):
     _fields_ = [("d", c_int32), ("d_out", c_int32), ("k", c_int32), ("dtype", c_int32),
-                ("W", c_void_p), ("V", c_void_p), ("M", c_void_p)]
+                ("W", c_void_p), ("V", c_void_p), ("M", c_void_p), ("G", c_void_p)]
 
 
 class GsiCallStruct(ctypes.Structure):
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.gsi_status_str.argtypes = [c_int32]
         L.gsi_image_bytes.restype = c_size_t
         L.gsi_image_bytes.argtypes = [c_int32, c_int32, c_int32]
+        L.gsi_gram_bytes.restype = c_size_t
+        L.gsi_gram_bytes.argtypes = [c_int32, c_int32]
         L.gsi_prepare.restype = c_int32
         L.gsi_prepare.argtypes = [POINTER(GsiMapStruct), c_void_p]
         L.gsi_linear_workspace.restype = c_size_t
@@ -111,9 +113,12 @@ def gsi_image_bytes(d_out: int, k: int, dtype: int) -> int:
 
 
 class Map:
-    """A linear map W [d_out][d] with basis V [d][k] and its cached image M."""
+    """A linear map W [d_out][d] with basis V [d][k], its cached image M and,
+    with exact_rho, the cached E = V^T V - I that makes its gates use the
+    exact residual ratio of the stored basis."""
 
-    def __init__(self, W: torch.Tensor, V: torch.Tensor, M: torch.Tensor | None = None):
+    def __init__(self, W: torch.Tensor, V: torch.Tensor, M: torch.Tensor | None = None,
+                 exact_rho: bool = False):
         if W.dim() != 2 or V.dim() != 2 or W.shape[1] != V.shape[0]:
             raise ValueError(f"shapes W {tuple(W.shape)} and V {tuple(V.shape)} do not chain")
         if W.dtype != V.dtype:
@@ -128,8 +133,16 @@ class Map:
         if M is None:
             M = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=W.device)
         self.M = M
+        self.G = None
+        if exact_rho:
+            self.G = torch.empty(max(int(lib().gsi_gram_bytes(self.k, self.dtype)), 16), dtype=torch.uint8,
+                                 device=W.device)
         self.struct = GsiMapStruct(self.d, self.d_out, self.k, self.dtype,
-                                   _ptr(W), _ptr(V), _ptr(M))
+                                   _ptr(W), _ptr(V), _ptr(M), _ptr(self.G))
+
+    def gram(self) -> torch.Tensor:
+        """E = V^T V - I as built by gsi_prepare ([k][k], storage dtype)."""
+        return self.G[: self.k * self.k * self.W.element_size()].view(self.W.dtype).view(self.k, self.k)
 
     def image_rows(self) -> torch.Tensor:
         """The image M as a [d_out][k] tensor (un-tiles the library layout)."""

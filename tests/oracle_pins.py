@@ -400,9 +400,29 @@ def pin_chain(orc):
         raise AssertionError(f"chain accepted {bad}")
 
 
+def pin_gram_identity(orc):
+    """For any basis V (orthonormal or not) and g = V^T x, the explicit
+    residual satisfies ||x - V g||^2 = ||x||^2 - ||g||^2 + g^T E g with
+    E = V^T V - I; E vanishes for an orthonormal basis and is diag(s^2 - 1)
+    for columns scaled by s."""
+    rng = _rng(28)
+    d, k = 40, 6
+    Q = _orthonormal(rng, d, k)
+    assert np.max(np.abs(orc.gram_deviation(Q))) < 1e-13
+    s = np.array([1.0, 0.5, 2.0, 1.01, 0.99, 3.0])
+    _close(orc.gram_deviation(Q * s), np.diag(s * s - 1.0), 1e-12, 1e-12, "scaled columns")
+    for V in (Q * s, Q + 0.05 * rng.standard_normal((d, k)), rng.standard_normal((d, k))):
+        E = orc.gram_deviation(V)
+        for _ in range(3):
+            x = rng.standard_normal(d)
+            g = orc.project(V, x)
+            r = orc.residual(V, x, g)
+            _close(np.dot(r, r), np.dot(x, x) - np.dot(g, g) + g @ E @ g, 1e-10, 1e-10, "gram identity")
+
+
 ALL_PINS = [
     pin_identity_basis, pin_full_rank, pin_in_span_and_orthogonal, pin_construction,
     pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
     pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity, pin_nested_bases,
-    pin_storage_rounding, pin_chain,
+    pin_storage_rounding, pin_chain, pin_gram_identity,
 ]

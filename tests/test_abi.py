@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gsi.gsi_abi_version() == 2
+    assert gsi.gsi_abi_version() == 3
     m = re.search(r"#define GSI_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == gsi.gsi_abi_version()
     assert gsi.status_str(0) == "GSI_OK"
@@ -301,3 +301,13 @@ def test_stack_plan_shares_projections():
     assert len(set(desc["g_off"][[0, 2, 3, 5]].tolist())) == 4
     assert set(unit_call.tolist()) == {0, 2, 3, 5}
     assert h["units_a"] == sum(desc["a_units"])
+
+
+def test_gram_bytes_and_alignment():
+    L = gsi.lib()
+    assert L.gsi_gram_bytes(256, 1) == 256 * 256 * 2
+    assert L.gsi_gram_bytes(16, 0) == 16 * 16 * 4
+    assert L.gsi_gram_bytes(0, 1) == 0 and L.gsi_gram_bytes(8, 5) == 0
+    m = mk_map()
+    m.G = FAKE + 0x600008  # misaligned E
+    assert prep(m) == E_ALIGN

@@ -56,6 +56,9 @@ MUTANTS = {
     "chain_unrounded_input": ("chain", None),
     "chain_ignores_offset": ("chain", None),
     "chain_reads_previous_call": ("chain", None),
+    # Gram deviation: no identity subtracted, transposed product
+    "gram_no_identity": ("gram_deviation", lambda V: f64(V).T @ f64(V)),
+    "gram_outer": ("gram_deviation", lambda V: f64(V) @ f64(V).T - np.eye(f64(V).shape[0])),
 }
 
 
