@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--workload", default="gptj6b-28L",
                    choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--exact-rho", action="store_true",
+                   help="every map caches E = V^T V - I and gates on the exact residual ratio")
     p.add_argument("--shared-bases", action="store_true",
                    help="maps that read one input (GPT-J qkv and fc_in, LLaMA gate and up) share "
                         "its tokens and basis, hence one projection")
@@ -52,7 +54,7 @@ def parse():
     return p.parse_args()
 
 
-def build_workload(name, layers_override, dev, shared=False):
+def build_workload(name, layers_override, dev, shared=False, exact=False):
     import torch
 
     from rank_gated_memory_amd import gsi, synth
@@ -66,7 +68,7 @@ def build_workload(name, layers_override, dev, shared=False):
     torch.cuda.synchronize()
     log(f"inputs drawn in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
-    maps = [[gsi.Map(mi.W, mi.V) for mi in row] for row in data]
+    maps = [[gsi.Map(mi.W, mi.V, exact_rho=exact) for mi in row] for row in data]
     for row in maps:
         for m in row:
             gsi.gsi_prepare(m)
@@ -91,7 +93,7 @@ def build_workload(name, layers_override, dev, shared=False):
     torch.cuda.synchronize()
     log(f"{steps} stack plans of {len(plans[0]._keep)} calls built in {time.perf_counter() - t0:.2f}s")
     return dict(cfg=cfg, layers=layers, roles=roles, steps=steps, rate=rate, data=data, maps=maps,
-                outs=outs, plans=plans)
+                outs=outs, plans=plans, exact=exact)
 
 
 class _Shape:
@@ -180,6 +182,8 @@ def step_bytes(wl, step_slow):
             slow = bool(step_slow[i])
             if not getattr(mi, "shared", False):
                 proj += acc.project_bytes(mi.d, mi.k, 2)
+                if wl.get("exact"):
+                    proj += acc.gram_bytes(mi.k, 2)
             apply += acc.apply_bytes(mi.d, mi.d_out, mi.k, 2, slow)
             i += 1
     return proj, apply
@@ -485,7 +489,7 @@ def main():
     if args.workload == "gptj6b-28L-chained":
         wl = build_chained_workload(args.layers, dev)
     else:
-        wl = build_workload(args.workload, args.layers, dev, shared=args.shared_bases)
+        wl = build_workload(args.workload, args.layers, dev, shared=args.shared_bases, exact=args.exact_rho)
     chained = bool(wl.get("chained"))
     plans = wl["plans"]
     S = wl["steps"]
@@ -610,7 +614,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}{' (shared bases)' if args.shared_bases else ''}: "
+            "workload": f"{args.workload}{' (shared bases)' if args.shared_bases else ''}"
+                        f"{' (exact rho)' if args.exact_rho else ''}: "
                         f"{wl['layers']} layers x {len(wl['roles'])} maps "
                         f"({maps_per_step} gated batch-1 calls per step"
                         + (f" in {2 * wl['layers']} dependent waves" if chained else "") + "), "

@@ -203,6 +203,42 @@ typedef enum { GSI_PHASE_PROJECT = 1, GSI_PHASE_APPLY = 2 } gsi_phase;
 gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t mode,
                            int32_t phase, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- basis calibration (GSI-TS §2.3) ----
+ * The summary computes each layer's basis once from activations of a
+ * calibration pass, as the top-k subspace of those activations, and starts
+ * layer l+1 from layer l's basis so that only small corrections are needed
+ * (the depth cascade).  gsi_calibrate runs `iters` sweeps of block subspace
+ * iteration V <- orth(A^T (A V)) from V0: with a random V0 (a cold start)
+ * the sweeps converge to the dominant k-dimensional subspace of the samples
+ * at the rate of the spectral gap; with the previous layer's basis as V0
+ * (the cascade) a few sweeps suffice.  orth() is the Q factor of the block
+ * (Q^T Y upper triangular with a positive diagonal, the basis Gram-Schmidt
+ * gives), formed by two CholeskyQR passes in fp64; the products with A
+ * accumulate in fp32. */
+typedef struct gsi_calib {
+  int32_t n;        /* activation samples (tokens); k <= n                     */
+  int32_t d;        /* their dimension                                         */
+  int32_t k;        /* basis columns, k <= min(d, 1024)                        */
+  int32_t dtype;    /* gsi_dtype of A, V0 and V                                */
+  const void *A;    /* [n][d] row-major samples (device)                       */
+  const void *V0;   /* [d][k] starting basis (device); need not be orthonormal */
+  void *V;          /* [d][k] output: orthonormal basis (device); may equal V0 */
+  int32_t iters;    /* sweeps, 0..1000 (0 copies V0)                           */
+  int32_t reserved;
+} gsi_calib;
+
+/* Workspace bytes of gsi_calibrate (0 for invalid arguments). */
+size_t gsi_calibrate_workspace(const gsi_calib *c);
+
+/* Byte offset in the calibration workspace of its 32-bit status word: 0
+ * after a good run, nonzero if a block was numerically rank deficient (V is
+ * then not reliable).  The word is not cleared by the library. */
+size_t gsi_calibrate_status_offset(void);
+
+/* Run the sweeps (asynchronous on `stream`).  The workspace needs no
+ * initial contents except a zero status word. */
+gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -206,6 +206,65 @@ def stack(calls, mode: int = GATED) -> list:
     return [linear(c["W"], c["V"], c["M"], c["X"], c["eps"], mode) for c in calls]
 
 
+# ---- basis calibration (GSI-TS §2.3) ----------------------------------------
+#
+# The summary computes V_k once per layer from activations of a calibration
+# pass, as the top-k subspace of those activations (the directions a full
+# SVD would give), and starts layer l+1 from layer l's basis so that only
+# small corrections, orthogonalised by DGKS, are needed.  Reading used here:
+# V_k is the dominant k-dimensional left singular subspace of the sample
+# matrix A^T (A = [n tokens][d]); it is reached by block subspace iteration
+# V <- orth(A^T (A V)) from a starting basis V0 (random for a cold start, the
+# previous layer's basis for the cascade), each sweep orthonormalising the
+# new block column by column with DGKS (classical Gram-Schmidt, repeated
+# while a column loses more than half its norm to the projection).
+
+
+def dgks_orth(Y, eta: float = 1.0 / np.sqrt(2.0)) -> np.ndarray:
+    """Orthonormal Q with span(Q) = span(Y) and Q^T Y upper triangular with a
+    positive diagonal (the Q of Y = QR), by classical Gram-Schmidt with DGKS
+    reorthogonalisation: a column's projection on the earlier columns is
+    removed again while the removal shrinks its norm below eta times what it
+    was."""
+    Y = _f64(Y)
+    d, k = Y.shape
+    Q = np.zeros((d, k))
+    for j in range(k):
+        w = Y[:, j].copy()
+        for _ in range(4):
+            before = np.linalg.norm(w)
+            w = w - Q[:, :j] @ (Q[:, :j].T @ w)
+            if np.linalg.norm(w) > eta * before:
+                break
+        nw = np.linalg.norm(w)
+        if not nw > 0.0:
+            raise ValueError(f"column {j} of the block is dependent on the earlier ones")
+        Q[:, j] = w / nw
+    return Q
+
+
+def subspace_iteration(A, V0, iters: int) -> np.ndarray:
+    """`iters` sweeps of V <- orth(A^T (A V)) from V0 ([d][k]); A is [n][d]."""
+    A = _f64(A)
+    V = _f64(V0)
+    for _ in range(iters):
+        V = dgks_orth(A.T @ (A @ V))
+    return V
+
+
+def dominant_subspace(A, k: int) -> np.ndarray:
+    """Top-k right singular vectors of A ([n][d]) via LAPACK SVD: the
+    subspace the iteration converges to (reference only)."""
+    _, _, vt = np.linalg.svd(_f64(A), full_matrices=False)
+    return vt[:k].T
+
+
+def principal_cosines(V1, V2) -> np.ndarray:
+    """Cosines of the principal angles between span(V1) and span(V2)
+    (orthonormal bases), largest first."""
+    return np.linalg.svd(_f64(V1).T @ _f64(V2), compute_uv=False)
+
+
 # ---- diagnostics (not compared against the GPU, used by pins) -------------
 
 def rho_from_norms(x, g) -> float:

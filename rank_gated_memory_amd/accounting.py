@@ -27,6 +27,12 @@ def project_bytes(d: int, k: int, esize: int) -> int:
     return esize * (d * k + d)
 
 
+def gram_bytes(k: int, esize: int) -> int:
+    """Bytes of E = V_k^T V_k - I, read once per gate when the exact residual
+    ratio is used (GSI-TS §2.2's ||r|| / ||x|| for the stored basis)."""
+    return esize * k * k
+
+
 def apply_bytes(d: int, d_out: int, k: int, esize: int, slow: bool) -> int:
     """Bytes of the output phase of one token: M (fast) or W and x (slow), plus y."""
     if slow:

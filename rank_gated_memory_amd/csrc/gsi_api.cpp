@@ -15,6 +15,7 @@
 
 #include "../../include/gsi.h"
 #include "gsi_batched.h"
+#include "gsi_calib.h"
 #include "gsi_internal.h"
 
 namespace gsi {
@@ -23,6 +24,7 @@ hipError_t launch_prepare(int dtype, const void *W, const void *V, void *M, int 
 hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipStream_t s);
 hipError_t launch_stack(int dtype, const FArgs &a, int mode, int max_groups, hipStream_t s);
 hipError_t launch_gram(int dtype, const void *V, void *E, int d, int k, hipStream_t s);
+hipError_t launch_calibrate(const CalibArgs &c, hipStream_t s);
 hipError_t launch_batched(const BArgs &a, hipStream_t s);
 }  // namespace gsi
 
@@ -664,6 +666,62 @@ gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t 
   set_ws(a, ws, h->ws_gate_off, h->ws_need_off, h->ws_pref_off, h->ws_float_off);
   const hipError_t e = launch_batch1(h->dtype, a, apply_grid(h->units_b), phase,
                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSI_OK : GSI_E_HIP;
+}
+
+// ---- basis calibration ----------------------------------------------------
+
+static gsi_status check_calib(const gsi_calib *c) {
+  if (!c) return GSI_E_NULL;
+  const int es = esize_of(c->dtype);
+  if (es == 0) return GSI_E_DTYPE;
+  if (c->n <= 0 || c->d <= 0 || c->k <= 0 || c->k > c->d || c->k > c->n || c->k > kMaxK) return GSI_E_SHAPE;
+  if (c->iters < 0 || c->iters > 1000) return GSI_E_ARG;
+  if (!c->A || !c->V0 || !c->V) return GSI_E_NULL;
+  if (!aligned(c->A, 16) || !aligned(c->V0, 16) || !aligned(c->V, 16)) return GSI_E_ALIGN;
+  return GSI_OK;
+}
+
+size_t gsi_calibrate_workspace(const gsi_calib *c) {
+  if (check_calib(c) != GSI_OK) return 0;
+  return calib_ws_bytes(c->n, c->d, c->k);
+}
+
+size_t gsi_calibrate_status_offset(void) { return 0; }
+
+gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *stream) {
+  const gsi_status s = check_calib(c);
+  if (s != GSI_OK) return s;
+  if (!ws) return GSI_E_NULL;
+  if (!aligned(ws, 256)) return GSI_E_ALIGN;
+  if (ws_bytes < calib_ws_bytes(c->n, c->d, c->k)) return GSI_E_WORKSPACE;
+  CalibArgs a{};
+  a.n = c->n;
+  a.d = c->d;
+  a.k = c->k;
+  a.dtype = c->dtype;
+  a.iters = c->iters;
+  a.A = c->A;
+  a.V0 = c->V0;
+  a.V = c->V;
+  char *w = static_cast<char *>(ws);
+  auto al = [](uint64_t v) { return (v + 255) / 256 * 256; };
+  const uint64_t dk = (uint64_t)c->d * c->k, nk = (uint64_t)c->n * c->k, kk = (uint64_t)c->k * c->k;
+  uint64_t off = 0;
+  a.status = reinterpret_cast<uint32_t *>(w + off);
+  off += al(256);
+  a.vw = reinterpret_cast<float *>(w + off);
+  off += al(dk * 4);
+  a.z = reinterpret_cast<float *>(w + off);
+  off += al(nk * 4);
+  a.y = reinterpret_cast<double *>(w + off);
+  off += al(dk * 8);
+  a.y2 = reinterpret_cast<double *>(w + off);
+  off += al(dk * 8);
+  a.g = reinterpret_cast<double *>(w + off);
+  off += al(kk * 8);
+  a.rinv = reinterpret_cast<double *>(w + off);
+  const hipError_t e = launch_calibrate(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }
 

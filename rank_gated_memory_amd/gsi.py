@@ -38,6 +38,12 @@ class GsiCallStruct(ctypes.Structure):
                 ("wave", c_int32), ("rho", c_void_p), ("slow", c_void_p)]
 
 
+class GsiCalibStruct(ctypes.Structure):
+    _fields_ = [("n", c_int32), ("d", c_int32), ("k", c_int32), ("dtype", c_int32),
+                ("A", c_void_p), ("V0", c_void_p), ("V", c_void_p), ("iters", c_int32),
+                ("reserved", c_int32)]
+
+
 _lib = None
 
 
@@ -72,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.gsi_stack.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
         L.gsi_stack_status_offset.restype = c_size_t
         L.gsi_stack_status_offset.argtypes = [c_void_p]
+        L.gsi_calibrate_workspace.restype = c_size_t
+        L.gsi_calibrate_workspace.argtypes = [POINTER(GsiCalibStruct)]
+        L.gsi_calibrate_status_offset.restype = c_size_t
+        L.gsi_calibrate_status_offset.argtypes = []
+        L.gsi_calibrate.restype = c_int32
+        L.gsi_calibrate.argtypes = [POINTER(GsiCalibStruct), c_void_p, c_size_t, c_void_p]
         L.gsi_stack_phase.restype = c_int32
         L.gsi_stack_phase.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
                                       c_void_p]
@@ -247,3 +259,26 @@ def gsi_stack_phase(plan: Stack, mode: int, phase: int, ws: torch.Tensor, stream
     st = lib().gsi_stack_phase(_ptr(plan.host), _ptr(plan.dev), int(mode), int(phase), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "gsi_stack_phase")
+
+
+def gsi_calibrate(A: torch.Tensor, V0: torch.Tensor, iters: int, V=None, ws=None, stream=None):
+    """Basis of the dominant k-dim subspace of the samples A [n][d] after
+    `iters` sweeps of subspace iteration from V0 [d][k] (random: a cold
+    start; the previous layer's basis: the cascade).  Returns (V, status)
+    where status is the device status word (0 = good) as a 1-element tensor."""
+    if A.dim() != 2 or V0.dim() != 2 or A.shape[1] != V0.shape[0]:
+        raise ValueError("A [n][d] and V0 [d][k] do not chain")
+    if A.dtype != V0.dtype or not (A.is_contiguous() and V0.is_contiguous()):
+        raise ValueError("A and V0 must be contiguous and share a dtype")
+    n, d = A.shape
+    k = V0.shape[1]
+    if V is None:
+        V = torch.empty_like(V0)
+    c = GsiCalibStruct(n, d, k, _dtype_code(A), _ptr(A), _ptr(V0), _ptr(V), int(iters), 0)
+    need = int(lib().gsi_calibrate_workspace(ctypes.byref(c)))
+    if ws is None:
+        ws = workspace(need, A.device)
+    _check(lib().gsi_calibrate(ctypes.byref(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "gsi_calibrate")
+    o = int(lib().gsi_calibrate_status_offset())
+    return V, ws[o:o + 4].view(torch.int32)

@@ -190,6 +190,21 @@ def chain_config(d: int, k: int, f: int, kf: int, layers: int, key, device="cpu"
     return out, h[0]
 
 
+def frame_samples(frame: torch.Tensor, spec: torch.Tensor, n: int, key, device="cpu") -> torch.Tensor:
+    """n activation samples [n][d] = (Z * spec) frame^T with Z ~ N(0, I): the
+    samples' covariance has eigenvalues spec^2 along the orthonormal columns
+    of frame [d][m] (calibration inputs for the basis builder)."""
+    g = generator(device, *key)
+    z = torch.randn((n, frame.shape[1]), generator=g, device=device, dtype=torch.float64)
+    return (z * spec.to(device=device, dtype=torch.float64)) @ frame.to(device=device, dtype=torch.float64).T
+
+
+def gaussian_block(d: int, k: int, key, device="cpu") -> torch.Tensor:
+    """A seeded Gaussian [d][k] block: the random start of a cold calibration."""
+    g = generator(device, *key)
+    return torch.randn((d, k), generator=g, device=device, dtype=torch.float64)
+
+
 def pick_slow(n: int, count: int, key, device="cpu") -> torch.Tensor:
     """Boolean mask with exactly `count` True entries at seeded positions."""
     g = generator("cpu", *key)

@@ -420,9 +420,60 @@ def pin_gram_identity(orc):
             _close(np.dot(r, r), np.dot(x, x) - np.dot(g, g) + g @ E @ g, 1e-10, 1e-10, "gram identity")
 
 
+def _spectral_samples(rng, n, d, spec):
+    """n samples whose covariance has eigenvalues spec**2 along a random orthonormal frame."""
+    F = _orthonormal(rng, d, len(spec))
+    return (rng.standard_normal((n, len(spec))) * spec) @ F.T, F
+
+
+def pin_dgks_orth(orc):
+    """DGKS Gram-Schmidt gives the Q factor of Y = QR with diag(R) > 0:
+    the same matrix as numpy's Householder QR after fixing its column signs,
+    orthonormal to rounding even for an ill-conditioned block."""
+    rng = _rng(29)
+    for cond in (1.0, 1e6):
+        U = _orthonormal(rng, 60, 8)
+        Y = U @ np.diag(np.logspace(0, -np.log10(cond), 8)) @ _orthonormal(rng, 8, 8).T
+        Q = orc.dgks_orth(Y)
+        q, r = np.linalg.qr(Y)
+        q = q * np.sign(np.diag(r))
+        _close(Q, q, 1e-6 if cond > 1 else 1e-12, 1e-6 if cond > 1 else 1e-12, "dgks vs householder")
+        assert np.max(np.abs(Q.T @ Q - np.eye(8))) < 1e-13
+        R = Q.T @ Y
+        assert np.all(np.diag(R) > 0) and np.max(np.abs(np.tril(R, -1))) < 1e-12 * np.abs(R).max()
+
+
+def pin_subspace_iteration(orc):
+    """The iteration converges to the top-k singular subspace (LAPACK SVD)
+    at the rate of the spectral gap, keeps an exact top-k basis fixed, and
+    from a nearby start (the cascade) needs fewer sweeps than from a random
+    start to reach the same accuracy (GSI-TS §2.3)."""
+    rng = _rng(30)
+    d, k = 80, 6
+    spec = np.concatenate([np.linspace(10.0, 6.0, k), np.linspace(2.0, 0.1, d - k)])
+    A, F = _spectral_samples(rng, 400, d, spec)
+    top = orc.dominant_subspace(A, k)
+    assert orc.principal_cosines(top, F[:, :k]).min() > 0.95
+    cold = orc.subspace_iteration(A, rng.standard_normal((d, k)), 30)
+    assert 1.0 - orc.principal_cosines(cold, top).min() < 1e-12
+    fixed = orc.subspace_iteration(A, top, 1)
+    assert 1.0 - orc.principal_cosines(fixed, top).min() < 1e-13
+    near = orc.dgks_orth(top + 0.05 * rng.standard_normal((d, k)))
+    far = rng.standard_normal((d, k))
+
+    def sweeps(V0, tol=1e-10):
+        V = V0
+        for it in range(1, 60):
+            V = orc.subspace_iteration(A, V, 1)
+            if 1.0 - orc.principal_cosines(V, top).min() < tol:
+                return it
+        return 60
+    assert sweeps(near) < sweeps(far)
+
+
 ALL_PINS = [
     pin_identity_basis, pin_full_rank, pin_in_span_and_orthogonal, pin_construction,
     pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
     pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity, pin_nested_bases,
-    pin_storage_rounding, pin_chain, pin_gram_identity,
+    pin_storage_rounding, pin_chain, pin_gram_identity, pin_dgks_orth, pin_subspace_iteration,
 ]

@@ -311,3 +311,31 @@ def test_gram_bytes_and_alignment():
     m = mk_map()
     m.G = FAKE + 0x600008  # misaligned E
     assert prep(m) == E_ALIGN
+
+
+def calib(n=512, d=256, k=16, dtype=1, A=FAKE, V0=FAKE + 0x1000000, V=FAKE + 0x2000000, iters=2):
+    return gsi.GsiCalibStruct(n, d, k, dtype, A, V0, V, iters, 0)
+
+
+def test_calibrate_rejects_before_launch():
+    L = gsi.lib()
+    good = calib()
+    need = L.gsi_calibrate_workspace(ctypes.byref(good))
+    assert need > 0
+    ws = FAKE + 0x3000000
+    def run(c, ws=ws, nb=need):
+        return L.gsi_calibrate(ctypes.byref(c), ws, nb, None)
+    assert L.gsi_calibrate(None, ws, need, None) == E_NULL
+    assert run(calib(k=300)) == E_SHAPE        # k > d
+    assert run(calib(n=8)) == E_SHAPE          # k > n
+    assert run(calib(k=0)) == E_SHAPE
+    assert run(calib(dtype=4)) == E_DTYPE
+    assert run(calib(iters=-1)) == E_ARG
+    assert run(calib(A=0)) == E_NULL
+    assert run(calib(V=FAKE + 8)) == E_ALIGN
+    assert run(good, ws=0) == E_NULL
+    assert run(good, ws=FAKE + 64) == E_ALIGN
+    assert run(good, nb=need - 1) == E_WS
+    assert L.gsi_calibrate_status_offset() == 0
+    # workspace grows with the block
+    assert L.gsi_calibrate_workspace(ctypes.byref(calib(n=4096, d=4096, k=256))) > need

@@ -59,7 +59,35 @@ MUTANTS = {
     # Gram deviation: no identity subtracted, transposed product
     "gram_no_identity": ("gram_deviation", lambda V: f64(V).T @ f64(V)),
     "gram_outer": ("gram_deviation", lambda V: f64(V) @ f64(V).T - np.eye(f64(V).shape[0])),
+    # calibration: no reorthogonalisation pass, no normalisation, no block orthonormalisation
+    "dgks_single_pass": ("dgks_orth", None),
+    "dgks_unnormalised": ("dgks_orth", None),
+    "iteration_one_sided": ("subspace_iteration", None),
 }
+
+
+def _mutant_dgks(how):
+    def dgks_orth(Y, eta=0.7071):
+        Y = f64(Y)
+        d, k = Y.shape
+        Q = np.zeros((d, k))
+        for j in range(k):
+            w = Y[:, j] - Q[:, :j] @ (Q[:, :j].T @ Y[:, j])
+            Q[:, j] = w if how == "unnormalised" else w / np.linalg.norm(w)
+        return Q
+    return dgks_orth
+
+
+def _mutant_iteration(mod):
+    # columns normalised one by one instead of orthonormalised as a block:
+    # every column drifts toward the top direction
+    def subspace_iteration(A, V0, iters):
+        V = f64(V0)
+        for _ in range(iters):
+            V = f64(A).T @ (f64(A) @ V)
+            V = V / np.linalg.norm(V, axis=0)
+        return V
+    return subspace_iteration
 
 
 def _mutant_to_storage(mod, how):
@@ -134,6 +162,10 @@ def test_pins_catch_mutant(name):
     elif name.startswith("storage_"):
         fn = _mutant_to_storage(mod, {"storage_truncates": "trunc", "storage_ties_away": "away",
                                       "storage_bf16_as_fp32": "as_fp32"}[name])
+    elif name.startswith("dgks_"):
+        fn = _mutant_dgks("unnormalised" if name == "dgks_unnormalised" else "single")
+    elif name == "iteration_one_sided":
+        fn = _mutant_iteration(mod)
     elif name.startswith("chain_"):
         fn = _mutant_chain(mod, {"chain_unrounded_input": "unrounded", "chain_ignores_offset": "no_offset",
                                  "chain_reads_previous_call": "previous"}[name])
