@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=512)
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default="gptj6b-28L",
-                   choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep"])
+                   choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep",
+                            "calibrate-gptj6b-28L"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--exact-rho", action="store_true",
                    help="every map caches E = V^T V - I and gates on the exact residual ratio")
@@ -465,6 +466,102 @@ def bench_sweep(args):
     }), flush=True)
 
 
+def bench_calibrate(args):
+    """Basis calibration of a GPT-J-shaped 28-layer stack on the GPU.
+
+    Per layer three inputs are calibrated (the block input read by qkv and
+    fc_in, k=256; the attention output read by out, k=256; fc_in's output
+    read by fc_out, d=16384, k=512) from n=2048 synthetic activation samples
+    each, whose dominant subspace follows a depth cascade (rotated from
+    layer to layer, mean principal cosine > 0.9) over a weaker tail.  Cold:
+    every input from a Gaussian start, `cold` sweeps.  Cascade (GSI-TS
+    §2.3): layer 0 cold, every later layer warm-started from the same
+    input's basis one layer below, `warm` sweeps.  Reports seconds for the
+    whole stack and the worst principal-angle gap to the samples' own top-k
+    subspace (fp64 SVD on the host, outside the timed region) for a sample
+    of inputs.
+    """
+    import numpy as np
+    import torch
+
+    from rank_gated_memory_amd import gsi, synth
+
+    dev = torch.device("cuda:0")
+    layers, n, cold, warm = args.layers or 28, 2048, 8, 2
+    inputs = (("block_in", 4096, 256), ("attn_out", 4096, 256), ("mlp_hidden", 16384, 512))
+    t0 = time.perf_counter()
+    data = []
+    for r, (name, d, k) in enumerate(inputs):
+        frames = synth.cascade_frames(d, k, 256, layers, (7, 0, r, synth.P_CASCADE), dev)
+        spec = torch.cat([torch.linspace(8.0, 4.0, k, dtype=torch.float64),
+                          torch.linspace(1.0, 0.2, 256, dtype=torch.float64)])
+        row = []
+        for l in range(layers):
+            A = synth.frame_samples(torch.cat(frames[l], 1), spec, n, (7, l, r, 1), dev).to(torch.bfloat16)
+            frames[l] = None
+            row.append(A)
+        R0 = synth.gaussian_block(d, k, (7, 0, r, 2), dev).to(torch.bfloat16)
+        data.append((name, d, k, row, R0))
+    torch.cuda.synchronize()
+    log(f"calibration samples drawn in {time.perf_counter() - t0:.1f}s")
+    wss = {(d, k): gsi.workspace(int(gsi.lib().gsi_calibrate_workspace(ctypes_calib(n, d, k))), dev)
+           for _, d, k, _, _ in data}
+
+    def run(mode):
+        out = []
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for name, d, k, row, R0 in data:
+            prev = None
+            bases = []
+            for l, A in enumerate(row):
+                if mode == "cascade" and prev is not None:
+                    V, _ = gsi.gsi_calibrate(A, prev, warm, ws=wss[(d, k)])
+                else:
+                    V, _ = gsi.gsi_calibrate(A, R0, cold, ws=wss[(d, k)])
+                bases.append(V)
+                prev = V
+            out.append(bases)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t, out
+
+    run("cascade")  # warm-up (module load, first launches)
+    t_cold, cold_b = run("cold")
+    t_casc, casc_b = run("cascade")
+    status = max(int(ws[:4].view(torch.int32).item()) for ws in wss.values())
+    log(f"cold ({cold} sweeps): {t_cold:.3f}s; cascade ({cold} then {warm} sweeps): {t_casc:.3f}s; status {status}")
+
+    from oracle import gsi_oracle as orc
+    gaps = {"cold": 0.0, "cascade": 0.0}
+    for (name, d, k, row, _), cb, wb in zip(data, cold_b, casc_b):
+        for l in (1, layers // 2, layers - 1):
+            A = row[l].to("cpu", torch.float64).numpy()
+            top = orc.dominant_subspace(A, k)
+            for key, b in (("cold", cb), ("cascade", wb)):
+                V = orc.dgks_orth(b[l].to("cpu", torch.float64).numpy())
+                gaps[key] = max(gaps[key], float(1.0 - orc.principal_cosines(V, top).min()))
+    log(f"worst principal-angle gap to the samples' top-k subspace: cold {gaps['cold']:.2e}, "
+        f"cascade {gaps['cascade']:.2e}")
+    print(json.dumps({
+        "metric": "GSI basis calibration time, 28-layer GPT-J-shaped stack (84 inputs)",
+        "value": t_casc, "unit": "s", "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": t_casc * 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"calibrate-gptj6b-28L: {layers} layers x 3 inputs (4096/k256, 4096/k256, "
+                               f"16384/k512), {n} samples each; cascade {cold} cold sweeps at layer 0 then "
+                               f"{warm} warm sweeps per layer; cold {cold} sweeps everywhere",
+                   "cold_s": t_cold, "cascade_s": t_casc, "saving": 1.0 - t_casc / t_cold,
+                   "worst_gap_cold": gaps["cold"], "worst_gap_cascade": gaps["cascade"], "status": status},
+    }), flush=True)
+
+
+def ctypes_calib(n, d, k):
+    import ctypes
+
+    from rank_gated_memory_amd import gsi
+    return ctypes.byref(gsi.GsiCalibStruct(n, d, k, 1, 16, 16, 16, 1, 0))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -476,6 +573,9 @@ def main():
         return
     if args.workload == "sweep":
         bench_sweep(args)
+        return
+    if args.workload == "calibrate-gptj6b-28L":
+        bench_calibrate(args)
         return
     import numpy as np
     import torch
