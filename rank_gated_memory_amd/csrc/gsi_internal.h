@@ -180,9 +180,14 @@ struct UnitShape {
 // Output units aim at this many bytes of M (fast) or W (slow), so that a
 // contiguous range of units is a balanced share of a launch.
 #ifndef GSI_APPLY_UNIT_KB
-#define GSI_APPLY_UNIT_KB 128
+#define GSI_APPLY_UNIT_KB 256
 #endif
 constexpr int64_t kApplyUnitBytes = GSI_APPLY_UNIT_KB * 1024;
+// Slow units stage x (up to 32 KiB) once per unit: larger units amortise it.
+#ifndef GSI_SLOW_UNIT_KB
+#define GSI_SLOW_UNIT_KB 256
+#endif
+constexpr int64_t kSlowUnitBytes = GSI_SLOW_UNIT_KB * 1024;
 
 // fine: latency-bound waves (few bytes per wave) take the smallest fast
 // output units, one 64-row image tile whose columns are split over the
@@ -208,7 +213,7 @@ inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_p
   if (fine) ft = 1;
   s.fast_tiles = (int32_t)ft;
   s.fast_units = (int32_t)((tiles + ft - 1) / ft);
-  int64_t srows = kApplyUnitBytes / ((int64_t)d * esize);
+  int64_t srows = kSlowUnitBytes / ((int64_t)d * esize);
   srows = srows / kWaves * kWaves;
   if (srows < kWaves) srows = kWaves;
   if (srows > 256) srows = 256;
