@@ -128,7 +128,7 @@ DESC = np.dtype([("ptrs", "<u8", 7), ("d", "<i4"), ("d_out", "<i4"), ("k", "<i4"
                  ("a_begin", "<i4"), ("a_units", "<i4"), ("a_rows", "<i4"), ("fast_units", "<i4"),
                  ("slow_units", "<i4"), ("slow_rows", "<i4"), ("part_off", "<i8"), ("g_off", "<i8"),
                  ("gate_off", "<i4"), ("fast_tiles", "<i4"), ("flags", "<i4"), ("wave", "<i4"),
-                 ("share_next", "<i4"), ("pad", "<i4", 3)])
+                 ("share_next", "<i4"), ("pad", "<i4"), ("G", "<u8")])
 
 
 def header(plan):
@@ -301,6 +301,22 @@ def test_stack_plan_shares_projections():
     assert len(set(desc["g_off"][[0, 2, 3, 5]].tolist())) == 4
     assert set(unit_call.tolist()) == {0, 2, 3, 5}
     assert h["units_a"] == sum(desc["a_units"])
+
+
+def test_stack_plan_many_projection_units():
+    """Latency-bound waves split V_k into 16-row units (bf16, k = 512: 16 KiB
+    each), up to 64 per call; the last unit may be ragged.  Partial rows of
+    the calls do not overlap and fit the float region."""
+    specs = [(592, 200, 512, 1), (536, 72, 512, 1), (512, 64, 512, 1), (2048, 128, 512, 1)]
+    st, plan, _ = build_plan(specs, waves=[0, 1, 2, 3])
+    assert st == GSI_OK
+    h, desc, *_ = plan_tables(plan)
+    assert list(desc["a_units"]) == [37, 34, 32, 64]
+    assert list(desc["a_rows"]) == [16, 16, 16, 32]
+    spans = sorted((int(o), int(o) + int(u) * (int(k) + 4))
+                   for o, u, k in zip(desc["part_off"], desc["a_units"], desc["k"]))
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    assert h["ws_float_off"] + 4 * spans[-1][1] <= h["ws_ctl_off"]
 
 
 def test_gram_bytes_and_alignment():

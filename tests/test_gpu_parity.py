@@ -491,3 +491,72 @@ def test_shared_projection_stack(dtype):
     gsi.gsi_stack_phase(st, gsi.GATED, gsi.PHASE_APPLY, ws)
     sync()
     assert all(torch.equal(o[3], a) for o, a in zip(outs, ref))
+
+
+# ------------------------------------------------ many projection units ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_many_projection_units(dtype):
+    """Calls split into many 16-row projection units (d = 592: 37 units;
+    d = 536: 34 units, the last of 8 rows; d = 2048: 64 units of 32 rows in a
+    stack).  Oracle parity through gsi_linear and through a stack of one call
+    per wave, repeated runs on one workspace (the counters must return to
+    zero), and the same bits from the two-launch form."""
+    shapes = [(592, 200, 512), (536, 72, 512), (2048, 128, 512)]
+    items = []
+    for i, (d, d_out, k) in enumerate(shapes):
+        W = synth.gaussian_weight(d_out, d, (95, 0, i, 0), dtype=dtype)
+        v, u = synth.orthonormal_frame(d, k, 16, (95, 0, i, 1))
+        mask = torch.tensor([False, True, False])
+        X, _ = synth.tokens(v, u, mask, (95, 0, i))
+        items.append((W, v.to(dtype), X.to(dtype)))
+    maps = [new_map(W, V) for W, V, _ in items]
+    for (W, V, X), m in zip(items, maps):
+        Xd = X.to(DEV)
+        lws = gsi.workspace(gsi.gsi_linear_workspace(m, 1), DEV)
+        for _ in range(2):
+            ys, rs, ss = [], [], []
+            for t in range(X.shape[0]):
+                y, r, s = gsi.gsi_linear(m, Xd[t:t + 1], 0.05, ws=lws)
+                ys.append(y)
+                rs.append(r)
+                ss.append(s)
+            sync()
+            compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(torch.cat(ys)), torch.cat(ss).cpu().numpy(),
+                           f64(torch.cat(rs)), dtype, rho_tol=2e-2, what=f"linear d={W.shape[1]}")
+    calls, outs = [], []
+    for wave, ((W, V, X), m) in enumerate(zip(items, maps)):
+        for t in range(X.shape[0]):
+            y = torch.empty(W.shape[0], dtype=dtype, device=DEV)
+            r = torch.empty(1, dtype=torch.float32, device=DEV)
+            s = torch.empty(1, dtype=torch.uint8, device=DEV)
+            calls.append((m, X[t].to(DEV), y, 0.05, r, s, wave))
+            outs.append((W, V, X[t:t + 1], y, r, s))
+    st = gsi.Stack(calls)
+    ws = gsi.workspace(st.ws_bytes, DEV)
+    ref = None
+    for _ in range(3):
+        gsi.gsi_stack(st, gsi.GATED, ws)
+        sync()
+        got = [tuple(t.clone() for t in o[3:]) for o in outs]
+        if ref is None:
+            ref = got
+        assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(got, ref))
+    for W, V, X, y, r, s in outs:
+        compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y)[None], np.array([int(s.item())]),
+                       np.array([float(r.item())]), dtype, rho_tol=2e-2, what=f"stack d={W.shape[1]}")
+    assert st.status(ws) == 0
+    # one wave: the single launch and the two-launch form give the same bits
+    st1 = gsi.Stack([c[:6] for c in calls])
+    ws1 = gsi.workspace(st1.ws_bytes, DEV)
+    gsi.gsi_stack(st1, gsi.GATED, ws1)
+    sync()
+    one = [tuple(t.clone() for t in o[3:]) for o in outs]
+    assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(one, ref))
+    for _ in range(2):
+        gsi.gsi_stack_phase(st1, gsi.GATED, gsi.PHASE_PROJECT, ws1)
+        gsi.gsi_stack_phase(st1, gsi.GATED, gsi.PHASE_APPLY, ws1)
+        sync()
+        two = [tuple(t.clone() for t in o[3:]) for o in outs]
+        assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(two, one))
+    assert st1.status(ws1) == 0
