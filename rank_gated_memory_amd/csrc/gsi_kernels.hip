@@ -116,6 +116,23 @@ struct Vec<bf16_t> {
   }
 };
 
+// Streaming 16-byte loads of data read once per launch (V_k, M and W rows):
+// marked nontemporal so that they do not displace the lines that are
+// reused.  On this part a chunked streaming read reaches ~7.2 TB/s this way
+// against ~6.3 TB/s with ordinary loads.
+#ifndef GSI_NT_LOADS
+#define GSI_NT_LOADS 1
+#endif
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+#if GSI_NT_LOADS
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+#else
+  return *p;
+#endif
+}
+
 // One element of y: agent-coherent when a later wave of the same launch reads it.
 template <typename T>
 __device__ __forceinline__ void store_y(const CallDesc &cd, int i, float v) {
@@ -250,7 +267,7 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
       float xv[UNROLL];
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
-        v[j] = vp[(size_t)(r + j * rpp) * tpr];
+        v[j] = ld_stream(vp + (size_t)(r + j * rpp) * tpr);
         xv[j] = XC ? Vec<T>::load1c(xp, r + j * rpp) : Vec<T>::load1(xp, r + j * rpp);
       }
 #pragma unroll
@@ -264,7 +281,7 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
     }
     // remainder rows of the last chunk of a call
     for (; r < rows; r += rpp) {
-      const uint4 v = vp[(size_t)r * tpr];
+      const uint4 v = ld_stream(vp + (size_t)r * tpr);
       const float xv = XC ? Vec<T>::load1c(xp, r) : Vec<T>::load1(xp, r);
       float f[VW];
       Vec<T>::unpack(v, f);
@@ -432,7 +449,7 @@ __device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, co
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
       const int cg = cg0 + j * kWaves;
-      v[j] = cg < kv ? m[(size_t)cg * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+      v[j] = cg < kv ? ld_stream(m + (size_t)cg * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
@@ -486,8 +503,8 @@ __device__ __forceinline__ void fast_unit(const CallDesc &cd, int local, const f
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         const bool ok = cg + j < kv;
-        va[j] = ok ? ma[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
-        vb[j] = (ok && two) ? mb[(size_t)(cg + j) * kTileRows] : make_uint4(0u, 0u, 0u, 0u);
+        va[j] = ok ? ld_stream(ma + (size_t)(cg + j) * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
+        vb[j] = (ok && two) ? ld_stream(mb + (size_t)(cg + j) * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
@@ -533,8 +550,8 @@ __device__ __forceinline__ void slow_unit(const CallDesc &cd, int local, const u
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         const int vv = v0 + j * 64;
-        wA[j] = vv < nv ? wa[vv] : make_uint4(0u, 0u, 0u, 0u);
-        wB[j] = (two && vv < nv) ? wb[vv] : make_uint4(0u, 0u, 0u, 0u);
+        wA[j] = vv < nv ? ld_stream(wa + vv) : make_uint4(0u, 0u, 0u, 0u);
+        wB[j] = (two && vv < nv) ? ld_stream(wb + vv) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
