@@ -1212,9 +1212,13 @@ size_t stack_lds_bytes(int max_d, int max_k, int esize) {
 #endif
 constexpr size_t kLdsPerCu = 160 * 1024;
 
+#ifndef GSI_STACK_UNROLL
+#define GSI_STACK_UNROLL 8
+#endif
+
 template <typename T, int MODE>
 hipError_t launch_stack_mode(const FArgs &a, int max_groups, hipStream_t s) {
-  constexpr int U = 8;
+  constexpr int U = GSI_STACK_UNROLL;
   // Fewer concurrent streams than the registers allow read HBM faster
   // (512 workgroups beat 768 on the 112-map step), and they must be spread
   // evenly over the CUs: the LDS request is raised so that at most
