@@ -226,8 +226,6 @@ static gsi_status linear_batched(const gsi_map *map, const void *x, void *y, int
     a.glo = reinterpret_cast<uint16_t *>(w + b.glo_off);
     a.flags = reinterpret_cast<int32_t *>(w + b.flags_off);
     a.zeros = w + b.zeros_off;
-    a.ctl = reinterpret_cast<int32_t *>(w + b.ctl_off);
-    a.list = reinterpret_cast<int32_t *>(w + b.list_off);
     if (launch_batched(a, st) != hipSuccess) return GSI_E_HIP;
   }
   return GSI_OK;

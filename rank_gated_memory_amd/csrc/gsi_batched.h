@@ -29,13 +29,11 @@ struct BArgs {
   uint16_t *glo;   // [n][kpad] bf16(g - hi)
   int32_t *flags;  // [n] 1 = slow
   const void *zeros;  // 256 bytes of the workspace that stay zero
-  int32_t *ctl;    // [0] gate arrival counter (back to 0 after each launch), [1] fast count, [2] slow count
-  int32_t *list;   // [2][n]: fast tokens, then slow tokens, each in increasing order
 };
 
 struct BatchShape {
   int32_t kpad, kc, splits;
-  uint64_t zeros_off, ctl_off, part_off, xxp_off, ghi_off, glo_off, flags_off, list_off, total;
+  uint64_t zeros_off, part_off, xxp_off, ghi_off, glo_off, flags_off, total;
 };
 
 // Projection GEMM G = X V_k: 64 x 64 tiles of G, each split over K into
@@ -57,8 +55,6 @@ inline BatchShape batch_shape(int n, int d, int k) {
   uint64_t off = 0;
   b.zeros_off = off;  // never written: zero since the caller zero-filled the workspace
   off += 256;
-  b.ctl_off = off;    // the counter is zero before and after every launch
-  off += 256;
   b.part_off = off;
   off = align_up(off + (uint64_t)b.splits * n * k * 4, 256);
   b.xxp_off = off;
@@ -69,8 +65,6 @@ inline BatchShape batch_shape(int n, int d, int k) {
   off = align_up(off + (uint64_t)n * b.kpad * 2, 256);
   b.flags_off = off;
   off = align_up(off + (uint64_t)n * 4, 256);
-  b.list_off = off;
-  off = align_up(off + (uint64_t)2 * n * 4, 256);
   b.total = off;
   return b;
 }

@@ -78,28 +78,6 @@ __device__ __forceinline__ float rho_of(float xx, float gg) {
 
 namespace {
 
-__device__ __forceinline__ void store_flag(int32_t *p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_flag(const int32_t *p) {
-  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Hands this workgroup's agent-coherent stores over to whichever workgroup
-// arrives last at counter c (of `expect` arrivals); returns true in that one,
-// which also puts the counter back to 0 for the next launch.
-__device__ __forceinline__ bool arrive_last(int32_t *c, int expect, int *s_last) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = prev == expect - 1;
-    if (*s_last) *c = 0;
-  }
-  __syncthreads();
-  return *s_last != 0;
-}
-
 // Inclusive workgroup scan of two counters at once (Hillis-Steele in LDS).
 __device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
   const int tid = threadIdx.x;
@@ -113,6 +91,34 @@ __device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
     __syncthreads();
   }
   return sh[tid];
+}
+
+// Tokens of each path in increasing order, from the gate flags: the fast
+// tokens in idx[0, nf), the slow ones in idx[nf, n).  Every output
+// workgroup compacts the n flags itself (one load per thread at n = 256 and
+// a scan in LDS), so the gate needs no grid-wide step.  Returns (nf, ns).
+__device__ __forceinline__ int2 path_lists(const BArgs &a, int16_t *idx, int2 *scan) {
+  const int tid = threadIdx.x;
+  const int per = (a.n + kBlock - 1) / kBlock;
+  const int c0 = tid * per;
+  int fl[kMaxBatch / kBlock];
+  int2 mine = make_int2(0, 0);
+#pragma unroll
+  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+    fl[i] = (i < per && c0 + i < a.n) ? a.flags[c0 + i] : -1;
+    mine.x += fl[i] == 0;
+    mine.y += fl[i] == 1;
+  }
+  const int2 inc = block_scan2(mine, scan);
+  const int2 tot = scan[kBlock - 1];
+  int wf = inc.x - mine.x, ws = tot.x + inc.y - mine.y;
+#pragma unroll
+  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+    if (fl[i] == 0) idx[wf++] = (int16_t)(c0 + i);
+    if (fl[i] == 1) idx[ws++] = (int16_t)(c0 + i);
+  }
+  __syncthreads();
+  return tot;
 }
 
 }  // namespace
@@ -217,17 +223,13 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
 // Gate per token: one workgroup per token sums the split partials of g in
 // split order (every partial of a column requested before any is summed),
 // writes g as bf16 hi + lo (g = hi + lo to ~2^-16) for the fast GEMM, and
-// forms rho and the gate (GSI-TS §2.2).  The flags travel to the last
-// workgroup to finish the way the batch-1 partials do (agent-scope stores,
-// s_waitcnt 0, barrier, relaxed agent-scope counter); that workgroup writes
-// the per-path token lists and counts the output kernels read.
+// forms rho and the gate (GSI-TS §2.2).  The flags are all the output
+// kernels need: each of their workgroups compacts the tokens itself.
 // ---------------------------------------------------------------------------
 template <int MODE>
 __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   __shared__ float sh[kWaves];
   __shared__ float gl[1024];  // g of the token, for the exact rho
-  __shared__ int2 scan[kBlock];
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   float gg = 0.f;
@@ -274,33 +276,9 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
   if (tid == 0) {
     const float rho = a.G ? rho_exact(xx, ggt, q) : rho_of(xx, ggt);
     const int slow = MODE == 2 ? 1 : (MODE == 1 ? 0 : !(rho < a.eps));
-    store_flag(a.flags + t, slow);
+    a.flags[t] = slow;
     if (a.rho) a.rho[t] = rho;
     if (a.slow) a.slow[t] = (uint8_t)slow;
-  }
-  if (!arrive_last(a.ctl, a.n, &s_last)) return;
-
-  // compaction: tokens of each path in increasing order
-  const int per = (a.n + kBlock - 1) / kBlock;
-  const int c0 = tid * per;
-  int fl[kMaxBatch / kBlock];
-  int2 mine = make_int2(0, 0);
-#pragma unroll
-  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
-    fl[i] = (i < per && c0 + i < a.n) ? load_flag(a.flags + c0 + i) : -1;
-    mine.x += fl[i] == 0;
-    mine.y += fl[i] == 1;
-  }
-  const int2 inc = block_scan2(mine, scan);
-  int wf = inc.x - mine.x, ws = inc.y - mine.y;
-#pragma unroll
-  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
-    if (fl[i] == 1) a.list[a.n + ws++] = c0 + i;
-    if (fl[i] == 0) a.list[wf++] = c0 + i;
-  }
-  if (tid == kBlock - 1) {
-    a.ctl[1] = inc.x;
-    a.ctl[2] = inc.y;
   }
 }
 
@@ -415,21 +393,18 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
 struct OutLds {
   u32x4_t Bs[2][8][64];                  // double-buffered 64-wide K chunk: [k group][column]
   u32x4_t As[kWaves][2 * 64 * kOutArow];  // each wavefront's A chunk
-  int16_t idx[kMaxBatch];                // tokens of the path
+  int16_t idx[kMaxBatch];                // tokens of both paths (path_lists)
+  int2 scan[kBlock];
 };
 
 template <int PATH>
-__device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L) {
+__device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, const int16_t *idx,
+                                          int count) {
   auto &Bs = L.Bs;
   auto &As = L.As;
-  auto &idx = L.idx;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int o0 = blockIdx.x * 64;
-  const int count = a.ctl[1 + PATH];
-  if (count <= kThin) return;  // none, or few enough for bthin_kernel
-  for (int i = tid; i < count; i += kBlock) idx[i] = (int16_t)a.list[PATH * a.n + i];
-  __syncthreads();
+  const int o0 = tile * 64;
   // one zero piece per lane (a uniform fallback address becomes a branch)
   const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
 
@@ -492,14 +467,21 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L) {
   }
 }
 
-// Both paths in one launch (blockIdx.y = path): a kernel boundary costs
-// microseconds even when the kernel has nothing to do.
+// Both paths in one launch: the workgroups (about one per CU) walk the
+// 64-column tiles of every path with more than kThin tokens, fast path
+// first; with no such path they leave after the compaction.
 __global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
   __shared__ __align__(16) OutLds L;
-  if (blockIdx.y == 0)
-    bout_path<0>(a, L);
-  else
-    bout_path<1>(a, L);
+  const int2 cnt = path_lists(a, L.idx, L.scan);
+  const int tiles = (a.d_out + 63) / 64;
+  const int nf = cnt.x > kThin ? tiles : 0;
+  const int ns = cnt.y > kThin ? tiles : 0;
+  for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
+    if (it < nf)
+      bout_path<0>(a, L, it, L.idx, cnt.x);
+    else
+      bout_path<1>(a, L, it - nf, L.idx + cnt.x, cnt.y);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -617,14 +599,11 @@ constexpr int kThinPieces = ThinLds<0>::kPieces > ThinLds<1>::kPieces ? ThinLds<
 static_assert(kThinPieces * 16 >= 2 * 4 * 64 * 4, "the final sums reuse a wavefront's region");
 
 template <int PATH>
-__device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], int *toks) {
-  const int count = a.ctl[1 + PATH];
-  if (count == 0 || count > kThin) return;
+__device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], const int *toks,
+                                           int rb) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int r0 = blockIdx.x * 16;
-  if (tid < kThin) toks[tid] = tid < count ? a.list[PATH * a.n + tid] : -1;
-  __syncthreads();
+  const int r0 = rb * 16;
   // one zero piece per lane (a uniform fallback address becomes a branch)
   const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
   const int K = PATH == 0 ? a.kpad : a.d;
@@ -667,16 +646,34 @@ __device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinP
     const int r = r0 + 4 * (l >> 4) + i;
     if (t >= 0 && r < a.d_out) Y[(size_t)t * a.d_out + r] = f2bf(v);
   }
+  __syncthreads();  // every wavefront's region is free again
 }
 
-// Both paths in one launch (blockIdx.y = path).
+// Both paths in one launch: the workgroups walk the 16-row blocks of every
+// path with 1 to kThin tokens; with no such path they leave after the
+// compaction.
 __global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
   __shared__ u32x4_t lds[kWaves][kThinPieces];
-  __shared__ int toks[kThin];
-  if (blockIdx.y == 0)
-    bthin_path<0>(a, lds, toks);
-  else
-    bthin_path<1>(a, lds, toks);
+  __shared__ int16_t idx[kMaxBatch];
+  __shared__ int2 scan[kBlock];
+  __shared__ int toks[2][kThin];
+  const int2 cnt = path_lists(a, idx, scan);
+  const int tid = threadIdx.x;
+  if (tid < 2 * kThin) {
+    const int p = tid / kThin, i = tid % kThin;
+    const int c = p == 0 ? cnt.x : cnt.y;
+    toks[p][i] = i < c ? idx[(p == 0 ? 0 : cnt.x) + i] : -1;
+  }
+  __syncthreads();
+  const int rbs = (a.d_out + 15) / 16;
+  const int nf = (cnt.x > 0 && cnt.x <= kThin) ? rbs : 0;
+  const int ns = (cnt.y > 0 && cnt.y <= kThin) ? rbs : 0;
+  for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
+    if (it < nf)
+      bthin_path<0>(a, lds, toks[0], it);
+    else
+      bthin_path<1>(a, lds, toks[1], it - nf);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -753,10 +750,19 @@ hipError_t launch_batched(const BArgs &a, hipStream_t s) {
   else
     hipLaunchKernelGGL(bgate_kernel<0>, gg, dim3(kBlock), 0, s, a);
   // Each path has a wide kernel (more than kThin tokens) and a row-streaming
-  // one (at most kThin); the one that does not apply returns at once.
-  // One launch holds the wide kernels of both paths, one the row-streaming ones.
-  hipLaunchKernelGGL(bout_kernel, dim3((a.d_out + 63) / 64, 2), dim3(kBlock), 0, s, a);
-  hipLaunchKernelGGL(bthin_kernel, dim3((a.d_out + 15) / 16, 2), dim3(kBlock), 0, s, a);
+  // one (at most kThin); one launch holds the wide kernels of both paths,
+  // one the row-streaming ones.  Their grids are what fits on the chip at
+  // once: the workgroups loop over the work there is.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, bthin_kernel, kBlock, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  const int tiles = (a.d_out + 63) / 64, rbs = (a.d_out + 15) / 16;
+  hipLaunchKernelGGL(bout_kernel, dim3(cus < 2 * tiles ? cus : 2 * tiles), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(bthin_kernel, dim3(occ * cus < 2 * rbs ? occ * cus : 2 * rbs), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
