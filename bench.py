@@ -293,7 +293,7 @@ def kernel_source_sha() -> str:
     """sha256 of the kernel sources; counter figures are only reported for the code they measured."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gsi_kernels.hip", "gsi_internal.h"):
+    for f in ("gsi_kernels.hip", "gsi_internal.h", "gsi_gram.h"):
         with open(os.path.join(ROOT, "rank_gated_memory_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
