@@ -718,7 +718,9 @@ gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *st
   off += al(dk * 8);
   a.g = reinterpret_cast<double *>(w + off);
   off += al(kk * 8);
-  a.rinv = reinterpret_cast<double *>(w + off);
+  a.r = reinterpret_cast<double *>(w + off);
+  off += al(kk * 8);
+  a.dinv = reinterpret_cast<double *>(w + off);
   const hipError_t e = launch_calibrate(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }

@@ -6,7 +6,8 @@
 //
 // One sweep: Z = A V (fp32 accumulation), Y = A^T Z (fp32 accumulation,
 // stored fp64), then Y = QR by CholeskyQR2 in fp64: G = Y^T Y, G = R^T R
-// (Cholesky), Y <- Y R^-1, and the same once more to restore
+// (blocked Cholesky), Y <- Y R^-1 (blocked substitution), and the same once
+// more to restore
 // orthogonality to rounding.  The Q factor with a positive diagonal R is
 // unique, so this is the same basis that Gram-Schmidt (DGKS) gives.
 // Everything runs on the device; a Cholesky breakdown (a rank-deficient
@@ -97,57 +98,244 @@ __global__ void __launch_bounds__(kCB) gemm_kernel(const TX *__restrict__ X, con
     }
 }
 
-// In place on G [k][k] (fp64, symmetric positive definite): the upper
-// Cholesky factor R (G = R^T R) in the upper triangle, then R^-1 into Rinv
-// (upper triangular).  One workgroup.  A pivot that keeps at most 1e-12 of
-// its column's squared norm (G_jj) means the block is numerically rank
+// Blocked fp64 factorisation, 64 x 64 tiles in LDS (rows padded to 65).
+constexpr int kNb = 64;
+constexpr int kLd = kNb + 1;
+
+// dst[r][c] = M[(r0 + r) * ld + c0 + c] for r < nr, c < nc, zero elsewhere.
+__device__ __forceinline__ void load_tile(double (*dst)[kLd], const double *M, size_t ld, int r0, int c0,
+                                          int nr, int nc) {
+  for (int e = threadIdx.x; e < kNb * kNb; e += kCB) {
+    const int r = e / kNb, c = e % kNb;
+    dst[r][c] = (r < nr && c < nc) ? M[(size_t)(r0 + r) * ld + c0 + c] : 0.0;
+  }
+}
+
+// This thread's 4 x 4 outputs of a 64 x 64 tile: rows ti.., columns tj..
+__device__ __forceinline__ int tile_ti() { return (threadIdx.x >> 4) * 4; }
+__device__ __forceinline__ int tile_tj() { return (threadIdx.x & 15) * 4; }
+
+// acc -= A^T B over the 64 rows of A and B (A^T: A read by columns).
+__device__ __forceinline__ void sub_atb(double (&acc)[4][4], const double (*A)[kLd], const double (*B)[kLd]) {
+  const int ti = tile_ti(), tj = tile_tj();
+#pragma unroll 4
+  for (int i = 0; i < kNb; ++i) {
+    double av[4], bv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) av[x] = A[i][ti + x];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) bv[y] = B[i][tj + y];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = fma(-av[x], bv[y], acc[x][y]);
+  }
+}
+
+// acc -= A B (A read by rows).
+__device__ __forceinline__ void sub_ab(double (&acc)[4][4], const double (*A)[kLd], const double (*B)[kLd]) {
+  const int ti = tile_ti(), tj = tile_tj();
+#pragma unroll 4
+  for (int i = 0; i < kNb; ++i) {
+    double av[4], bv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) av[x] = A[ti + x][i];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) bv[y] = B[i][tj + y];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = fma(-av[x], bv[y], acc[x][y]);
+  }
+}
+
+__device__ __forceinline__ void acc_from_tile(double (&acc)[4][4], const double (*T)[kLd]) {
+  const int ti = tile_ti(), tj = tile_tj();
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = T[ti + x][tj + y];
+}
+
+__device__ __forceinline__ void acc_to_tile(double (*T)[kLd], const double (&acc)[4][4]) {
+  const int ti = tile_ti(), tj = tile_tj();
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) T[ti + x][tj + y] = acc[x][y];
+}
+
+// R (upper, [k][k]) with G = R^T R, by the left-looking blocked Cholesky
+// (one workgroup; 64 x 64 blocks): for block row J,
+//     S = G_JJ - sum_{I<J} R_IJ^T R_IJ,   R_JJ = chol(S)      (in LDS)
+//     R_JL = R_JJ^-T (G_JL - sum_{I<J} R_IJ^T R_IL)  for L > J.
+// The inverse of each diagonal block goes to Dinv[J] (64 x 64, upper): the
+// solve for Q = Y R^-1 needs only those.  A pivot that keeps at most 1e-12
+// of its column's squared norm (G_jj) means the block is numerically rank
 // deficient (the fp32 products leave ~1e-14 there): status <- 1.
-__global__ void __launch_bounds__(kCB) chol_inv_kernel(double *G, double *Rinv, int k, uint32_t *status) {
-  __shared__ double colj[1024];
+__global__ void __launch_bounds__(kCB) chol_kernel(const double *G, double *R, double *Dinv, int k,
+                                                   uint32_t *status) {
+  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
+  __shared__ double diag0[kNb];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
+  const int ti = tile_ti(), tj = tile_tj();
+  const int nbk = (k + kNb - 1) / kNb;
   if (tid == 0) s_bad = 0;
+  for (int J = 0; J < nbk; ++J) {
+    const int c0 = J * kNb, nJ = min(kNb, k - c0);
+    __syncthreads();
+    load_tile(S, G, k, c0, c0, nJ, nJ);
+    __syncthreads();
+    if (tid < kNb) diag0[tid] = S[tid][tid];
+    double acc[4][4];
+    acc_from_tile(acc, S);
+    for (int I = 0; I < J; ++I) {
+      __syncthreads();
+      load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
+      __syncthreads();
+      sub_atb(acc, Ta, Ta);
+    }
+    __syncthreads();
+    acc_to_tile(S, acc);
+    __syncthreads();
+    // unblocked Cholesky of S (upper)
+    for (int j = 0; j < nJ; ++j) {
+      if (tid == 0) {
+        double p = S[j][j];
+        if (!(p > 1e-12 * diag0[j])) {
+          s_bad = 1;
+          p = 1.0;
+        }
+        S[j][j] = sqrt(p);
+      }
+      __syncthreads();
+      const double rjj = S[j][j];
+      for (int l = j + 1 + tid; l < nJ; l += kCB) S[j][l] /= rjj;
+      __syncthreads();
+      const int m = nJ - j - 1;
+      for (int e = tid; e < m * m; e += kCB) {
+        const int i = j + 1 + e / m, l = j + 1 + e % m;
+        if (l >= i) S[i][l] = fma(-S[j][i], S[j][l], S[i][l]);
+      }
+      __syncthreads();
+    }
+    // Di = R_JJ^-1 (upper), column by column
+    for (int e = tid; e < kNb * kNb; e += kCB) {
+      const int r = e / kNb, c = e % kNb;
+      if (r > c || c >= nJ) S[r][c] = (r == c && c >= nJ) ? 1.0 : (r > c ? 0.0 : S[r][c]);
+      Di[r][c] = 0.0;
+    }
+    __syncthreads();
+    for (int j = 0; j < kNb; ++j) {
+      const double rjj = S[j][j];
+      for (int i = tid; i <= j; i += kCB) {
+        double x;
+        if (i == j) {
+          x = 1.0 / rjj;
+        } else {
+          double sm = 0.0;
+          for (int l = i; l < j; ++l) sm = fma(Di[i][l], S[l][j], sm);
+          x = -sm / rjj;
+        }
+        Di[i][j] = x;
+      }
+      __syncthreads();
+    }
+    // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
+    for (int e = tid; e < kNb * kNb; e += kCB) {
+      const int r = e / kNb, c = e % kNb;
+      if (r < nJ && c < nJ) R[(size_t)(c0 + r) * k + c0 + c] = S[r][c];
+      Dinv[(size_t)J * kNb * kNb + e] = (r < nJ && c < nJ) ? Di[r][c] : 0.0;
+    }
+    // the block row J right of the diagonal
+    for (int L = J + 1; L < nbk; ++L) {
+      const int l0 = L * kNb, nL = min(kNb, k - l0);
+      __syncthreads();
+      load_tile(S, G, k, c0, l0, nJ, nL);
+      __syncthreads();
+      acc_from_tile(acc, S);
+      for (int I = 0; I < J; ++I) {
+        __syncthreads();
+        load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
+        load_tile(Tb, R, k, I * kNb, l0, kNb, nL);
+        __syncthreads();
+        sub_atb(acc, Ta, Tb);
+      }
+      __syncthreads();
+      acc_to_tile(S, acc);
+      __syncthreads();
+      // R_JL = Di^T S: out[r][c] = sum_{i <= r} Di[i][r] S[i][c]
+      double out[4][4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
+      for (int i = 0; i < kNb; ++i) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) out[x][y] = fma(Di[i][ti + x], S[i][tj + y], out[x][y]);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          if (ti + x < nJ && tj + y < nL) R[(size_t)(c0 + ti + x) * k + l0 + tj + y] = out[x][y];
+    }
+    // R's block row J is read back by later block rows: its stores land first
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();
-  for (int j = 0; j < k; ++j) {
-    // column j of R above the diagonal is final: stage it
-    for (int i = tid; i < j; i += kCB) colj[i] = G[(size_t)i * k + j];
-    __syncthreads();
-    if (tid == 0) {
-      const double gjj = G[(size_t)j * k + j];
-      double dsum = gjj;
-      for (int i = 0; i < j; ++i) dsum -= colj[i] * colj[i];
-      if (!(dsum > 1e-12 * gjj)) {
-        s_bad = 1;
-        dsum = 1.0;
-      }
-      G[(size_t)j * k + j] = sqrt(dsum);
-    }
-    __syncthreads();
-    const double rjj = G[(size_t)j * k + j];
-    for (int l = j + 1 + tid; l < k; l += kCB) {
-      double s = G[(size_t)j * k + l];
-      for (int i = 0; i < j; ++i) s -= colj[i] * G[(size_t)i * k + l];
-      G[(size_t)j * k + l] = s / rjj;
-    }
-    __syncthreads();
-  }
-  // R^-1, column by column: X[j][j] = 1/R[j][j], X[i][j] = -(sum_{i<=l<j} X[i][l] R[l][j]) / R[j][j]
-  for (int j = 0; j < k; ++j) {
-    const double rjj = G[(size_t)j * k + j];
-    for (int i = tid; i < k; i += kCB) {
-      double x = 0.0;
-      if (i == j) {
-        x = 1.0 / rjj;
-      } else if (i < j) {
-        double s = 0.0;
-        for (int l = i; l < j; ++l) s += Rinv[(size_t)i * k + l] * G[(size_t)l * k + j];
-        x = -s / rjj;
-      }
-      Rinv[(size_t)i * k + j] = x;
-    }
-    __syncthreads();
-  }
   if (tid == 0 && s_bad) *status = 1u;
+}
+
+// Q = Y R^-1 ([d][k]) by a blocked forward substitution over the block
+// columns: Q_J = (Y_J - sum_{I<J} Q_I R_IJ) R_JJ^-1.  Rows are independent:
+// one workgroup per 64 rows, which reads back the Q blocks it wrote.
+__global__ void __launch_bounds__(kCB) trsm_kernel(const double *Y, const double *R, const double *Dinv,
+                                                   double *Q, int d, int k) {
+  __shared__ double Ta[kNb][kLd], Tb[kNb][kLd];
+  const int ti = tile_ti(), tj = tile_tj();
+  const int r0 = blockIdx.x * kNb, nr = min(kNb, d - r0);
+  const int nbk = (k + kNb - 1) / kNb;
+  for (int J = 0; J < nbk; ++J) {
+    const int c0 = J * kNb, nJ = min(kNb, k - c0);
+    __syncthreads();
+    load_tile(Ta, Y, k, r0, c0, nr, nJ);
+    __syncthreads();
+    double acc[4][4];
+    acc_from_tile(acc, Ta);
+    for (int I = 0; I < J; ++I) {
+      __syncthreads();
+      load_tile(Ta, Q, k, r0, I * kNb, nr, kNb);
+      load_tile(Tb, R, k, I * kNb, c0, kNb, nJ);
+      __syncthreads();
+      sub_ab(acc, Ta, Tb);
+    }
+    __syncthreads();
+    acc_to_tile(Ta, acc);
+    load_tile(Tb, Dinv + (size_t)J * kNb * kNb, kNb, 0, 0, kNb, kNb);
+    __syncthreads();
+    double out[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
+    for (int i = 0; i < kNb; ++i) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) out[x][y] = fma(Ta[ti + x][i], Tb[i][tj + y], out[x][y]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        if (ti + x < nr && tj + y < nJ) Q[(size_t)(r0 + ti + x) * k + c0 + tj + y] = out[x][y];
+    // this block column of Q is read back for the next ones
+    __builtin_amdgcn_s_waitcnt(0);
+  }
 }
 
 template <typename TI, typename TO>
@@ -175,11 +363,11 @@ void convert(const TI *in, TO *out, size_t n, hipStream_t s) {
 }
 
 // Q <- the Q factor of Y ([d][k] fp64), one CholeskyQR pass.
-void cholqr_pass(const double *Y, double *Q, double *G, double *Rinv, int d, int k, uint32_t *status,
-                 hipStream_t s) {
-  gemm<double, double, double, double, true>(Y, Y, G, k, k, d, s);     // G = Y^T Y
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kCB), 0, s, G, Rinv, k, status);
-  gemm<double, double, double, double, false>(Y, Rinv, Q, d, k, k, s);  // Q = Y R^-1
+void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv, int d, int k,
+                 uint32_t *status, hipStream_t s) {
+  gemm<double, double, double, double, true>(Y, Y, G, k, k, d, s);  // G = Y^T Y
+  hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, status);
+  hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
 
 template <typename T>
@@ -189,8 +377,8 @@ hipError_t run(const CalibArgs &c, hipStream_t s) {
   for (int it = 0; it < c.iters; ++it) {
     gemm<T, float, float, float, false>(A, c.vw, c.z, c.n, c.k, c.d, s);    // Z = A V      [n][k]
     gemm<T, float, double, float, true>(A, c.z, c.y, c.d, c.k, c.n, s);     // Y = A^T Z    [d][k]
-    cholqr_pass(c.y, c.y2, c.g, c.rinv, c.d, c.k, c.status, s);  // y2 = Q(y)
-    cholqr_pass(c.y2, c.y, c.g, c.rinv, c.d, c.k, c.status, s);  // y = Q(y2): orthogonal to rounding
+    cholqr_pass(c.y, c.y2, c.g, c.r, c.dinv, c.d, c.k, c.status, s);  // y2 = Q(y)
+    cholqr_pass(c.y2, c.y, c.g, c.r, c.dinv, c.d, c.k, c.status, s);  // y = Q(y2): orthogonal to rounding
     if (it + 1 < c.iters) convert(c.y, c.vw, (size_t)c.d * c.k, s);
   }
   if (c.iters == 0)
