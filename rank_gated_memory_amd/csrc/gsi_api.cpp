@@ -721,6 +721,8 @@ gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *st
   a.r = reinterpret_cast<double *>(w + off);
   off += al(kk * 8);
   a.dinv = reinterpret_cast<double *>(w + off);
+  off += al((uint64_t)(c->k + 63) / 64 * 64 * 64 * 8);
+  a.gpart = reinterpret_cast<double *>(w + off);
   const hipError_t e = launch_calibrate(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }

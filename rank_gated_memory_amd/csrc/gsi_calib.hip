@@ -102,12 +102,44 @@ __global__ void __launch_bounds__(kCB) gemm_kernel(const TX *__restrict__ X, con
 constexpr int kNb = 64;
 constexpr int kLd = kNb + 1;
 
+
+
 // dst[r][c] = M[(r0 + r) * ld + c0 + c] for r < nr, c < nc, zero elsewhere.
+// Every load of the tile is issued before the first LDS store.
+constexpr int kTileLoads = kNb * kNb / kCB;
 __device__ __forceinline__ void load_tile(double (*dst)[kLd], const double *M, size_t ld, int r0, int c0,
                                           int nr, int nc) {
-  for (int e = threadIdx.x; e < kNb * kNb; e += kCB) {
+  double v[kTileLoads];
+#pragma unroll
+  for (int q = 0; q < kTileLoads; ++q) {
+    const int e = threadIdx.x + q * kCB;
     const int r = e / kNb, c = e % kNb;
-    dst[r][c] = (r < nr && c < nc) ? M[(size_t)(r0 + r) * ld + c0 + c] : 0.0;
+    v[q] = (r < nr && c < nc) ? M[(size_t)(r0 + r) * ld + c0 + c] : 0.0;
+  }
+#pragma unroll
+  for (int q = 0; q < kTileLoads; ++q) {
+    const int e = threadIdx.x + q * kCB;
+    dst[e / kNb][e % kNb] = v[q];
+  }
+}
+
+// Two tiles at once (all 32 loads in flight).
+__device__ __forceinline__ void load_tiles2(double (*da)[kLd], const double *Ma, size_t lda, int ra, int ca,
+                                            int nra, int nca, double (*db)[kLd], const double *Mb, size_t ldb,
+                                            int rb, int cb, int nrb, int ncb) {
+  double va[kTileLoads], vb[kTileLoads];
+#pragma unroll
+  for (int q = 0; q < kTileLoads; ++q) {
+    const int e = threadIdx.x + q * kCB;
+    const int r = e / kNb, c = e % kNb;
+    va[q] = (r < nra && c < nca) ? Ma[(size_t)(ra + r) * lda + ca + c] : 0.0;
+    vb[q] = (r < nrb && c < ncb) ? Mb[(size_t)(rb + r) * ldb + cb + c] : 0.0;
+  }
+#pragma unroll
+  for (int q = 0; q < kTileLoads; ++q) {
+    const int e = threadIdx.x + q * kCB;
+    da[e / kNb][e % kNb] = va[q];
+    db[e / kNb][e % kNb] = vb[q];
   }
 }
 
@@ -213,35 +245,47 @@ __global__ void __launch_bounds__(kCB) chol_kernel(const double *G, double *R, d
       const double rjj = S[j][j];
       for (int l = j + 1 + tid; l < nJ; l += kCB) S[j][l] /= rjj;
       __syncthreads();
-      const int m = nJ - j - 1;
-      for (int e = tid; e < m * m; e += kCB) {
-        const int i = j + 1 + e / m, l = j + 1 + e % m;
-        if (l >= i) S[i][l] = fma(-S[j][i], S[j][l], S[i][l]);
+      // trailing update of the upper part: thread (a, b) takes rows j+1+a,
+      // j+1+a+16, ... and columns j+1+b, j+1+b+16, ...
+      const int a0 = tid >> 4, b0 = tid & 15;
+      for (int i = j + 1 + a0; i < nJ; i += 16) {
+        const double sji = S[j][i];
+        for (int l = j + 1 + b0; l < nJ; l += 16)
+          if (l >= i) S[i][l] = fma(-sji, S[j][l], S[i][l]);
       }
       __syncthreads();
     }
-    // Di = R_JJ^-1 (upper), column by column
+    // strictly lower part and the padding of a partial block: zero, with an
+    // identity diagonal so that the inverse is defined
     for (int e = tid; e < kNb * kNb; e += kCB) {
       const int r = e / kNb, c = e % kNb;
-      if (r > c || c >= nJ) S[r][c] = (r == c && c >= nJ) ? 1.0 : (r > c ? 0.0 : S[r][c]);
-      Di[r][c] = 0.0;
+      if (r > c || c >= nJ) S[r][c] = (r == c) ? 1.0 : 0.0;
     }
     __syncthreads();
-    for (int j = 0; j < kNb; ++j) {
-      const double rjj = S[j][j];
-      for (int i = tid; i <= j; i += kCB) {
-        double x;
-        if (i == j) {
-          x = 1.0 / rjj;
-        } else {
-          double sm = 0.0;
-          for (int l = i; l < j; ++l) sm = fma(Di[i][l], S[l][j], sm);
-          x = -sm / rjj;
+    // Di = S^-1 (upper): row i on thread i (rows are independent), read S only
+    if (tid < kNb) {
+      const int i = tid;
+      for (int j = 0; j < kNb; ++j) {
+        double x = 0.0;
+        if (j == i) {
+          x = 1.0 / S[j][j];
+        } else if (j > i) {
+          // four partial sums: the loads run ahead of the dependent adds
+          double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+          int l = i;
+          for (; l + 4 <= j; l += 4) {
+            s0 = fma(Di[i][l], S[l][j], s0);
+            s1 = fma(Di[i][l + 1], S[l + 1][j], s1);
+            s2 = fma(Di[i][l + 2], S[l + 2][j], s2);
+            s3 = fma(Di[i][l + 3], S[l + 3][j], s3);
+          }
+          for (; l < j; ++l) s0 = fma(Di[i][l], S[l][j], s0);
+          x = -((s0 + s1) + (s2 + s3)) / S[j][j];
         }
         Di[i][j] = x;
       }
-      __syncthreads();
     }
+    __syncthreads();
     // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
     for (int e = tid; e < kNb * kNb; e += kCB) {
       const int r = e / kNb, c = e % kNb;
@@ -257,8 +301,7 @@ __global__ void __launch_bounds__(kCB) chol_kernel(const double *G, double *R, d
       acc_from_tile(acc, S);
       for (int I = 0; I < J; ++I) {
         __syncthreads();
-        load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
-        load_tile(Tb, R, k, I * kNb, l0, kNb, nL);
+        load_tiles2(Ta, R, k, I * kNb, c0, kNb, nJ, Tb, R, k, I * kNb, l0, kNb, nL);
         __syncthreads();
         sub_atb(acc, Ta, Tb);
       }
@@ -308,8 +351,7 @@ __global__ void __launch_bounds__(kCB) trsm_kernel(const double *Y, const double
     acc_from_tile(acc, Ta);
     for (int I = 0; I < J; ++I) {
       __syncthreads();
-      load_tile(Ta, Q, k, r0, I * kNb, nr, kNb);
-      load_tile(Tb, R, k, I * kNb, c0, kNb, nJ);
+      load_tiles2(Ta, Q, k, r0, I * kNb, nr, kNb, Tb, R, k, I * kNb, c0, kNb, nJ);
       __syncthreads();
       sub_ab(acc, Ta, Tb);
     }
@@ -338,6 +380,75 @@ __global__ void __launch_bounds__(kCB) trsm_kernel(const double *Y, const double
   }
 }
 
+// Split partials of G = Y^T Y (fp64, [d][k]): workgroup (tile, range) sums
+// the 64 x 64 upper-triangle tile `tile` (bi <= bj) over rows
+// [range * chunk, (range + 1) * chunk) of Y into P[range].
+__global__ void __launch_bounds__(kCB) gram_split_kernel(const double *__restrict__ Y, double *__restrict__ P,
+                                                         int d, int k, int chunk) {
+  constexpr int KC = 32;
+  __shared__ double Xs[KC][64 + 1];
+  __shared__ double Ys[KC][64 + 1];
+  const int t = (k + 63) / 64;
+  int b = blockIdx.x, bi = 0;
+  while (b >= t - bi) {
+    b -= t - bi;
+    ++bi;
+  }
+  const int i0 = bi * 64, j0 = (bi + b) * 64;
+  const int r0 = blockIdx.y * chunk, r1 = min(d, r0 + chunk);
+  const int tid = threadIdx.x;
+  const int ti = (tid >> 4) * 4, tj = (tid & 15) * 4;
+  double acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int t0 = r0; t0 < r1; t0 += KC) {
+    for (int e = tid; e < KC * 64; e += kCB) {
+      const int r = e / 64, c = e % 64;
+      const bool ok = t0 + r < r1;
+      Xs[r][c] = (ok && i0 + c < k) ? Y[(size_t)(t0 + r) * k + i0 + c] : 0.0;
+      Ys[r][c] = (ok && j0 + c < k) ? Y[(size_t)(t0 + r) * k + j0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < KC; ++r) {
+      double xv[4], yv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) xv[x] = Xs[r][ti + x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) yv[y] = Ys[r][tj + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(xv[x], yv[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+  double *Pr = P + (size_t)blockIdx.y * k * k;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int i = i0 + ti + x, j = j0 + tj + y;
+      if (i < k && j < k) Pr[(size_t)i * k + j] = acc[x][y];
+    }
+}
+
+// G = sum of the S partials in range order, on the upper-triangle tiles
+// (the only part of G the factorisation reads).
+__global__ void __launch_bounds__(kCB) gram_reduce_kernel(const double *__restrict__ P, double *__restrict__ G,
+                                                          int k, int S) {
+  const size_t kk = (size_t)k * k;
+  for (size_t e = (size_t)blockIdx.x * kCB + threadIdx.x; e < kk; e += (size_t)gridDim.x * kCB) {
+    const int i = (int)(e / k), j = (int)(e % k);
+    if (i / 64 > j / 64) continue;
+    double s = 0.0;
+    for (int r = 0; r < S; ++r) s += P[(size_t)r * kk + e];
+    G[e] = s;
+  }
+}
+
 template <typename TI, typename TO>
 __global__ void __launch_bounds__(kCB) convert_kernel(const TI *in, TO *out, size_t n) {
   for (size_t i = (size_t)blockIdx.x * kCB + threadIdx.x; i < n; i += (size_t)gridDim.x * kCB) {
@@ -363,9 +474,16 @@ void convert(const TI *in, TO *out, size_t n, hipStream_t s) {
 }
 
 // Q <- the Q factor of Y ([d][k] fp64), one CholeskyQR pass.
-void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv, int d, int k,
+void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv, double *P, int d, int k,
                  uint32_t *status, hipStream_t s) {
-  gemm<double, double, double, double, true>(Y, Y, G, k, k, d, s);  // G = Y^T Y
+  // G = Y^T Y: split partials, then their sum
+  const int S = calib_gram_splits(d, k);
+  const int chunk = (d + S - 1) / S;
+  const int t = (k + 63) / 64;
+  hipLaunchKernelGGL(gram_split_kernel, dim3(t * (t + 1) / 2, S), dim3(kCB), 0, s, Y, P, d, k, chunk);
+  int rb = (int)(((size_t)k * k + kCB - 1) / kCB);
+  if (rb > 2048) rb = 2048;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(rb), dim3(kCB), 0, s, P, G, k, S);
   hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, status);
   hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
@@ -377,8 +495,8 @@ hipError_t run(const CalibArgs &c, hipStream_t s) {
   for (int it = 0; it < c.iters; ++it) {
     gemm<T, float, float, float, false>(A, c.vw, c.z, c.n, c.k, c.d, s);    // Z = A V      [n][k]
     gemm<T, float, double, float, true>(A, c.z, c.y, c.d, c.k, c.n, s);     // Y = A^T Z    [d][k]
-    cholqr_pass(c.y, c.y2, c.g, c.r, c.dinv, c.d, c.k, c.status, s);  // y2 = Q(y)
-    cholqr_pass(c.y2, c.y, c.g, c.r, c.dinv, c.d, c.k, c.status, s);  // y = Q(y2): orthogonal to rounding
+    cholqr_pass(c.y, c.y2, c.g, c.r, c.dinv, c.gpart, c.d, c.k, c.status, s);  // y2 = Q(y)
+    cholqr_pass(c.y2, c.y, c.g, c.r, c.dinv, c.gpart, c.d, c.k, c.status, s);  // y = Q(y2): orthogonal to rounding
     if (it + 1 < c.iters) convert(c.y, c.vw, (size_t)c.d * c.k, s);
   }
   if (c.iters == 0)
