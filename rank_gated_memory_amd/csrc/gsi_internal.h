@@ -97,11 +97,13 @@ constexpr int kCtlWave0 = 96;       // per wave: kCtlWaveWords words, then the o
 // group of workgroups (blockIdx % kGroups), each on its own line: one
 // address taking every workgroup's atomics serialises them (~13 ns each).
 constexpr int kGroups = 8;
-constexpr int kCtlWaveWords = (3 * kGroups + 1) * 32;
+constexpr int kCtlWaveWords = (4 * kGroups + 2) * 32;
 constexpr int kWvProj = 0;               // + 32 g: projection tickets taken by group g
 constexpr int kWvOut = 32 * kGroups;     // + 32 g: output tickets taken by group g
-constexpr int kWvDone = 64 * kGroups;    // + 32 g: output units finished by group g
-constexpr int kWvOpen = 96 * kGroups;    // open word (64-bit): calls open << 40 | their output units
+constexpr int kWvLeft = 64 * kGroups;    // + 32 g: workgroups of group g that have left the wave
+constexpr int kWvReady = 96 * kGroups;   // + 32 g: 1 once every workgroup has left (a copy per group)
+constexpr int kWvOpen = 128 * kGroups;   // open word (64-bit): calls open << 40 | their output units
+constexpr int kWvGroups = 128 * kGroups + 32;  // groups whose workgroups have all left
 // After the wave blocks: the open list, one 64-bit entry per call, indexed by
 // the wave's first a_order slot plus the order in which the call's gate
 // opened: base | need << 32 | slow << 50 | (call + 1) << 51, where base is

@@ -731,7 +731,6 @@ struct Sched {
   int last_out;   // the last job was an output unit
   int pf;         // ticket to fetch while the job runs: 1 projection, 2 output
   int slot;       // first open-list slot that may hold the output ticket
-  int done;       // output units of wave w finished by this workgroup, not yet reported
   uint32_t tp;    // projection ticket held
   uint32_t to;    // output ticket held
   uint64_t open;  // last open word seen for wave w
@@ -792,19 +791,16 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
     uint32_t *wv = wave_ctl(a, w);
     if (!st.entered) {
       if (w > 0) {
-        // x of this wave may be y of the previous one: wait for its outputs
-        // (every unit of that wave is held by a running workgroup).
+        // x of this wave may be y of the previous one: wait until every
+        // workgroup has left that wave (each leaves once the wave has no
+        // ticket for it, after its outputs landed; every unit of the wave is
+        // held by a running workgroup).  The last one out raises a ready
+        // flag on each group's own line, so that the pollers of one line
+        // are a group, not the grid.
         const uint32_t *pv = wave_ctl(a, w - 1);
-        const uint32_t pcalls = (uint32_t)(a.wave_tab[a.n_waves + 1 + w] - a.wave_tab[a.n_waves + w]);
         for (int s = 0;; ++s) {
           uint32_t ok = 0;
-          if (lane == 0) {
-            const uint64_t ow = ctl_load64(reinterpret_cast<const uint64_t *>(pv + kWvOpen));
-            uint32_t fin = 0;
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g) fin += ctl_load(pv + kWvDone + 32 * g);
-            ok = (ow >> 40) == pcalls && fin == (uint32_t)(ow & kLow40);
-          }
+          if (lane == 0) ok = ctl_load(pv + kWvReady + 32 * (blockIdx.x % kGroups));
           if (bcast(ok)) break;
           if (s >= a.spin_limit) return sched_fail(a, 1, job);
           __builtin_amdgcn_s_sleep(8);
@@ -836,7 +832,8 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
     const uint32_t to = bcast(st.to);
     const int q0 = a.wave_tab[a.n_waves + 1 + w];
     const uint32_t ncalls = (uint32_t)(a.wave_tab[a.n_waves + 2 + w] - q0);
-    if (to >= (uint32_t)(st.open & kLow40)) st.open = load_open(a, w);
+    // (once every gate of the wave is open the cached open word is final)
+    if (to >= (uint32_t)(st.open & kLow40) && (uint32_t)(st.open >> 40) != ncalls) st.open = load_open(a, w);
     if (to < (uint32_t)(st.open & kLow40)) {
       // ---- output unit: find the open call that covers ticket `to` ----
       const int nopen = (int)(st.open >> 40);
@@ -896,11 +893,21 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
       st.p_out = 1;
     }
     if ((uint32_t)(st.open >> 40) == ncalls) {  // every gate open and `to` beyond the last unit
-      // the outputs this workgroup wrote in the wave have landed (each
-      // output unit of a wave with a successor ends with s_waitcnt 0 and a
-      // barrier): count them for the next wave's entry
-      if (lane == 0 && st.done) ctl_add(wv + kWvDone + 32 * (blockIdx.x % kGroups), (uint32_t)st.done);
-      st.done = 0;
+      // Leave the wave.  The outputs this workgroup wrote in it have landed
+      // (each output unit of a wave with a successor ends with s_waitcnt 0
+      // and a barrier).  The last workgroup of its group to leave counts the
+      // group; the last group raises the ready flags of the next wave's entry.
+      if (lane == 0 && w + 1 < a.n_waves) {
+        const uint32_t g = blockIdx.x % kGroups;
+        const uint32_t gsize = (gridDim.x - g + kGroups - 1) / kGroups;
+        if (ctl_add(wv + kWvLeft + 32 * g, 1u) == gsize - 1) {
+          const uint32_t ngroups = gridDim.x < (uint32_t)kGroups ? gridDim.x : (uint32_t)kGroups;
+          if (ctl_add(wv + kWvGroups, 1u) == ngroups - 1) {
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) ctl_store(wv + kWvReady + 32 * q, 1u);
+          }
+        }
+      }
       st.w += 1;
       st.entered = 0;
       continue;
@@ -948,7 +955,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
   int cur = -1, cur_slow = 0;
   for (;;) {
     if (tid < 64) next_job(a, st, s_job);
@@ -1019,11 +1026,10 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
       else
         fast_unit<T, UNROLL>(cd, u, gs, scr);
       if (cd.wave + 1 < a.n_waves) {
-        // a later wave may read this y: the unit counts once its stores
-        // landed (reported when the workgroup leaves the wave)
+        // a later wave may read this y: its stores land before the
+        // workgroup can leave the wave
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        st.done += 1;
       }
     }
   }

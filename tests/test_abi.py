@@ -236,7 +236,7 @@ def test_stack_plan_waves():
     for i in range(8):
         assert list(unit_call[desc["a_begin"][i]:desc["a_begin"][i] + desc["a_units"][i]]) == [i] * desc["a_units"][i]
     # control words: header, one block per wave, one open-list entry per call
-    assert h["ctl_words"] == 96 + 800 * 4 + 2 * 8
+    assert h["ctl_words"] == 96 + 1088 * 4 + 2 * 8
     assert h["ws_ctl_off"] + 4 * h["ctl_words"] <= h["ws_bytes"]
     assert gsi.lib().gsi_stack_status_offset(plan.ctypes.data) == h["ws_ctl_off"]
 
