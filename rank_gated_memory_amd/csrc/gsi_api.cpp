@@ -89,25 +89,31 @@ int64_t proj_target_bytes(int64_t total_v_bytes) {
 }
 
 struct WsLayout {
-  uint64_t gate_off, need_off, pref_off, float_off, ctl_off, total;
+  uint64_t gate_off, need_off, pref_off, float_off, ctl_off, gcnt_off, total;
 };
 
-// ctl: control words of the single-launch stack kernel (0 for gsi_linear)
-WsLayout ws_layout(int64_t n, int64_t floats, int64_t ctl = 0) {
+// The group counters of two-level partial sums follow the control words.
+uint64_t gcnt_offset(uint64_t ctl_off, int64_t ctl) { return align_up(ctl_off + (uint64_t)ctl * 4, 256); }
+
+// ctl: control words of the single-launch stack kernel (0 for gsi_linear);
+// units_a: projection units (at most one group counter each)
+WsLayout ws_layout(int64_t n, int64_t floats, int64_t ctl, int64_t units_a) {
   WsLayout w;
   w.gate_off = align_up((uint64_t)(n + 1) * 4, 256);
   w.need_off = align_up(w.gate_off + (uint64_t)n * 16, 256);
   w.pref_off = align_up(w.need_off + (uint64_t)n * 4, 256);
   w.float_off = align_up(w.pref_off + (uint64_t)(n + 1) * 4, 256);
   w.ctl_off = align_up(w.float_off + (uint64_t)floats * 4, 256);
-  w.total = align_up(w.ctl_off + (uint64_t)ctl * 4, 256);
+  w.gcnt_off = gcnt_offset(w.ctl_off, ctl);
+  w.total = align_up(w.gcnt_off + (uint64_t)units_a * 4, 256);
   return w;
 }
 
 void set_ws(KArgs &a, void *ws, uint64_t gate_off, uint64_t need_off, uint64_t pref_off,
-            uint64_t float_off) {
+            uint64_t float_off, uint64_t gcnt_off) {
   char *b = static_cast<char *>(ws);
   a.counters = reinterpret_cast<uint32_t *>(b);
+  a.gcounters = reinterpret_cast<uint32_t *>(b + gcnt_off);
   a.gate = b + gate_off;
   a.need = reinterpret_cast<int32_t *>(b + need_off);
   a.pref = reinterpret_cast<int32_t *>(b + pref_off);
@@ -167,7 +173,7 @@ static uint64_t linear_ws_bytes(const gsi_map *map, int64_t n) {
   const int es = esize_of(map->dtype);
   const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
                                   proj_target_bytes((int64_t)map->d * map->k * es * n));
-  return ws_layout(n, n * (us.g_floats + us.part_floats)).total;
+  return ws_layout(n, n * (us.g_floats + us.part_floats), 0, n * us.a_units).total;
 }
 
 // bf16 maps with two or more tokens take the batched MFMA path; fp32 maps
@@ -254,7 +260,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     const int32_t n = (T - t0) < kMaxCalls ? (T - t0) : kMaxCalls;
     const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
                                     proj_target_bytes((int64_t)map->d * map->k * es * n));
-    const WsLayout wl = ws_layout(n, n * (us.g_floats + us.part_floats));
+    const WsLayout wl = ws_layout(n, n * (us.g_floats + us.part_floats), 0, n * us.a_units);
     KArgs a{};
     a.table = nullptr;
     a.unit_call = nullptr;
@@ -278,6 +284,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     o.fast_tiles = us.fast_tiles;
     o.slow_units = us.slow_units;
     o.slow_rows = us.slow_rows;
+    o.groups = us.groups;
     o.g_off = 0;
     o.part_off = (int64_t)n * us.g_floats;
     o.gate_off = 0;
@@ -288,7 +295,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
     a.mode = mode;
     a.max_k = map->k;
     a.max_d = map->d;
-    set_ws(a, ws, wl.gate_off, wl.need_off, wl.pref_off, wl.float_off);
+    set_ws(a, ws, wl.gate_off, wl.need_off, wl.pref_off, wl.float_off, wl.gcnt_off);
     const int64_t ub = (int64_t)n * (us.fast_units > us.slow_units ? us.fast_units : us.slow_units);
     const hipError_t e = launch_batch1(map->dtype, a, apply_grid(ub), 3, st);
     if (e != hipSuccess) return GSI_E_HIP;
@@ -363,6 +370,8 @@ constexpr int64_t kFineUnits = 1024;
 #define GSI_PLAN_MAX_PARTIALS 64
 #endif
 constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
+constexpr int64_t kTwoLevelUnitBytes = 64 * 1024;
+constexpr int64_t kMaxPartials2 = 256;
 
 // For each call, the earlier call of the same wave whose projection it
 // shares (same x, V_k, E, d and k: g, ||x|| and rho are then the same), or -1.
@@ -396,10 +405,17 @@ static std::vector<UnitShape> call_shapes(const gsi_call *calls, int32_t n, int 
     const bool fine = fast_units < kFineUnits;
     for (int32_t i = b; i < e; ++i) {
       const int64_t vi = (int64_t)calls[i].map.d * calls[i].map.k * es;
-      const int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
+      int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
+      // Where the cap of kMaxPartials one-level partials would make the
+      // units larger than the wave's target and than kTwoLevelUnitBytes
+      // (a wide V_k in a latency-bound wave), up to kMaxPartials2 smaller
+      // units are summed in two levels instead.
+      if (ti > t && ti > kTwoLevelUnitBytes)
+        ti = std::max<int64_t>({t, kTwoLevelUnitBytes, (vi + kMaxPartials2 - 1) / kMaxPartials2});
       shapes[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, ti, fine);
       if (owner[i] >= 0) {  // projected by its owner
         shapes[i].a_units = 0;
+        shapes[i].groups = 1;
         shapes[i].part_floats = 0;
       }
     }
@@ -526,6 +542,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     o.fast_tiles = us.fast_tiles;
     o.slow_units = us.slow_units;
     o.slow_rows = us.slow_rows;
+    o.groups = us.groups;
     o.g_off = owner[i] < 0 ? g_off : desc[owner[i]].g_off;
     o.part_off = part_off;
     o.gate_off = i;
@@ -568,7 +585,7 @@ gsi_status gsi_stack_plan(const gsi_call *calls, int32_t n, void *plan, size_t p
     wave_tab[n_waves + 1 + w] = i;                               // first output slot
   }
   h->ctl_words = (int32_t)ctl_words(n, n_waves);
-  const WsLayout wl = ws_layout(n, part_off, h->ctl_words);
+  const WsLayout wl = ws_layout(n, part_off, h->ctl_words, h->units_a);
   h->ws_bytes = n > 0 ? wl.total : 0;
   h->ws_gate_off = wl.gate_off;
   h->ws_need_off = wl.need_off;
@@ -632,6 +649,7 @@ gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, 
   a.ctl = reinterpret_cast<uint32_t *>(w + h->ws_ctl_off);
   a.entries = reinterpret_cast<uint64_t *>(a.ctl + kCtlWave0 + kCtlWaveWords * h->n_waves);
   a.counters = reinterpret_cast<uint32_t *>(w);
+  a.gcounters = reinterpret_cast<uint32_t *>(w + gcnt_offset(h->ws_ctl_off, h->ctl_words));
   a.gate = w + h->ws_gate_off;
   a.wsf = reinterpret_cast<float *>(w + h->ws_float_off);
   a.n = h->n;
@@ -661,7 +679,8 @@ gsi_status gsi_stack_phase(const void *plan_host, const void *plan_dev, int32_t 
   a.mode = mode;
   a.max_k = h->max_k;
   a.max_d = h->max_d;
-  set_ws(a, ws, h->ws_gate_off, h->ws_need_off, h->ws_pref_off, h->ws_float_off);
+  set_ws(a, ws, h->ws_gate_off, h->ws_need_off, h->ws_pref_off, h->ws_float_off,
+         gcnt_offset(h->ws_ctl_off, h->ctl_words));
   const hipError_t e = launch_batch1(h->dtype, a, apply_grid(h->units_b), phase,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;

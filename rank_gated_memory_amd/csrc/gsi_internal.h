@@ -47,7 +47,7 @@ struct alignas(16) CallDesc {
   // last projection unit.  share_next = 1 + the next call of the group
   // (0: none), so a zero-filled descriptor shares nothing.
   int32_t share_next;
-  int32_t pad_;
+  int32_t groups;      // partial groups (1: the last unit sums all partials; see kGroupUnits)
   const void *G;       // E = V_k^T V_k - I [k][k] (exact rho), or null (norm form)
 };
 static_assert(sizeof(CallDesc) == 144, "CallDesc layout");
@@ -143,6 +143,7 @@ struct KArgs {
   int32_t max_d;
   int32_t pad_;
   uint32_t *counters;
+  uint32_t *gcounters;  // group counters of two-level partial sums (index a_begin + group)
   void *gate;   // float4 records
   int32_t *need;
   int32_t *pref;
@@ -162,6 +163,7 @@ struct FArgs {
   uint32_t *ctl;             // control words (kCtl*)
   uint64_t *entries;         // open lists: ctl + kCtlWave0 + kCtlWaveWords * n_waves
   uint32_t *counters;        // per-call projection counters
+  uint32_t *gcounters;       // group counters of two-level partial sums (index a_begin + group)
   void *gate;                // float4 records
   float *wsf;
   int32_t n;
@@ -172,10 +174,18 @@ struct FArgs {
   int32_t pad_;
 };
 
+// A call with more than kGroupUnits2 projection units sums its partials in
+// two levels: the last unit of each group of kGroupUnits sums the group into
+// a group partial (stored after the unit partials), and the last group to
+// finish sums the group partials.  One workgroup then never sums more than
+// 64 rows, so a wide V_k can be split into many small units.
+constexpr int kGroupUnits = 16;
+constexpr int kGroupUnits2 = 64;
+
 // Unit sizing shared by the stack plan and the single-map path.
 struct UnitShape {
-  int32_t a_units, a_rows, fast_units, fast_tiles, slow_units, slow_rows;
-  int64_t part_floats;  // a_units * (k + 4)
+  int32_t a_units, a_rows, fast_units, fast_tiles, slow_units, slow_rows, groups;
+  int64_t part_floats;  // (a_units + group partials) * (k + 4)
   int64_t g_floats;     // k rounded up to a multiple of 4
 };
 
@@ -221,7 +231,8 @@ inline UnitShape unit_shape(int d, int d_out, int k, int esize, int64_t target_p
   if (srows > 256) srows = 256;
   s.slow_rows = (int32_t)srows;
   s.slow_units = (int32_t)((d_out + srows - 1) / srows);
-  s.part_floats = (int64_t)s.a_units * (k + 4);
+  s.groups = s.a_units > kGroupUnits2 ? (s.a_units + kGroupUnits - 1) / kGroupUnits : 1;
+  s.part_floats = (int64_t)(s.a_units + (s.groups > 1 ? s.groups : 0)) * (k + 4);
   s.g_floats = (k + 3) / 4 * 4;
   return s;
 }

@@ -187,7 +187,8 @@ __device__ __forceinline__ CallDesc load_call(const KArgs &a, int c) {
   if (d.rho) d.rho += c;
   if (d.slow) d.slow += c;
   d.a_begin = c * a.one.a_units;
-  d.part_off = a.one.part_off + (int64_t)c * ((int64_t)a.one.a_units * (a.one.k + 4));
+  d.part_off = a.one.part_off +
+               (int64_t)c * ((int64_t)(a.one.a_units + (a.one.groups > 1 ? a.one.groups : 0)) * (a.one.k + 4));
   d.g_off = a.one.g_off + (int64_t)c * ((a.one.k + 3) / 4 * 4);
   d.gate_off = c;
   return d;
@@ -302,45 +303,87 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
   if (tid == 0) store_coherent(part + k, xx);
 }
 
-// Run by the workgroup that wrote a call's last partial: sums the partials
-// in a fixed order (bitwise deterministic), writes g (agent-coherent stores
-// when GC), forms ||x||^2, ||g||^2 and rho (GSI-TS §2.2), and clears the
-// call's counter.  With a cached E = V_k^T V_k - I, rho is exact for the
+// Column j of `count` partial rows (stride floats apart) summed in row
+// order with agent-coherent loads, up to 64 loads in flight.
+__device__ __forceinline__ float sum_rows(const float *p0, int count, int stride, int j) {
+  float s = 0.f;
+  int qq = 0;
+  for (; qq + 64 <= count; qq += 64) {
+    float t[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) s += t[i];
+  }
+  for (; qq + 16 <= count; qq += 16) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += t[i];
+  }
+  for (; qq < count; ++qq) s += load_coherent(p0 + (int64_t)qq * stride + j);
+  return s;
+}
+
+// Hand-off after a projection unit stored its partial (after s_waitcnt 0
+// and a barrier).  Returns 1 on the workgroup that must finish the call:
+// with one group, the last unit; with several, the last unit of a group
+// first sums its group's partials into the group partial, and the last
+// group to do so finishes.  flag: an LDS int.
+__device__ __forceinline__ int projection_handoff(const CallDesc &cd, int c, int q, float *wsf,
+                                                  uint32_t *counters, uint32_t *gcounters, int *flag) {
+  const int tid = threadIdx.x;
+  const int stride = cd.k + 4;
+  if (cd.groups > 1) {
+    const int grp = q / kGroupUnits;
+    const int gsize = min(kGroupUnits, cd.a_units - grp * kGroupUnits);
+    if (tid == 0)
+      *flag = __hip_atomic_fetch_add(gcounters + cd.a_begin + grp, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(gsize - 1) ? 1 : 0;
+    __syncthreads();
+    if (!*flag) return 0;
+    const float *src = wsf + cd.part_off + (int64_t)grp * kGroupUnits * stride;
+    float *dst = wsf + cd.part_off + (int64_t)(cd.a_units + grp) * stride;
+    for (int j = tid; j <= cd.k; j += kBlock) store_coherent(dst + j, sum_rows(src, gsize, stride, j));
+    if (tid == 0) __hip_atomic_store(gcounters + cd.a_begin + grp, 0u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  const unsigned last = (unsigned)((cd.groups > 1 ? cd.groups : cd.a_units) - 1);
+  if (tid == 0)
+    *flag = __hip_atomic_fetch_add(counters + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == last ? 1 : 0;
+  __syncthreads();
+  return *flag;
+}
+
+// The partial rows the finishing workgroup sums: the unit partials, or the
+// group partials stored after them.
+__device__ __forceinline__ const float *final_rows(const CallDesc &cd, const float *wsf, int *count) {
+  if (cd.groups > 1) {
+    *count = cd.groups;
+    return wsf + cd.part_off + (int64_t)cd.a_units * (cd.k + 4);
+  }
+  *count = cd.a_units;
+  return wsf + cd.part_off;
+}
+
+// Run by the workgroup that finishes a call: sums the `count` final partial
+// rows at p0 in a fixed order (bitwise deterministic), writes g
+// (agent-coherent stores when GC), forms ||x||^2, ||g||^2 and rho
+// (GSI-TS §2.2), and clears the call's counter.  With a cached E = V_k^T V_k - I, rho is exact for the
 // stored basis (g also goes to the LDS scratch gl, k floats).  Returns
 // {rho, ||x||^2, ||g||^2} (valid on thread 0).
 template <typename T, bool GC>
-__device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const float *wsf, float *gw,
-                                                    uint32_t *counters, float *sh, float *gl) {
+__device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const float *p0, int count,
+                                                    float *gw, uint32_t *counters, float *sh, float *gl) {
   const int tid = threadIdx.x;
   const int k = cd.k;
   const int stride = k + 4;
-  const float *p0 = wsf + cd.part_off;
   float gg = 0.f;
   for (int j = tid; j < k; j += kBlock) {
-    float s = 0.f;
-    int qq = 0;
-    for (; qq + 64 <= cd.a_units; qq += 64) {
-      float t[64];
-#pragma unroll
-      for (int i = 0; i < 64; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
-#pragma unroll
-      for (int i = 0; i < 64; ++i) s += t[i];
-    }
-    for (; qq + 32 <= cd.a_units; qq += 32) {
-      float t[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) s += t[i];
-    }
-    for (; qq + 8 <= cd.a_units; qq += 8) {
-      float t[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = load_coherent(p0 + (int64_t)(qq + i) * stride + j);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += t[i];
-    }
-    for (; qq < cd.a_units; ++qq) s += load_coherent(p0 + (int64_t)qq * stride + j);
+    const float s = sum_rows(p0, count, stride, j);
     if (GC)
       store_coherent(gw + j, s);
     else
@@ -349,7 +392,7 @@ __device__ __forceinline__ float3 finish_projection(const CallDesc &cd, const fl
     gg = fmaf(s, s, gg);
   }
   float xp = 0.f;
-  for (int qq = tid; qq < cd.a_units; qq += kBlock) xp += load_coherent(p0 + (int64_t)qq * stride + k);
+  for (int qq = tid; qq < count; qq += kBlock) xp += load_coherent(p0 + (int64_t)qq * stride + k);
   gg = block_sum(gg, sh);
   const float xxt = block_sum(xp, sh);
   if (tid == 0) counters[cd.gate_off] = 0u;  // ready for the next launch on this workspace
@@ -390,15 +433,11 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
   // Hand the partials over (see the header); the last chunk finishes the gate.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + cd.gate_off, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(cd.a_units - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
+  if (!projection_handoff(cd, cd.gate_off, q, a.wsf, a.counters, a.gcounters, &s_last)) return;
 
-  const float3 r = finish_projection<T, false>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh, red);
+  int rows = 0;
+  const float *p0 = final_rows(cd, a.wsf, &rows);
+  const float3 r = finish_projection<T, false>(cd, p0, rows, a.wsf + cd.g_off, a.counters, sh, red);
   if (tid == 0) {
     // the gates of this call and of every call sharing its projection
     unsigned members = 0;
@@ -978,11 +1017,10 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         proj_partial<T, GSI_STACK_PROJ_UNROLL, false>(cd, q, part, red, sh);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0)
-        s_flag = ctl_add(a.counters + c, 1u) == (uint32_t)(cd.a_units - 1) ? 1 : 0;
-      __syncthreads();
-      if (s_flag) {
-        const float3 r = finish_projection<T, true>(cd, a.wsf, a.wsf + cd.g_off, a.counters, sh, red);
+      if (projection_handoff(cd, c, q, a.wsf, a.counters, a.gcounters, &s_flag)) {
+        int rows = 0;
+        const float *p0 = final_rows(cd, a.wsf, &rows);
+        const float3 r = finish_projection<T, true>(cd, p0, rows, a.wsf + cd.g_off, a.counters, sh, red);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // g of every thread is stored before any gate opens
         if (tid == 0) {

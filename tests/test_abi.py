@@ -128,7 +128,7 @@ DESC = np.dtype([("ptrs", "<u8", 7), ("d", "<i4"), ("d_out", "<i4"), ("k", "<i4"
                  ("a_begin", "<i4"), ("a_units", "<i4"), ("a_rows", "<i4"), ("fast_units", "<i4"),
                  ("slow_units", "<i4"), ("slow_rows", "<i4"), ("part_off", "<i8"), ("g_off", "<i8"),
                  ("gate_off", "<i4"), ("fast_tiles", "<i4"), ("flags", "<i4"), ("wave", "<i4"),
-                 ("share_next", "<i4"), ("pad", "<i4"), ("G", "<u8")])
+                 ("share_next", "<i4"), ("groups", "<i4"), ("G", "<u8")])
 
 
 def header(plan):
@@ -305,18 +305,32 @@ def test_stack_plan_shares_projections():
 
 def test_stack_plan_many_projection_units():
     """Latency-bound waves split V_k into 16-row units (bf16, k = 512: 16 KiB
-    each), up to 64 per call; the last unit may be ragged.  Partial rows of
-    the calls do not overlap and fit the float region."""
-    specs = [(592, 200, 512, 1), (536, 72, 512, 1), (512, 64, 512, 1), (2048, 128, 512, 1)]
-    st, plan, _ = build_plan(specs, waves=[0, 1, 2, 3])
+    each), up to 64 per call summed in one level; the last unit may be
+    ragged.  A wide V_k that 64 units would cut into pieces above 64 KiB
+    (fc_out, 16384 x 512: 256 KiB) gets up to 256 units of 64 KiB, summed in
+    two levels (groups of 16).  Partial rows (unit rows plus one per group)
+    do not overlap and fit the float region; the group counters fit after
+    the control words."""
+    specs = [(592, 200, 512, 1), (536, 72, 512, 1), (512, 64, 512, 1), (2048, 128, 512, 1),
+             (16384, 4096, 512, 1)]
+    st, plan, _ = build_plan(specs, waves=[0, 1, 2, 3, 4])
     assert st == GSI_OK
     h, desc, *_ = plan_tables(plan)
-    assert list(desc["a_units"]) == [37, 34, 32, 64]
-    assert list(desc["a_rows"]) == [16, 16, 16, 32]
-    spans = sorted((int(o), int(o) + int(u) * (int(k) + 4))
-                   for o, u, k in zip(desc["part_off"], desc["a_units"], desc["k"]))
+    assert list(desc["a_units"]) == [37, 34, 32, 64, 256]
+    assert list(desc["a_rows"]) == [16, 16, 16, 32, 64]
+    assert list(desc["groups"]) == [1, 1, 1, 1, 16]
+    rows = [int(u) + (int(g) if g > 1 else 0) for u, g in zip(desc["a_units"], desc["groups"])]
+    spans = sorted((int(o), int(o) + r * (int(k) + 4)) for o, r, k in zip(desc["part_off"], rows, desc["k"]))
     assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
     assert h["ws_float_off"] + 4 * spans[-1][1] <= h["ws_ctl_off"]
+    gcnt = (int(h["ws_ctl_off"]) + 4 * int(h["ctl_words"]) + 255) // 256 * 256
+    assert gcnt + 4 * int(h["units_a"]) <= h["ws_bytes"]
+    # the 112-map single-wave step keeps one level (fc_out: 43 units of 384 KiB)
+    st, plan, _ = build_plan([(4096, 12288, 256, 1), (4096, 4096, 256, 1), (4096, 16384, 256, 1),
+                              (16384, 4096, 512, 1)] * 28)
+    assert st == GSI_OK
+    _, desc, *_ = plan_tables(plan)
+    assert set(desc["groups"].tolist()) == {1}
 
 
 def test_gram_bytes_and_alignment():

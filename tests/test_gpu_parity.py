@@ -497,12 +497,15 @@ def test_shared_projection_stack(dtype):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
 def test_many_projection_units(dtype):
-    """Calls split into many 16-row projection units (d = 592: 37 units;
-    d = 536: 34 units, the last of 8 rows; d = 2048: 64 units of 32 rows in a
-    stack).  Oracle parity through gsi_linear and through a stack of one call
-    per wave, repeated runs on one workspace (the counters must return to
-    zero), and the same bits from the two-launch form."""
-    shapes = [(592, 200, 512), (536, 72, 512), (2048, 128, 512)]
+    """Calls split into many projection units (d = 592: 37 units of 16
+    rows; d = 536: 34 units, the last of 8 rows; d = 2048: 64 units of 32
+    rows in a stack, 128 through gsi_linear, summed in two levels; d = 6400:
+    100 (bf16) or 200 (fp32) units of 64 KiB in a stack, summed in two levels
+    with a ragged last group).  Oracle parity through gsi_linear and through
+    a stack of one call per wave, repeated runs on one workspace (the
+    counters must return to zero), and the same bits from the two-launch
+    form."""
+    shapes = [(592, 200, 512), (536, 72, 512), (2048, 128, 512), (6400, 96, 512)]
     items = []
     for i, (d, d_out, k) in enumerate(shapes):
         W = synth.gaussian_weight(d_out, d, (95, 0, i, 0), dtype=dtype)
@@ -546,13 +549,16 @@ def test_many_projection_units(dtype):
         compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y)[None], np.array([int(s.item())]),
                        np.array([float(r.item())]), dtype, rho_tol=2e-2, what=f"stack d={W.shape[1]}")
     assert st.status(ws) == 0
-    # one wave: the single launch and the two-launch form give the same bits
+    # one wave (its unit sizes follow the whole wave's bytes): oracle parity,
+    # and the single launch and the two-launch form give the same bits
     st1 = gsi.Stack([c[:6] for c in calls])
     ws1 = gsi.workspace(st1.ws_bytes, DEV)
     gsi.gsi_stack(st1, gsi.GATED, ws1)
     sync()
     one = [tuple(t.clone() for t in o[3:]) for o in outs]
-    assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(one, ref))
+    for W, V, X, y, r, s in outs:
+        compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(y)[None], np.array([int(s.item())]),
+                       np.array([float(r.item())]), dtype, rho_tol=2e-2, what=f"one wave d={W.shape[1]}")
     for _ in range(2):
         gsi.gsi_stack_phase(st1, gsi.GATED, gsi.PHASE_PROJECT, ws1)
         gsi.gsi_stack_phase(st1, gsi.GATED, gsi.PHASE_APPLY, ws1)
