@@ -454,16 +454,31 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
     }
 #undef GSI_OUT_STEP
     __syncthreads();
+    // The wavefront's 64 tokens x 64 columns of y go through its own LDS
+    // region (free after the loop), so that each lane stores 16-byte pieces
+    // of token rows instead of single elements.
+    constexpr int kYrow = 72;  // bf16 per staged row: 64 columns, padded to a 16-byte multiple
+    uint16_t *yt = reinterpret_cast<uint16_t *>(As[wave]);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = base + wave * 64 + m * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
-          const int col = o0 + c * 32 + (lane & 31);
-          if (row < count && col < a.d_out) Y[(size_t)idx[row] * a.d_out + col] = f2bf(acc[m][c][i]);
+          const int r = m * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
+          yt[r * kYrow + c * 32 + (lane & 31)] = f2bf(acc[m][c][i]);
         }
+    wave_lds_fence();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int pc = q * 64 + lane;  // piece: staged row pc / 8, columns 8 (pc % 8) ..
+      const int r = pc >> 3, c8 = (pc & 7) * 8;
+      const int row = base + wave * 64 + r;
+      if (row < count && o0 + c8 < a.d_out)
+        *reinterpret_cast<u32x4_t *>(Y + (size_t)idx[row] * a.d_out + o0 + c8) =
+            *reinterpret_cast<const u32x4_t *>(yt + r * kYrow + c8);
+    }
+    wave_lds_fence();  // the next round's stores to this region come after these reads
   }
 }
 
