@@ -176,11 +176,15 @@ size_t gsi_stack_workspace(const void *plan_host);
  * below for the same plan.  One persistent launch: the output work of a
  * call starts as soon as its own gate is decided, while other calls are
  * still projecting.
+ * The launch sizes its grid to what fits on the device at once and relies
+ * on all of it being resident (the first tickets of a wave are static, and
+ * a wave starts once every workgroup has left the previous one).
  * Every device-side wait of the launch is bounded; if a bound ever ran out
- * (a library fault, never expected) the launch still ends, the outputs of
- * that run are incomplete and a nonzero code is left in the 32-bit status
- * word at byte gsi_stack_status_offset(plan_host) of the workspace.  The
- * word stays set until the caller clears it; other runs leave it alone. */
+ * (a library fault, or a device whose compute units other kernels hold)
+ * the launch still ends, the outputs of that run are incomplete and a
+ * nonzero code is left in the 32-bit status word at byte
+ * gsi_stack_status_offset(plan_host) of the workspace.  The word stays set
+ * until the caller clears it; other runs leave it alone. */
 gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, void *ws,
                      size_t ws_bytes, void *stream);
 
