@@ -3,36 +3,43 @@
 // Method: "Gated Subspace Inference for Transformer Acceleration"
 // (S. J. Thomas, 2026), technical summary (GSI-TS) §2.1-§2.2.
 //
-// Batch-1 path (one token per call, many calls per launch):
-//   proj_kernel  : one workgroup per row chunk of V_k.  x's chunk is staged
-//                  in LDS; lanes own 16-byte column slices of V_k rows, so a
-//                  wavefront reads whole rows contiguously and accumulates
-//                  partial g = V_k^T x (fp32) plus the partial ||x||^2.  The
-//                  last workgroup of a call (device-scope counter) sums the
-//                  partials in a fixed order, forms ||g||^2, rho and the gate
-//                  (GSI-TS §2.2) and publishes them.  Bitwise deterministic.
+// Batch-1 path (one token per call, many calls per launch).  Work comes in
+// units: a projection unit is a row chunk of one call's V_k (partial
+// g = V_k^T x and partial ||x||^2, fp32), an output unit a run of 64-row
+// tiles of M (fast, y = M g) or of rows of W (slow, y = W x).  V_k, M and W
+// are streamed with nontemporal 16-byte loads.
 //
-//                  Cross-XCD hand-off without cache maintenance: the eight
-//                  XCDs of gfx950 have private L2s, and an agent-scope fence
-//                  compiles to an L2 write-back + invalidate that costs ~10x
-//                  the whole kernel when every workgroup issues one.  So the
-//                  partials are written with agent-scope atomic stores
-//                  (write-through, "sc1"), each thread waits for its stores to
-//                  be acknowledged (s_waitcnt 0) before the workgroup barrier,
-//                  one thread bumps the call's counter with a relaxed
-//                  agent-scope atomic, and the last workgroup reads the
-//                  partials with agent-scope atomic loads (which bypass stale
-//                  L2 lines).  Nothing else crosses workgroups inside the
-//                  launch; g and the gate reach apply_kernel through the
-//                  kernel boundary.
-//   apply_kernel : persistent loop over output units.  The projection
-//                  launch leaves a prefix over calls of "units needed by the
-//                  path this call's gate chose" (written by the last call to
-//                  finish), so only the chosen path's bytes are ever read and
-//                  each workgroup takes a contiguous, equal share of units.  Fast units: one lane per output row,
-//                  reading the tiled image M in 16-byte vectors against g in
-//                  LDS (y = M g).  Slow units: one wavefront per row of W,
-//                  x staged in LDS, wave reduction (y = W x).
+//   stack_kernel : gsi_stack, one persistent launch per stack.  Workgroups
+//                  take projection and output tickets wave by wave.  The
+//                  workgroup that writes a call's last partial sums the
+//                  partials in a fixed order (bitwise deterministic; in two
+//                  levels of at most 64 rows for calls with many units),
+//                  forms ||g||^2, rho and the gate (GSI-TS §2.2) and appends
+//                  the call to the wave's open list; output units of open
+//                  calls run while other calls still project.  A wave is
+//                  entered once every workgroup has left the previous one
+//                  (per-group counters and ready flags), so a call may read
+//                  the y of an earlier wave.  Every device-side wait is
+//                  bounded and reports through a status word.
+//   proj_kernel  : the projection phase as its own launch (gsi_stack_phase,
+//   apply_kernel   and gsi_linear's single-map path), then the output phase:
+//                  the projection launch leaves a prefix over calls of the
+//                  units their chosen paths need, and apply_kernel's
+//                  workgroups take contiguous, equal shares of those units.
+//
+// Cross-XCD hand-off without cache maintenance: the eight XCDs of gfx950 have
+// private L2s, and an agent-scope fence compiles to an L2 write-back +
+// invalidate that costs ~10x the whole projection when every workgroup
+// issues one.  So partials, g, control words and the activations handed
+// between waves are written with agent-scope atomic stores (write-through,
+// "sc1"), each thread waits for its stores to be acknowledged (s_waitcnt 0)
+// before the workgroup barrier that precedes the publishing atomic, and the
+// readers use agent-scope atomic loads (which bypass stale L2 lines).
+//
+// Fast units read the tiled image M (gsi.h) in 16-byte vectors against g in
+// LDS, one lane per output row (one tile split over the four wavefronts in
+// latency-bound waves); slow units take one wavefront per row of W with x
+// staged in LDS and a wave reduction.
 // prepare_kernel: M = W V_k for fp32 maps (FMA, LDS tiled), written in the
 //                 tiled layout described in gsi.h (bf16 maps use the MFMA
 //                 kernel in gsi_batched.hip).
