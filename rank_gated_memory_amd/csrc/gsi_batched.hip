@@ -13,11 +13,15 @@
 //   bgate_kernel : one workgroup per token: sums the S partials in a fixed
 //                  order, forms ||g||^2, rho and the gate, writes g as bf16
 //                  hi + lo (g = hi + lo to ~2^-16) for the fast GEMM.
-//   bout_kernel  : one launch per path.  Each workgroup compacts the tokens
-//                  of its path (deterministic order), takes 64 output columns
-//                  and all those tokens (256 per pass) and runs
-//                  v_mfma_f32_32x32x16_bf16 over K chunks of 64 with a
-//                  register-staged prefetch pipeline (see below).
+//   bout_kernel  : both paths' wide outputs (more than kThin tokens) in one
+//                  launch.  Each workgroup compacts the tokens of each path
+//                  from the gate flags itself (deterministic order), then
+//                  loops over 64-column tiles: all of a path's tokens (256
+//                  per pass) against the tile with v_mfma_f32_32x32x16_bf16
+//                  over K chunks of 64, register-staged prefetch, y leaving
+//                  through LDS in 16-byte pieces (see below).
+//   bthin_kernel : both paths' outputs with 1 to kThin tokens: the matrix is
+//                  streamed by 16-row blocks (v_mfma_f32_16x16x32_bf16).
 //
 // MFMA operand layouts (checked on the device): for 32x32x16, lane l holds
 // A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32], e = 0..7, and
