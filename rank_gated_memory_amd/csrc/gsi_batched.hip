@@ -418,6 +418,10 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
   uint16_t *Y = static_cast<uint16_t *>(a.y);
 
   for (int base = 0; base < count; base += 256) {
+    // A wavefront with no token in this round (fewer than 256 tokens left)
+    // still loads and stores its share of every B chunk and keeps the
+    // barriers, but skips the products.
+    const bool has_tokens = base + wave * 64 < count;
     int tk[8];  // token of each of this lane's A pieces
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -434,16 +438,15 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
 
     // Three named stages (an array of stages would live in scratch memory):
     // chunk i is consumed while chunks i+1 and i+2 load.  The main loop is
-    // branch-free and runs a multiple of three chunks, the last one or two
-    // chunks follow it; loads past K read the zero block and wavefronts
-    // without tokens multiply zeros.
+    // runs a multiple of three chunks, the last one or two chunks follow it;
+    // loads past K read the zero block.
     OutStage<PATH> s0, s1, s2;
 #define GSI_OUT_STEP(cur, ahead, i)                        \
   do {                                                     \
     out_load<PATH>(ahead, a, ((i) + 2) * 64, o0, tk, zero); \
     out_store<PATH>(cur, Bs[(i) & 1], As[wave]);           \
     __syncthreads();                                       \
-    out_mma<PATH>(Bs[(i) & 1], As[wave], acc);             \
+    if (has_tokens) out_mma<PATH>(Bs[(i) & 1], As[wave], acc); \
   } while (0)
     out_load<PATH>(s0, a, 0, o0, tk, zero);
     out_load<PATH>(s1, a, 64, o0, tk, zero);
