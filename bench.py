@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--dense-steps", type=int, default=16)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cells", default=None,
+                   help="batched-t256 only: run just these cells, 'k:slow_share,...' (for profiling)")
     return p.parse_args()
 
 
@@ -329,37 +331,40 @@ def bench_batched(args):
 
     dev = torch.device("cuda:0")
     cells = []
-    for k in (64, 256, 512):
-        for frac in (0.0, 0.1, 0.5, 1.0):
-            mi = synth.config5(k, frac, device=dev, w_device=dev)
-            m = gsi.Map(mi.W, mi.V)
-            gsi.gsi_prepare(m)
-            T = mi.X.shape[0]
-            y = torch.empty(T, mi.d_out, dtype=torch.bfloat16, device=dev)
-            rho = torch.empty(T, device=dev)
-            sl = torch.empty(T, dtype=torch.uint8, device=dev)
-            ws = gsi.workspace(gsi.gsi_linear_workspace(m, T), dev)
-            for _ in range(args.warmup):
-                gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / args.steps * 1e3
-            ns = int(sl.sum())
-            nf = T - ns
-            d, do = mi.d, mi.d_out
-            byts = 2 * (d * k + T * d + T * do) + (2 * do * k if nf else 0) + (2 * d * do if ns else 0)
-            flops = 2 * T * d * k + 2 * 2 * nf * do * k + 2 * ns * d * do
-            cells.append({"k": k, "slow_share": frac, "slow_tokens": ns, "us_per_call": us,
-                          "tokens_per_s": T / (us * 1e-6), "gbps": byts / us / 1e3,
-                          "tflops": flops / us / 1e6, "mfma_frac": flops / us / 1e6 / PEAK_BF16_TFLOPS})
-            log(f"k={k} slow={frac}: {us:.1f} us, {T / us * 1e6:.0f} tokens/s")
-            del m, mi, ws, y
-    head = [c for c in cells if c["k"] == 256 and c["slow_share"] == 0.1][0]
+    grid = [(k, frac) for k in (64, 256, 512) for frac in (0.0, 0.1, 0.5, 1.0)]
+    if args.cells:
+        grid = [(int(c.split(":")[0]), float(c.split(":")[1])) for c in args.cells.split(",")]
+    for k, frac in grid:
+        mi = synth.config5(k, frac, device=dev, w_device=dev)
+        m = gsi.Map(mi.W, mi.V)
+        gsi.gsi_prepare(m)
+        T = mi.X.shape[0]
+        y = torch.empty(T, mi.d_out, dtype=torch.bfloat16, device=dev)
+        rho = torch.empty(T, device=dev)
+        sl = torch.empty(T, dtype=torch.uint8, device=dev)
+        ws = gsi.workspace(gsi.gsi_linear_workspace(m, T), dev)
+        for _ in range(args.warmup):
+            gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        ns = int(sl.sum())
+        nf = T - ns
+        d, do = mi.d, mi.d_out
+        byts = 2 * (d * k + T * d + T * do) + (2 * do * k if nf else 0) + (2 * d * do if ns else 0)
+        flops = 2 * T * d * k + 2 * 2 * nf * do * k + 2 * ns * d * do
+        cells.append({"k": k, "slow_share": frac, "slow_tokens": ns, "us_per_call": us,
+                      "tokens_per_s": T / (us * 1e-6), "gbps": byts / us / 1e3,
+                      "tflops": flops / us / 1e6, "mfma_frac": flops / us / 1e6 / PEAK_BF16_TFLOPS})
+        log(f"k={k} slow={frac}: {us:.1f} us, {T / us * 1e6:.0f} tokens/s")
+        del m, mi, ws, y
+    heads = [c for c in cells if c["k"] == 256 and c["slow_share"] == 0.1]
+    head = heads[0] if heads else cells[0]
     print(json.dumps({
         "metric": "GSI batched gated linear tokens/s (T=256, d=4096 -> 16384)",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
