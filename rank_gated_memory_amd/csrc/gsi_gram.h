@@ -18,62 +18,46 @@ namespace gsi {
 // 4: fp32), g [k] in LDS; k a multiple of 16 / ESIZE.  E is symmetric
 // (entries (i, j) and (j, i) sum the same products in the same order), so
 // only its upper triangle is read: q = sum_i E_ii g_i^2 + 2 sum_{i<j} E_ij
-// g_i g_j.  The 16-byte pieces of row i from the one holding E_ii on form a
-// staircase: rows of block b (rows b VW .. b VW + VW - 1) hold the pieces
-// b .. n-1 (n = k / VW), so block b starts at piece VW (b n - b (b-1) / 2)
-// of the flattened triangle.  The workgroup (NT threads) walks that range
-// with U pieces per thread in flight; every thread returns the same,
-// order-fixed sum (sh: NT/64 floats).
+// g_i g_j.  Wavefront w takes rows w, w + NT/64, ...; in row r its lanes
+// take the 16-byte pieces from the one holding E_rr on (shifts only, no
+// division), U rows per batch with every load issued first.  Every thread
+// returns the same, order-fixed sum (sh: NT/64 floats).
 template <int ESIZE, int NT>
 __device__ __forceinline__ float gram_quadratic(const void *E, int k, const float *g, float *sh) {
   constexpr int VW = 16 / ESIZE;
-#ifndef GSI_GRAM_UNROLL
-#define GSI_GRAM_UNROLL 16
-#endif
-  constexpr int U = GSI_GRAM_UNROLL;
-  const int n = k / VW;
-  const int total = VW * n * (n + 1) / 2;
+  constexpr int NW = NT / 64;
+  constexpr int U = 16;
+  const int n = k / VW;  // pieces per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint4 *e4 = static_cast<const uint4 *>(E);
-  const float nn = (float)(2 * n + 1);
   float acc = 0.f;
-  for (int p0 = threadIdx.x; p0 < total; p0 += NT * U) {
-    uint4 v[U];
-    int rc[U];  // row * n + piece column
+  for (int r0 = wave; r0 < k; r0 += NW * U) {
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      uint4 v[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int p = p0 + i * NT;
-      int r = 0, c = 0;
-      if (p < total) {
-        // block b: the largest b with VW (b n - b (b-1)/2) <= p
-        int b = (int)((nn - sqrtf(nn * nn - 8.f * (float)p / VW)) * 0.5f);
-        b = b < 0 ? 0 : (b > n - 1 ? n - 1 : b);
-        while (b > 0 && VW * (b * n - b * (b - 1) / 2) > p) --b;
-        while (b < n - 1 && VW * ((b + 1) * n - (b + 1) * b / 2) <= p) ++b;
-        const int q = p - VW * (b * n - b * (b - 1) / 2);
-        const int len = n - b;
-        r = b * VW + q / len;
-        c = b + q % len;
-        v[i] = e4[(size_t)r * n + c];
-      } else {
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * NW;
+        const int c = r / VW + c0 + lane;  // VW is a power of two
+        v[u] = (r < k && c < n) ? e4[(size_t)r * n + c] : make_uint4(0u, 0u, 0u, 0u);
       }
-      rc[i] = p < total ? r * n + c : -1;
-    }
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (rc[i] >= 0) {
-        const int r = rc[i] / n, c0 = (rc[i] - r * n) * VW;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        float s = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * NW;
+        const int c = r / VW + c0 + lane;
+        if (r < k && c < n) {
+          const int col0 = c * VW;
+          const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < VW; ++e) {
-          const int col = c0 + e;
-          const float ev = ESIZE == 2 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
-                                      : __uint_as_float(w[e]);
-          const float wt = col > r ? 2.f : (col == r ? 1.f : 0.f);
-          s = fmaf(wt * ev, g[col], s);
+          for (int e = 0; e < VW; ++e) {
+            const int col = col0 + e;
+            const float ev = ESIZE == 2 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
+                                        : __uint_as_float(w[e]);
+            const float wt = col > r ? 2.f : (col == r ? 1.f : 0.f);
+            sum = fmaf(wt * ev, g[col], sum);
+          }
+          acc = fmaf(g[r], sum, acc);
         }
-        acc = fmaf(g[r], s, acc);
       }
     }
   }

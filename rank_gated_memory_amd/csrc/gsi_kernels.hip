@@ -311,7 +311,10 @@ __device__ __forceinline__ void proj_partial(const CallDesc &cd, int q, float *p
 }
 
 // Column j of `count` partial rows (stride floats apart) summed in row
-// order with agent-coherent loads, up to 64 loads in flight.
+// order with agent-coherent loads: batches of 64, then of 16, then one
+// predicated batch for the last 1-15 rows, every load of a batch issued
+// before its first add (a tail of a few rows costs one round trip, not one
+// each).
 __device__ __forceinline__ float sum_rows(const float *p0, int count, int stride, int j) {
   float s = 0.f;
   int qq = 0;
@@ -329,7 +332,15 @@ __device__ __forceinline__ float sum_rows(const float *p0, int count, int stride
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += t[i];
   }
-  for (; qq < count; ++qq) s += load_coherent(p0 + (int64_t)qq * stride + j);
+  if (qq < count) {
+    float t[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i)
+      t[i] = qq + i < count ? load_coherent(p0 + (int64_t)(qq + i) * stride + j) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 15; ++i)
+      if (qq + i < count) s += t[i];
+  }
   return s;
 }
 
