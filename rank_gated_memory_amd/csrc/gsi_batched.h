@@ -36,14 +36,19 @@ struct BatchShape {
   uint64_t zeros_off, part_off, xxp_off, ghi_off, glo_off, flags_off, total;
 };
 
+#ifndef GSI_BPROJ_WGS
+#define GSI_BPROJ_WGS 256
+#endif
+
 // Projection GEMM G = X V_k: 64 x 64 tiles of G, each split over K into
-// `splits` ranges of kc rows (at least 512 workgroups in all when d allows).
+// `splits` ranges of kc rows (at least 256 workgroups in all when d allows:
+// more splits cost the gate more partial rows than the extra parallelism buys).
 inline BatchShape batch_shape(int n, int d, int k) {
   BatchShape b{};
   b.kpad = (k + 15) / 16 * 16;
   const int tt = (n + 63) / 64, kt = (k + 63) / 64;
   int s = (d + kBatchKc - 1) / kBatchKc;
-  const int want = (512 + tt * kt - 1) / (tt * kt);
+  const int want = (GSI_BPROJ_WGS + tt * kt - 1) / (tt * kt);
   if (want > s) s = want;
   const int smax = (d + 31) / 32;
   if (s > smax) s = smax;
