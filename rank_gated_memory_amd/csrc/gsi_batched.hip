@@ -301,9 +301,17 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 // through the wavefront's own LDS region, since loading it in operand layout
 // would touch a different token row, and cache line, in every lane.
 // ---------------------------------------------------------------------------
+#ifndef GSI_OUT_DEPTH_FAST
+#define GSI_OUT_DEPTH_FAST 3
+#endif
+#ifndef GSI_OUT_DEPTH_SLOW
+#define GSI_OUT_DEPTH_SLOW 3
+#endif
+
 template <int PATH>
 struct OutStage {
   static constexpr int NA = PATH == 0 ? 2 : 1;  // A matrices: (hi, lo) or (x)
+  static constexpr int kDepth = PATH == 0 ? GSI_OUT_DEPTH_FAST : GSI_OUT_DEPTH_SLOW;  // stages in the ring
   u32x4_t b0, b1;                               // this thread's two 16-byte pieces of B
   u32x4_t a[NA][8];                             // piece i * 64 + lane of the 64 x 128-byte A chunk
 };
@@ -353,6 +361,18 @@ __device__ __forceinline__ void out_load(OutStage<PATH> &st, const BArgs &a, int
   }
 }
 
+// Column slot of piece (k group cg, column c) in the B chunk.  The slow
+// path's eight lanes of one W row write the eight k groups of one column,
+// 1 KiB apart in [k group][column] order, which would fall in one bank; the
+// column is XOR-ed with the k group so that they spread over eight 16-byte
+// slots.  The operand reads (one k group, 32 consecutive columns) then read
+// a permutation of those columns, still without conflict.  The fast path
+// stores whole k-group rows and keeps the plain order.
+template <int PATH>
+__device__ __forceinline__ int b_col(int cg, int c) {
+  return PATH == 0 ? c : (c ^ cg);
+}
+
 // The wavefront's A region: 64 token rows of 8 pieces, padded to 9 so that
 // the 16 rows read by a quarter-wave fall in different banks.
 constexpr int kOutArow = 9;
@@ -365,8 +385,8 @@ __device__ __forceinline__ void out_store(const OutStage<PATH> &st, u32x4_t (*Bs
     Bs[tid >> 6][tid & 63] = st.b0;
     Bs[v1 >> 6][v1 & 63] = st.b1;
   } else {
-    Bs[tid & 7][tid >> 3] = st.b0;
-    Bs[v1 & 7][v1 >> 3] = st.b1;
+    Bs[tid & 7][b_col<PATH>(tid & 7, tid >> 3)] = st.b0;
+    Bs[v1 & 7][b_col<PATH>(v1 & 7, v1 >> 3)] = st.b1;
   }
   wave_lds_fence();  // the previous chunk's reads of As are done
 #pragma unroll
@@ -380,8 +400,9 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8_t b0 = as_bf16x8(Bs[ks * 2 + (lane >> 5)][lane & 31]);
-    const bf16x8_t b1 = as_bf16x8(Bs[ks * 2 + (lane >> 5)][32 + (lane & 31)]);
+    const int cg = ks * 2 + (lane >> 5);
+    const bf16x8_t b0 = as_bf16x8(Bs[cg][b_col<PATH>(cg, lane & 31)]);
+    const bf16x8_t b1 = as_bf16x8(Bs[cg][b_col<PATH>(cg, 32 + (lane & 31))]);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -414,7 +435,6 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
 
   const int K = PATH == 0 ? a.kpad : a.d;
   const int nch = (K + 63) / 64;
-  const int nch3 = nch - nch % 3;
   uint16_t *Y = static_cast<uint16_t *>(a.y);
 
   for (int base = 0; base < count; base += 256) {
@@ -436,30 +456,32 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.f;
 
-    // Three named stages (an array of stages would live in scratch memory):
-    // chunk i is consumed while chunks i+1 and i+2 load.  The main loop is
-    // runs a multiple of three chunks, the last one or two chunks follow it;
-    // loads past K read the zero block.
-    OutStage<PATH> s0, s1, s2;
-#define GSI_OUT_STEP(cur, ahead, i)                        \
-  do {                                                     \
-    out_load<PATH>(ahead, a, ((i) + 2) * 64, o0, tk, zero); \
-    out_store<PATH>(cur, Bs[(i) & 1], As[wave]);           \
-    __syncthreads();                                       \
-    if (has_tokens) out_mma<PATH>(Bs[(i) & 1], As[wave], acc); \
-  } while (0)
-    out_load<PATH>(s0, a, 0, o0, tk, zero);
-    out_load<PATH>(s1, a, 64, o0, tk, zero);
-    for (int i = 0; i < nch3; i += 3) {
-      GSI_OUT_STEP(s0, s2, i);
-      GSI_OUT_STEP(s1, s0, i + 1);
-      GSI_OUT_STEP(s2, s1, i + 2);
+    // A ring of D stages: chunk i is consumed while chunks i+1 .. i+D-1
+    // load (3 stages; deeper rings for the slow path, 4-6, measured no
+    // faster).  The ring is indexed by constants only (every loop over it is
+    // unrolled), so it stays in registers; loads past K read the zero block.
+    constexpr int D = OutStage<PATH>::kDepth;
+    OutStage<PATH> st[D];
+#pragma unroll
+    for (int j = 0; j + 1 < D; ++j) out_load<PATH>(st[j], a, j * 64, o0, tk, zero);
+    int i = 0;
+    for (; i + D <= nch; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        out_load<PATH>(st[(j + D - 1) % D], a, (i + j + D - 1) * 64, o0, tk, zero);
+        out_store<PATH>(st[j], Bs[(i + j) & 1], As[wave]);
+        __syncthreads();
+        if (has_tokens) out_mma<PATH>(Bs[(i + j) & 1], As[wave], acc);
+      }
     }
-    if (nch3 < nch) {
-      GSI_OUT_STEP(s0, s2, nch3);
-      if (nch3 + 1 < nch) GSI_OUT_STEP(s1, s0, nch3 + 1);
+#pragma unroll
+    for (int j = 0; j + 1 < D; ++j) {
+      if (i + j < nch) {
+        out_store<PATH>(st[j], Bs[(i + j) & 1], As[wave]);
+        __syncthreads();
+        if (has_tokens) out_mma<PATH>(Bs[(i + j) & 1], As[wave], acc);
+      }
     }
-#undef GSI_OUT_STEP
     __syncthreads();
     // The wavefront's 64 tokens x 64 columns of y go through its own LDS
     // region (free after the loop), so that each lane stores 16-byte pieces
