@@ -82,12 +82,14 @@ __device__ __forceinline__ float rho_of(float xx, float gg) {
 
 namespace {
 
-// Inclusive workgroup scan of two counters at once (Hillis-Steele in LDS).
+// Inclusive workgroup scan of two counters at once (Hillis-Steele in LDS)
+// over the NT threads of the workgroup.
+template <int NT>
 __device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
   const int tid = threadIdx.x;
   sh[tid] = v;
   __syncthreads();
-  for (int off = 1; off < kBlock; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     const int2 u = tid >= off ? sh[tid - off] : make_int2(0, 0);
     __syncthreads();
     sh[tid].x += u.x;
@@ -99,25 +101,28 @@ __device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
 
 // Tokens of each path in increasing order, from the gate flags: the fast
 // tokens in idx[0, nf), the slow ones in idx[nf, n).  Every output
-// workgroup compacts the n flags itself (one load per thread at n = 256 and
-// a scan in LDS), so the gate needs no grid-wide step.  Returns (nf, ns).
+// workgroup (NT threads) compacts the n flags itself (one load per thread at
+// n = 256 and a scan in LDS), so the gate needs no grid-wide step.  Returns
+// (nf, ns).
+template <int NT>
 __device__ __forceinline__ int2 path_lists(const BArgs &a, int16_t *idx, int2 *scan) {
   const int tid = threadIdx.x;
-  const int per = (a.n + kBlock - 1) / kBlock;
+  const int per = (a.n + NT - 1) / NT;
   const int c0 = tid * per;
-  int fl[kMaxBatch / kBlock];
+  constexpr int kPer = (kMaxBatch + NT - 1) / NT;
+  int fl[kPer];
   int2 mine = make_int2(0, 0);
 #pragma unroll
-  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     fl[i] = (i < per && c0 + i < a.n) ? a.flags[c0 + i] : -1;
     mine.x += fl[i] == 0;
     mine.y += fl[i] == 1;
   }
-  const int2 inc = block_scan2(mine, scan);
-  const int2 tot = scan[kBlock - 1];
+  const int2 inc = block_scan2<NT>(mine, scan);
+  const int2 tot = scan[NT - 1];
   int wf = inc.x - mine.x, ws = tot.x + inc.y - mine.y;
 #pragma unroll
-  for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     if (fl[i] == 0) idx[wf++] = (int16_t)(c0 + i);
     if (fl[i] == 1) idx[ws++] = (int16_t)(c0 + i);
   }
@@ -291,15 +296,18 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 //
 // PATH 0 (fast): A = G as bf16 hi + lo [n][kpad], B = the image tile (M's
 // 64-row tile is already in MFMA order); PATH 1 (slow): A = X [n][d], B = 64
-// rows of W.  Each wavefront owns 64 tokens (two 32-row MFMA tiles) x 64
-// columns.  K advances in chunks of 64: every thread prefetches its share of
-// the B chunk and every wavefront its own token rows of the A chunk two
-// chunks ahead into registers; the B chunk goes through a double-buffered
-// LDS tile shared by the four wavefronts.  One workgroup per CU streams its
-// 64 rows of W (or M) exactly once per 256 tokens.  The A chunk is loaded
-// row-contiguously (eight lanes per 128-byte token row) and transposed
-// through the wavefront's own LDS region, since loading it in operand layout
-// would touch a different token row, and cache line, in every lane.
+// rows of W.  A workgroup has eight wavefronts, two per SIMD, so that one
+// wavefront's products run while the other waits on its loads, its LDS
+// traffic or the barrier; each owns 32 tokens (one 32-row MFMA tile) x 64
+// columns, 256 tokens per round.  K advances in chunks of 64: every thread
+// prefetches its 16-byte piece of the B chunk and every wavefront its own
+// token rows of the A chunk D-1 chunks ahead into registers; the B chunk
+// goes through a double-buffered LDS tile shared by the eight wavefronts.
+// One workgroup per CU streams its 64 rows of W (or M) exactly once per 256
+// tokens.  The A chunk is loaded row-contiguously (eight lanes per 128-byte
+// token row) and transposed through the wavefront's own LDS region, since
+// loading it in operand layout would touch a different token row, and cache
+// line, in every lane.
 // ---------------------------------------------------------------------------
 #ifndef GSI_OUT_DEPTH_FAST
 #define GSI_OUT_DEPTH_FAST 3
@@ -308,12 +316,17 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 #define GSI_OUT_DEPTH_SLOW 3
 #endif
 
+constexpr int kOutWaves = 8;
+constexpr int kOutThreads = kOutWaves * 64;
+constexpr int kOutTok = 32;                     // tokens of a wavefront in a round
+constexpr int kOutRound = kOutWaves * kOutTok;  // tokens of a round
+
 template <int PATH>
 struct OutStage {
   static constexpr int NA = PATH == 0 ? 2 : 1;  // A matrices: (hi, lo) or (x)
   static constexpr int kDepth = PATH == 0 ? GSI_OUT_DEPTH_FAST : GSI_OUT_DEPTH_SLOW;  // stages in the ring
-  u32x4_t b0, b1;                               // this thread's two 16-byte pieces of B
-  u32x4_t a[NA][8];                             // piece i * 64 + lane of the 64 x 128-byte A chunk
+  u32x4_t b;                                    // this thread's 16-byte piece of B
+  u32x4_t a[NA][4];                             // piece i * 64 + lane of the 32 x 128-byte A chunk
 };
 
 // Address of the 16-byte piece v (0..511) of the B chunk at K offset kk0.
@@ -340,14 +353,13 @@ __device__ __forceinline__ const u32x4_t *out_b_ptr(const BArgs &a, int kk0, int
 // prefetched load in flight.
 template <int PATH>
 __device__ __forceinline__ void out_load(OutStage<PATH> &st, const BArgs &a, int kk0, int o0,
-                                         const int (&tk)[8], const u32x4_t *zero) {
+                                         const int (&tk)[4], const u32x4_t *zero) {
   const int tid = threadIdx.x, lane = tid & 63;
-  st.b0 = *out_b_ptr<PATH>(a, kk0, o0, tid, zero);
-  st.b1 = *out_b_ptr<PATH>(a, kk0, o0, tid + kBlock, zero);
+  st.b = *out_b_ptr<PATH>(a, kk0, o0, tid, zero);
   const int K = PATH == 0 ? a.k : a.d;
   const int kg = kk0 + (lane & 7) * 8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const bool ok = tk[i] >= 0 && kg < K;
     if (PATH == 0) {
       const size_t off = (size_t)tk[i] * a.kpad + kg;
@@ -373,30 +385,26 @@ __device__ __forceinline__ int b_col(int cg, int c) {
   return PATH == 0 ? c : (c ^ cg);
 }
 
-// The wavefront's A region: 64 token rows of 8 pieces, padded to 9 so that
+// The wavefront's A region: 32 token rows of 8 pieces, padded to 9 so that
 // the 16 rows read by a quarter-wave fall in different banks.
 constexpr int kOutArow = 9;
 
 template <int PATH>
 __device__ __forceinline__ void out_store(const OutStage<PATH> &st, u32x4_t (*Bs)[64], u32x4_t *As) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int v1 = tid + kBlock;
-  if (PATH == 0) {
-    Bs[tid >> 6][tid & 63] = st.b0;
-    Bs[v1 >> 6][v1 & 63] = st.b1;
-  } else {
-    Bs[tid & 7][b_col<PATH>(tid & 7, tid >> 3)] = st.b0;
-    Bs[v1 & 7][b_col<PATH>(v1 & 7, v1 >> 3)] = st.b1;
-  }
+  if (PATH == 0)
+    Bs[tid >> 6][tid & 63] = st.b;
+  else
+    Bs[tid & 7][b_col<PATH>(tid & 7, tid >> 3)] = st.b;
   wave_lds_fence();  // the previous chunk's reads of As are done
 #pragma unroll
   for (int q = 0; q < OutStage<PATH>::NA; ++q)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) As[(q * 64 + i * 8 + (lane >> 3)) * kOutArow + (lane & 7)] = st.a[q][i];
+    for (int i = 0; i < 4; ++i) As[(q * kOutTok + i * 8 + (lane >> 3)) * kOutArow + (lane & 7)] = st.a[q][i];
 }
 
 template <int PATH>
-__device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *As, f32x16_t (&acc)[2][2]) {
+__device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *As, f32x16_t (&acc)[2]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -404,22 +412,20 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
     const bf16x8_t b0 = as_bf16x8(Bs[cg][b_col<PATH>(cg, lane & 31)]);
     const bf16x8_t b1 = as_bf16x8(Bs[cg][b_col<PATH>(cg, 32 + (lane & 31))]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int q = 0; q < OutStage<PATH>::NA; ++q) {
-        const bf16x8_t A = as_bf16x8(As[(q * 64 + m * 32 + (lane & 31)) * kOutArow + ks * 2 + (lane >> 5)]);
-        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b0, acc[m][0], 0, 0, 0);
-        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b1, acc[m][1], 0, 0, 0);
-      }
+    for (int q = 0; q < OutStage<PATH>::NA; ++q) {
+      const bf16x8_t A = as_bf16x8(As[(q * kOutTok + (lane & 31)) * kOutArow + ks * 2 + (lane >> 5)]);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b1, acc[1], 0, 0, 0);
+    }
   }
 }
 
 // LDS of the wide kernel, sized for the fast path (two A matrices).
 struct OutLds {
-  u32x4_t Bs[2][8][64];                  // double-buffered 64-wide K chunk: [k group][column]
-  u32x4_t As[kWaves][2 * 64 * kOutArow];  // each wavefront's A chunk
-  int16_t idx[kMaxBatch];                // tokens of both paths (path_lists)
-  int2 scan[kBlock];
+  u32x4_t Bs[2][8][64];                          // double-buffered 64-wide K chunk: [k group][column]
+  u32x4_t As[kOutWaves][2 * kOutTok * kOutArow];  // each wavefront's A chunk
+  int16_t idx[kMaxBatch];                        // tokens of both paths (path_lists)
+  int2 scan[kOutThreads];
 };
 
 template <int PATH>
@@ -437,28 +443,26 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
   const int nch = (K + 63) / 64;
   uint16_t *Y = static_cast<uint16_t *>(a.y);
 
-  for (int base = 0; base < count; base += 256) {
+  for (int base = 0; base < count; base += kOutRound) {
     // A wavefront with no token in this round (fewer than 256 tokens left)
     // still loads and stores its share of every B chunk and keeps the
     // barriers, but skips the products.
-    const bool has_tokens = base + wave * 64 < count;
-    int tk[8];  // token of each of this lane's A pieces
+    const int row0 = base + wave * kOutTok;
+    const bool has_tokens = row0 < count;
+    int tk[4];  // token of each of this lane's A pieces
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = base + wave * 64 + i * 8 + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + i * 8 + (lane >> 3);
       tk[i] = row < count ? idx[row] : -1;
     }
-    f32x16_t acc[2][2];
+    f32x16_t acc[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
 
     // A ring of D stages: chunk i is consumed while chunks i+1 .. i+D-1
-    // load (3 stages; deeper rings for the slow path, 4-6, measured no
-    // faster).  The ring is indexed by constants only (every loop over it is
+    // load.  The ring is indexed by constants only (every loop over it is
     // unrolled), so it stays in registers; loads past K read the zero block.
     constexpr int D = OutStage<PATH>::kDepth;
     OutStage<PATH> st[D];
@@ -483,26 +487,24 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
       }
     }
     __syncthreads();
-    // The wavefront's 64 tokens x 64 columns of y go through its own LDS
+    // The wavefront's 32 tokens x 64 columns of y go through its own LDS
     // region (free after the loop), so that each lane stores 16-byte pieces
     // of token rows instead of single elements.
     constexpr int kYrow = 72;  // bf16 per staged row: 64 columns, padded to a 16-byte multiple
     uint16_t *yt = reinterpret_cast<uint16_t *>(As[wave]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
-          yt[r * kYrow + c * 32 + (lane & 31)] = f2bf(acc[m][c][i]);
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+        yt[r * kYrow + c * 32 + (lane & 31)] = f2bf(acc[c][e]);
+      }
     wave_lds_fence();
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int pc = q * 64 + lane;  // piece: staged row pc / 8, columns 8 (pc % 8) ..
       const int r = pc >> 3, c8 = (pc & 7) * 8;
-      const int row = base + wave * 64 + r;
+      const int row = row0 + r;
       if (row < count && o0 + c8 < a.d_out)
         *reinterpret_cast<u32x4_t *>(Y + (size_t)idx[row] * a.d_out + o0 + c8) =
             *reinterpret_cast<const u32x4_t *>(yt + r * kYrow + c8);
@@ -514,9 +516,9 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
 // Both paths in one launch: the workgroups (about one per CU) walk the
 // 64-column tiles of every path with more than kThin tokens, fast path
 // first; with no such path they leave after the compaction.
-__global__ void __launch_bounds__(kBlock, 1) bout_kernel(BArgs a) {
+__global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
   __shared__ __align__(16) OutLds L;
-  const int2 cnt = path_lists(a, L.idx, L.scan);
+  const int2 cnt = path_lists<kOutThreads>(a, L.idx, L.scan);
   const int tiles = (a.d_out + 63) / 64;
   const int nf = cnt.x > kThin ? tiles : 0;
   const int ns = cnt.y > kThin ? tiles : 0;
@@ -701,7 +703,7 @@ __global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
   __shared__ int16_t idx[kMaxBatch];
   __shared__ int2 scan[kBlock];
   __shared__ int toks[2][kThin];
-  const int2 cnt = path_lists(a, idx, scan);
+  const int2 cnt = path_lists<kBlock>(a, idx, scan);
   const int tid = threadIdx.x;
   if (tid < 2 * kThin) {
     const int p = tid / kThin, i = tid % kThin;
@@ -805,7 +807,7 @@ hipError_t launch_batched(const BArgs &a, hipStream_t s) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, bthin_kernel, kBlock, 0) != hipSuccess || occ < 1)
     occ = 1;
   const int tiles = (a.d_out + 63) / 64, rbs = (a.d_out + 15) / 16;
-  hipLaunchKernelGGL(bout_kernel, dim3(cus < 2 * tiles ? cus : 2 * tiles), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(bout_kernel, dim3(cus < 2 * tiles ? cus : 2 * tiles), dim3(kOutThreads), 0, s, a);
   hipLaunchKernelGGL(bthin_kernel, dim3(occ * cus < 2 * rbs ? occ * cus : 2 * rbs), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
