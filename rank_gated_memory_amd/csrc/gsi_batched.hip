@@ -310,10 +310,10 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 // line, in every lane.
 // ---------------------------------------------------------------------------
 #ifndef GSI_OUT_DEPTH_FAST
-#define GSI_OUT_DEPTH_FAST 3
+#define GSI_OUT_DEPTH_FAST 2
 #endif
 #ifndef GSI_OUT_DEPTH_SLOW
-#define GSI_OUT_DEPTH_SLOW 3
+#define GSI_OUT_DEPTH_SLOW 2
 #endif
 
 constexpr int kOutWaves = 8;
@@ -462,8 +462,9 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
       for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
 
     // A ring of D stages: chunk i is consumed while chunks i+1 .. i+D-1
-    // load.  The ring is indexed by constants only (every loop over it is
-    // unrolled), so it stays in registers; loads past K read the zero block.
+    // load (two stages: with two wavefronts per SIMD, three or four measured
+    // no faster).  The ring is indexed by constants only (every loop over it
+    // is unrolled), so it stays in registers; loads past K read the zero block.
     constexpr int D = OutStage<PATH>::kDepth;
     OutStage<PATH> st[D];
 #pragma unroll
@@ -534,10 +535,13 @@ __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
 // Outputs of a path with at most kThin tokens: streaming the matrix by rows.
 //
 // With few tokens the output GEMM is a stream of W (slow) or M (fast) and is
-// bound by HBM.  A workgroup owns 16 output rows; its four wavefronts take a
-// quarter of K each and meet in LDS at the end, so there is no barrier in the
-// K loop.  v_mfma_f32_16x16x32_bf16 with A = 16 matrix rows and B = 16 tokens
-// (kThin tokens are two B groups).
+// bound by HBM.  A workgroup owns 16 RT output rows (RT tiles of 16);
+// its four wavefronts take a quarter of K each and meet in LDS at the end, so
+// there is no barrier in the K loop.  v_mfma_f32_16x16x32_bf16 with A = 16
+// matrix rows and B = 16 tokens (kThin tokens are two B groups).  Every
+// workgroup reads all of the path's token rows, so more rows per workgroup
+// means fewer token bytes per matrix byte: with 32 rows (the slow path) the
+// CUs take in one byte of x per byte of W (with 16 rows, two).
 //
 // In the MFMA operand layout the 16 lanes of a quarter-wave hold 16 different
 // rows, so loading W rows or token rows in that layout touches 16 cache lines
@@ -549,17 +553,28 @@ __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
 // read directly.  One stage is in flight in registers while the previous one
 // goes through LDS and the matrix cores.
 // ---------------------------------------------------------------------------
+#ifndef GSI_THIN_RT_SLOW
+#define GSI_THIN_RT_SLOW 2
+#endif
+#ifndef GSI_THIN_RT_FAST
+#define GSI_THIN_RT_FAST 1
+#endif
+
 template <int PATH>
 struct ThinStage {
   static constexpr int NB = PATH == 0 ? 2 : 1;  // B matrices: (g hi, g lo) or (x)
-  u32x4_t A[4];      // slow: piece i * 64 + lane of the 16 x 256-byte W tile; fast: k-step i of M
+  // 16-row tiles of a workgroup (the fast path's two B matrices leave no
+  // registers for a second tile at two wavefronts per SIMD)
+  static constexpr int RT = PATH == 0 ? GSI_THIN_RT_FAST : GSI_THIN_RT_SLOW;
+  static constexpr int kRows = 16 * RT;  // output rows of a workgroup
+  u32x4_t A[RT][4];  // slow: piece i * 64 + lane of row tile t (16 x 256 bytes); fast: k-step i of tile t of M
   u32x4_t B[NB][8];  // piece i * 64 + lane of the 32 x 256-byte token tile
 };
 
 template <int PATH>
 struct ThinLds {
   static constexpr int NB = ThinStage<PATH>::NB;
-  static constexpr int kRowA = PATH == 1 ? 16 : 0;
+  static constexpr int kRowA = PATH == 1 ? ThinStage<PATH>::kRows : 0;
   // pieces of 16 bytes, rows padded by one piece so that the 16 rows read by a
   // quarter-wave fall in different banks
   static constexpr int kA = kRowA * 17;
@@ -570,25 +585,28 @@ template <int PATH>
 __device__ __forceinline__ void thin_load(ThinStage<PATH> &st, const BArgs &a, int step0, int kend,
                                           int r0, const int (&tk)[8], const u32x4_t *zero) {
   const int lane = threadIdx.x & 63;
-  if (PATH == 0) {
-    const int q = lane >> 4, row = r0 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kg = (step0 + j) * 32 + 8 * q;
-      const bool ok = kg < kend && row < a.d_out;
-      const u32x4_t *p = static_cast<const u32x4_t *>(a.M) +
-                         ((size_t)(row / 64) * (a.k / 8) + kg / 8) * 64 + (row & 63);
-      st.A[j] = *(ok ? p : zero);
-    }
-  } else {
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
+    if (PATH == 0) {
+      const int q = lane >> 4, row = r0 + 16 * t + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pc = i * 64 + lane;
-      const int row = r0 + (pc >> 4), kg = step0 * 32 + (pc & 15) * 8;
-      const bool ok = kg < kend && row < a.d_out;
-      const u32x4_t *p =
-          reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.W) + (size_t)row * a.d + kg);
-      st.A[i] = *(ok ? p : zero);
+      for (int j = 0; j < 4; ++j) {
+        const int kg = (step0 + j) * 32 + 8 * q;
+        const bool ok = kg < kend && row < a.d_out;
+        const u32x4_t *p = static_cast<const u32x4_t *>(a.M) +
+                           ((size_t)(row / 64) * (a.k / 8) + kg / 8) * 64 + (row & 63);
+        st.A[t][j] = *(ok ? p : zero);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = i * 64 + lane;
+        const int row = r0 + 16 * t + (pc >> 4), kg = step0 * 32 + (pc & 15) * 8;
+        const bool ok = kg < kend && row < a.d_out;
+        const u32x4_t *p =
+            reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.W) + (size_t)row * a.d + kg);
+        st.A[t][i] = *(ok ? p : zero);
+      }
     }
   }
 #pragma unroll
@@ -607,17 +625,20 @@ __device__ __forceinline__ void thin_load(ThinStage<PATH> &st, const BArgs &a, i
 }
 
 template <int PATH>
-__device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t *lds, f32x4_t (&acc)[2]) {
+__device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t *lds,
+                                             f32x4_t (&acc)[ThinStage<PATH>::RT][2]) {
   constexpr int NB = ThinStage<PATH>::NB;
   constexpr int kA = ThinLds<PATH>::kA;
   const int lane = threadIdx.x & 63;
   wave_lds_fence();  // the previous stage's reads are done before it is overwritten
   if (PATH == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pc = i * 64 + lane;
-      lds[(pc >> 4) * 17 + (pc & 15)] = st.A[i];
-    }
+    for (int t = 0; t < ThinStage<PATH>::RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = i * 64 + lane;
+        lds[(16 * t + (pc >> 4)) * 17 + (pc & 15)] = st.A[t][i];
+      }
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -630,26 +651,33 @@ __device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t 
   const int r = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const u32x4_t A = PATH == 1 ? lds[r * 17 + 4 * j + q] : st.A[j];
+    u32x4_t B[2][NB];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const u32x4_t B = lds[kA + b * 32 * 17 + (16 * g + r) * 17 + 4 * j + q];
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(B), acc[g], 0, 0, 0);
-      }
+      for (int b = 0; b < NB; ++b) B[g][b] = lds[kA + b * 32 * 17 + (16 * g + r) * 17 + 4 * j + q];
+#pragma unroll
+    for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
+      const u32x4_t A = PATH == 1 ? lds[(16 * t + r) * 17 + 4 * j + q] : st.A[t][j];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(B[g][b]), acc[t][g], 0, 0, 0);
+    }
   }
 }
 
 constexpr int kThinPieces = ThinLds<0>::kPieces > ThinLds<1>::kPieces ? ThinLds<0>::kPieces : ThinLds<1>::kPieces;
-static_assert(kThinPieces * 16 >= 2 * 4 * 64 * 4, "the final sums reuse a wavefront's region");
+static_assert(kThinPieces * 16 >= ThinStage<0>::RT * 2 * 4 * 64 * 4 && kThinPieces * 16 >= ThinStage<1>::RT * 2 * 4 * 64 * 4,
+              "the final sums reuse a wavefront's region");
 
 template <int PATH>
 __device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], const int *toks,
                                            int rb) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int r0 = rb * 16;
+  const int r0 = rb * ThinStage<PATH>::kRows;
   // one zero piece per lane (a uniform fallback address becomes a branch)
   const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
   const int K = PATH == 0 ? a.kpad : a.d;
@@ -663,7 +691,11 @@ __device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinP
 #pragma unroll
   for (int i = 0; i < 8; ++i) tk[i] = toks[(i * 64 + lane) >> 4];
 
-  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc[ThinStage<PATH>::RT][2];
+#pragma unroll
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   ThinStage<PATH> sa, sb;
   thin_load<PATH>(sa, a, s0, kend, r0, tk, zero);
   for (int st = s0; st < s_end; st += 8) {
@@ -672,32 +704,34 @@ __device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinP
     thin_load<PATH>(sa, a, st + 8, kend, r0, tk, zero);
     thin_consume<PATH>(sb, lds[wave], acc);
   }
-  // partial sums of the four K quarters, through each wavefront's own region
+  // partial sums of the four K quarters, through each wavefront's own region:
+  // element ((t * 2 + g) * 4 + i) * 64 + lane
   wave_lds_fence();
   float *red = reinterpret_cast<float *>(lds[wave]);
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(g * 4 + i) * 64 + lane] = acc[g][i];
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((t * 2 + g) * 4 + i) * 64 + lane] = acc[t][g][i];
   __syncthreads();
   uint16_t *Y = static_cast<uint16_t *>(a.y);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = tid + h * kBlock;  // (group, element, lane)
-    const int g = e >> 8, i = (e >> 6) & 3, l = e & 63;
+  for (int h = 0; h < 2 * ThinStage<PATH>::RT; ++h) {
+    const int e = tid + h * kBlock;  // (tile, group, element, lane)
+    const int t = e >> 9, g = (e >> 8) & 1, i = (e >> 6) & 3, l = e & 63;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float *>(lds[w])[(g * 4 + i) * 64 + l];
-    const int t = toks[g * 16 + (l & 15)];
-    const int r = r0 + 4 * (l >> 4) + i;
-    if (t >= 0 && r < a.d_out) Y[(size_t)t * a.d_out + r] = f2bf(v);
+    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float *>(lds[w])[e];
+    const int tok = toks[g * 16 + (l & 15)];
+    const int r = r0 + 16 * t + 4 * (l >> 4) + i;
+    if (tok >= 0 && r < a.d_out) Y[(size_t)tok * a.d_out + r] = f2bf(v);
   }
   __syncthreads();  // every wavefront's region is free again
 }
 
-// Both paths in one launch: the workgroups walk the 16-row blocks of every
-// path with 1 to kThin tokens; with no such path they leave after the
-// compaction.
+// Both paths in one launch: the workgroups walk the row blocks of every path
+// with 1 to kThin tokens; with no such path they leave after the compaction.
 __global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
   __shared__ u32x4_t lds[kWaves][kThinPieces];
   __shared__ int16_t idx[kMaxBatch];
@@ -711,9 +745,8 @@ __global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
     toks[p][i] = i < c ? idx[(p == 0 ? 0 : cnt.x) + i] : -1;
   }
   __syncthreads();
-  const int rbs = (a.d_out + 15) / 16;
-  const int nf = (cnt.x > 0 && cnt.x <= kThin) ? rbs : 0;
-  const int ns = (cnt.y > 0 && cnt.y <= kThin) ? rbs : 0;
+  const int nf = (cnt.x > 0 && cnt.x <= kThin) ? (a.d_out + ThinStage<0>::kRows - 1) / ThinStage<0>::kRows : 0;
+  const int ns = (cnt.y > 0 && cnt.y <= kThin) ? (a.d_out + ThinStage<1>::kRows - 1) / ThinStage<1>::kRows : 0;
   for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
     if (it < nf)
       bthin_path<0>(a, lds, toks[0], it);
@@ -806,7 +839,7 @@ hipError_t launch_batched(const BArgs &a, hipStream_t s) {
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, bthin_kernel, kBlock, 0) != hipSuccess || occ < 1)
     occ = 1;
-  const int tiles = (a.d_out + 63) / 64, rbs = (a.d_out + 15) / 16;
+  const int tiles = (a.d_out + 63) / 64, rbs = (a.d_out + 15) / 16;  // rbs: row blocks of the larger count
   hipLaunchKernelGGL(bout_kernel, dim3(cus < 2 * tiles ? cus : 2 * tiles), dim3(kOutThreads), 0, s, a);
   hipLaunchKernelGGL(bthin_kernel, dim3(occ * cus < 2 * rbs ? occ * cus : 2 * rbs), dim3(kBlock), 0, s, a);
   return hipGetLastError();
