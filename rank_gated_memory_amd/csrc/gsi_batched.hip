@@ -175,15 +175,20 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
     const bool ok = r < rows && j < a.k;
     vv[q] = *(ok ? reinterpret_cast<const u32x4_t *>(V + (size_t)(i0 + r) * a.k + j) : zero);
   }
-  // stage V[i0 + r][j0 + c] as Vt[c][r] (zero outside the map)
+  // stage V[i0 + r][j0 + c] as Vt[c][r ^ 8 (c / 8)] (zero outside the map).
+  // A wavefront's stores cover 8 rows x 8 column groups; the row pitch is a
+  // multiple of 128 bytes, so unswizzled the eight column groups would share
+  // banks.  XOR-ing r with 8 (c / 8) spreads them and keeps every aligned
+  // group of 8 rows contiguous for the 16-byte operand reads.
 #pragma unroll
   for (int q = 0; q < VL; ++q) {
     const int v = tid + q * kBlock;
     const int r = v >> 3, cg = v & 7;
+    const int rs = r ^ (8 * cg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Vt[cg * 8 + 2 * e][r] = (uint16_t)(vv[q][e] & 0xffffu);
-      Vt[cg * 8 + 2 * e + 1][r] = (uint16_t)(vv[q][e] >> 16);
+      Vt[cg * 8 + 2 * e][rs] = (uint16_t)(vv[q][e] & 0xffffu);
+      Vt[cg * 8 + 2 * e + 1][rs] = (uint16_t)(vv[q][e] >> 16);
     }
   }
   __syncthreads();
@@ -206,7 +211,8 @@ __global__ void __launch_bounds__(kBlock) bproj_kernel(BArgs a) {
     const bf16x8_t A = as_bf16x8(xv[q]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Vt[c * 16 + (lane & 15)][q * 32 + kq]);
+      const int col = c * 16 + (lane & 15);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Vt[col][(q * 32 + kq) ^ (8 * (col >> 3))]);
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(b), acc[c], 0, 0, 0);
     }
   }
