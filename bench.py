@@ -334,10 +334,26 @@ def bench_batched(args):
     grid = [(k, frac) for k in (64, 256, 512) for frac in (0.0, 0.1, 0.5, 1.0)]
     if args.cells:
         grid = [(int(c.split(":")[0]), float(c.split(":")[1])) for c in args.cells.split(",")]
+    prep = []
     for k, frac in grid:
         mi = synth.config5(k, frac, device=dev, w_device=dev)
         m = gsi.Map(mi.W, mi.V)
         gsi.gsi_prepare(m)
+        if not any(p["k"] == k for p in prep):
+            # the image M = W V_k (once per map, off the per-token path)
+            reps = 5
+            torch.cuda.synchronize()
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record()
+            for _ in range(reps):
+                gsi.gsi_prepare(m)
+            p1.record()
+            torch.cuda.synchronize()
+            pus = p0.elapsed_time(p1) / reps * 1e3
+            pfl = 2.0 * mi.d * mi.d_out * k
+            prep.append({"k": k, "us_per_map": pus, "tflops": pfl / pus / 1e6,
+                         "mfma_frac": pfl / pus / 1e6 / PEAK_BF16_TFLOPS})
+            log(f"prepare M (d={mi.d}, d_out={mi.d_out}, k={k}): {pus:.1f} us, {pfl / pus / 1e6:.0f} TFLOP/s")
         T = mi.X.shape[0]
         y = torch.empty(T, mi.d_out, dtype=torch.bfloat16, device=dev)
         rho = torch.empty(T, device=dev)
@@ -371,7 +387,7 @@ def bench_batched(args):
         "warmup": args.warmup, "ms_per_step": head["us_per_call"] / 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "batched-t256: T=256, d=4096, d_out=16384, value at k=256, 10% slow",
-                   "cells": cells},
+                   "cells": cells, "prepare": prep},
     }), flush=True)
 
 

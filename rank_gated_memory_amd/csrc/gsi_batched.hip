@@ -790,8 +790,10 @@ __global__ void __launch_bounds__(kBlock)
       uint4 u = make_uint4(0u, 0u, 0u, 0u);
       if (r < rows && j < k) u = *reinterpret_cast<const uint4 *>(V + (size_t)(i0 + r) * k + j);
       const uint16_t *h = reinterpret_cast<const uint16_t *>(&u);
+      // swizzled by column group as in the projection GEMM (bank spread)
+      const int rs = r ^ (8 * cg);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[cg * 8 + e][r] = h[e];
+      for (int e = 0; e < 8; ++e) Vt[cg * 8 + e][rs] = h[e];
     }
     __syncthreads();
     for (int kk = 0; kk < rows; kk += 32) {
@@ -800,7 +802,8 @@ __global__ void __launch_bounds__(kBlock)
       const bf16x8_t A = as_bf16x8(u);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 b = *reinterpret_cast<const uint4 *>(&Vt[c * 16 + (lane & 15)][kk + kq]);
+        const int col = c * 16 + (lane & 15);
+        const uint4 b = *reinterpret_cast<const uint4 *>(&Vt[col][(kk + kq) ^ (8 * (col >> 3))]);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_bf16x8(b), acc[c], 0, 0, 0);
       }
     }
