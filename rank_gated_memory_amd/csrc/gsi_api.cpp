@@ -701,7 +701,7 @@ static gsi_status check_calib(const gsi_calib *c) {
 
 size_t gsi_calibrate_workspace(const gsi_calib *c) {
   if (check_calib(c) != GSI_OK) return 0;
-  return calib_ws_bytes(c->n, c->d, c->k);
+  return calib_ws_bytes(c->n, c->d, c->k, c->dtype);
 }
 
 size_t gsi_calibrate_status_offset(void) { return 0; }
@@ -711,7 +711,7 @@ gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *st
   if (s != GSI_OK) return s;
   if (!ws) return GSI_E_NULL;
   if (!aligned(ws, 256)) return GSI_E_ALIGN;
-  if (ws_bytes < calib_ws_bytes(c->n, c->d, c->k)) return GSI_E_WORKSPACE;
+  if (ws_bytes < calib_ws_bytes(c->n, c->d, c->k, c->dtype)) return GSI_E_WORKSPACE;
   CalibArgs a{};
   a.n = c->n;
   a.d = c->d;
@@ -722,26 +722,26 @@ gsi_status gsi_calibrate(const gsi_calib *c, void *ws, size_t ws_bytes, void *st
   a.V0 = c->V0;
   a.V = c->V;
   char *w = static_cast<char *>(ws);
-  auto al = [](uint64_t v) { return (v + 255) / 256 * 256; };
-  const uint64_t dk = (uint64_t)c->d * c->k, nk = (uint64_t)c->n * c->k, kk = (uint64_t)c->k * c->k;
-  uint64_t off = 0;
-  a.status = reinterpret_cast<uint32_t *>(w + off);
-  off += al(256);
-  a.vw = reinterpret_cast<float *>(w + off);
-  off += al(dk * 4);
-  a.z = reinterpret_cast<float *>(w + off);
-  off += al(nk * 4);
-  a.y = reinterpret_cast<double *>(w + off);
-  off += al(dk * 8);
-  a.y2 = reinterpret_cast<double *>(w + off);
-  off += al(dk * 8);
-  a.g = reinterpret_cast<double *>(w + off);
-  off += al(kk * 8);
-  a.r = reinterpret_cast<double *>(w + off);
-  off += al(kk * 8);
-  a.dinv = reinterpret_cast<double *>(w + off);
-  off += al((uint64_t)(c->k + 63) / 64 * 64 * 64 * 8);
-  a.gpart = reinterpret_cast<double *>(w + off);
+  const CalibLayout L = calib_layout(c->n, c->d, c->k, c->dtype);
+  a.status = reinterpret_cast<uint32_t *>(w + L.status);
+  a.mfma = L.mfma ? 1 : 0;
+  a.dp = (int32_t)L.dp;
+  a.np = (int32_t)L.np;
+  if (L.mfma) {
+    a.zeros = w + L.zeros;
+    a.vt3 = reinterpret_cast<uint16_t *>(w + L.vt3);
+    a.zt3 = reinterpret_cast<uint16_t *>(w + L.zt3);
+    a.at = reinterpret_cast<uint16_t *>(w + L.at);
+  } else {
+    a.vw = reinterpret_cast<float *>(w + L.vw);
+    a.z = reinterpret_cast<float *>(w + L.z);
+  }
+  a.y = reinterpret_cast<double *>(w + L.y);
+  a.y2 = reinterpret_cast<double *>(w + L.y2);
+  a.g = reinterpret_cast<double *>(w + L.g);
+  a.r = reinterpret_cast<double *>(w + L.r);
+  a.dinv = reinterpret_cast<double *>(w + L.dinv);
+  a.gpart = reinterpret_cast<double *>(w + L.gpart);
   const hipError_t e = launch_calibrate(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }

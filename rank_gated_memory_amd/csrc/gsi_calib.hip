@@ -98,6 +98,175 @@ __global__ void __launch_bounds__(kCB) gemm_kernel(const TX *__restrict__ X, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core products for bf16 samples.  Every product with A has one bf16
+// operand (A or A^T) and one fp32 operand (the iterate V, or Z = A V).  The
+// fp32 operand is carried as three bf16 parts hi + mid + lo (each the
+// rounding of what the previous ones leave, so together they hold its 24
+// significant bits), and the product is the sum of the three bf16 products
+// accumulated in fp32 by v_mfma_f32_32x32x16_bf16: the same fp32-accumulated
+// product as the FMA tiles, at the matrix cores' rate.  Both operands are
+// stored along K (rows of 16-byte pieces), padded with zeros to 64.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// v = hi + mid + lo to about 2^-24 |v| (each part rounds the remainder).
+__device__ __forceinline__ void split3(float v, uint16_t *p) {
+  const uint16_t hi = to_bf16(v);
+  const float r1 = v - from_bf16(hi);
+  const uint16_t mid = to_bf16(r1);
+  p[0] = hi;
+  p[1] = mid;
+  p[2] = to_bf16(r1 - from_bf16(mid));
+}
+
+// At[i][s] = A[s][i] for s < n, zero for n <= s < np (64 x 64 tiles through
+// LDS); workgroup (0, 0) also clears the 256-byte zero block.
+__global__ void __launch_bounds__(kCB) transpose_pad_kernel(const uint16_t *__restrict__ A, uint16_t *__restrict__ At,
+                                                            uint32_t *zeros, int n, int d, int np) {
+  __shared__ uint16_t T[64][66];
+  const int tid = threadIdx.x;
+  const int s0 = blockIdx.x * 64, i0 = blockIdx.y * 64;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 64) zeros[tid] = 0u;
+  for (int e = tid; e < 64 * 64; e += kCB) {
+    const int s = e / 64, i = e % 64;
+    T[s][i] = (s0 + s < n && i0 + i < d) ? A[(size_t)(s0 + s) * d + i0 + i] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += kCB) {
+    const int i = e / 64, s = e % 64;
+    if (i0 + i < d) At[(size_t)(i0 + i) * np + s0 + s] = T[s][i];
+  }
+}
+
+// parts[p][j][i] = part p of (float)Y[i][j] for i < d, zero for d <= i < dp
+// (Y [d][k], 64 x 64 tiles through LDS).
+template <typename TY>
+__global__ void __launch_bounds__(kCB) split_t_kernel(const TY *__restrict__ Y, uint16_t *__restrict__ parts, int d,
+                                                      int k, int dp) {
+  __shared__ float T[64][65];
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  for (int e = tid; e < 64 * 64; e += kCB) {
+    const int i = e / 64, j = e % 64;
+    T[i][j] = (i0 + i < d && j0 + j < k) ? (float)ld(Y, (size_t)(i0 + i) * k + j0 + j) : 0.f;
+  }
+  __syncthreads();
+  const size_t ps = (size_t)k * dp;
+  for (int e = tid; e < 64 * 64; e += kCB) {
+    const int j = e / 64, i = e % 64;
+    if (j0 + j < k) {
+      uint16_t p[3];
+      split3(T[i][j], p);
+      const size_t o = (size_t)(j0 + j) * dp + i0 + i;
+      parts[o] = p[0];
+      parts[ps + o] = p[1];
+      parts[2 * ps + o] = p[2];
+    }
+  }
+}
+
+// C[i][j] = sum_t P[i][t] Q[j][t], t < K: P rows i < M (NP parts, part
+// stride sp), Q rows j < N (NQ parts, part stride sq), rows along K with
+// strides ldp, ldq (multiples of 8).  OUT 0: C as three bf16 parts
+// [3][M][ldc] (part stride sc), columns up to ldc written (zero past N);
+// OUT 1: C fp64 [M][ldc], columns below N.
+struct MGemm {
+  const uint16_t *P, *Q;
+  void *C;
+  const u32x4_t *zero;
+  int M, N, K, ldp, ldq, ldc;
+  size_t sp, sq, sc;
+};
+
+constexpr int kMRow = 9;  // 16-byte pieces per staged 64-wide K row, padded (bank spread)
+
+// 64 x 64 tile of C per workgroup, four wavefronts of 32 x 32; K in chunks of
+// 64 through double-buffered LDS, the next chunk loaded into registers while
+// the current one is multiplied.  Pieces outside the operands read the zero
+// block.
+template <int NP, int NQ, int OUT>
+__global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
+  __shared__ u32x4_t Ps[2][NP][64 * kMRow];
+  __shared__ u32x4_t Qs[2][NQ][64 * kMRow];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int wi = wave >> 1, wj = wave & 1;
+  const u32x4_t *zero = g.zero + (lane & 15);
+  u32x4_t pr[NP][2], qr[NQ][2];
+  auto load = [&](int kk) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = tid + h * kCB, r = v >> 3, c = kk + (v & 7) * 8;
+      const bool kok = c < g.K;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        pr[p][h] = *((kok && i0 + r < g.M)
+                         ? reinterpret_cast<const u32x4_t *>(g.P + p * g.sp + (size_t)(i0 + r) * g.ldp + c)
+                         : zero);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        qr[q][h] = *((kok && j0 + r < g.N)
+                         ? reinterpret_cast<const u32x4_t *>(g.Q + q * g.sq + (size_t)(j0 + r) * g.ldq + c)
+                         : zero);
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  const int nch = (g.K + 63) / 64;
+  load(0);
+  for (int ch = 0; ch < nch; ++ch) {
+    const int b = ch & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = tid + h * kCB, r = v >> 3, c = v & 7;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) Ps[b][p][r * kMRow + c] = pr[p][h];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) Qs[b][q][r * kMRow + c] = qr[q][h];
+    }
+    if (ch + 1 < nch) load((ch + 1) * 64);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int pc = ks * 2 + (lane >> 5);
+      bf16x8_t a[NP], bq[NQ];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) a[p] = __builtin_bit_cast(bf16x8_t, Ps[b][p][(32 * wi + (lane & 31)) * kMRow + pc]);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) bq[q] = __builtin_bit_cast(bf16x8_t, Qs[b][q][(32 * wj + (lane & 31)) * kMRow + pc]);
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p], bq[q], acc, 0, 0, 0);
+    }
+  }
+  // accumulator e of lane l: C[8 (e / 4) + 4 (l / 32) + e % 4][l % 32] of the wavefront's block
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int i = i0 + 32 * wi + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+    const int j = j0 + 32 * wj + (lane & 31);
+    if (i >= g.M) continue;
+    if (OUT == 0) {
+      if (j < g.ldc) {
+        uint16_t pt[3];
+        split3(acc[e], pt);
+        uint16_t *C = static_cast<uint16_t *>(g.C) + (size_t)i * g.ldc + j;
+        C[0] = pt[0];
+        C[g.sc] = pt[1];
+        C[2 * g.sc] = pt[2];
+      }
+    } else if (j < g.N) {
+      static_cast<double *>(g.C)[(size_t)i * g.ldc + j] = (double)acc[e];
+    }
+  }
+}
+
 // Blocked fp64 factorisation, 64 x 64 tiles in LDS (rows padded to 65).
 constexpr int kNb = 64;
 constexpr int kLd = kNb + 1;
@@ -488,16 +657,70 @@ void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv,
   hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
 
+// One sweep's products on the matrix cores: Z^T = V^T A^T (as three bf16
+// parts), then Y = A^T Z (fp64).
+void mfma_products(const CalibArgs &c, hipStream_t s) {
+  MGemm g1{};
+  g1.P = c.vt3;
+  g1.Q = static_cast<const uint16_t *>(c.A);
+  g1.C = c.zt3;
+  g1.zero = static_cast<const u32x4_t *>(c.zeros);
+  g1.M = c.k;
+  g1.N = c.n;
+  g1.K = c.d;
+  g1.ldp = c.dp;
+  g1.ldq = c.d;
+  g1.ldc = c.np;
+  g1.sp = (size_t)c.k * c.dp;
+  g1.sc = (size_t)c.k * c.np;
+  hipLaunchKernelGGL((mgemm_kernel<3, 1, 0>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
+  MGemm g2{};
+  g2.P = c.at;
+  g2.Q = c.zt3;
+  g2.C = c.y;
+  g2.zero = g1.zero;
+  g2.M = c.d;
+  g2.N = c.k;
+  g2.K = c.np;
+  g2.ldp = c.np;
+  g2.ldq = c.np;
+  g2.ldc = c.k;
+  g2.sq = (size_t)c.k * c.np;
+  hipLaunchKernelGGL((mgemm_kernel<1, 3, 1>), dim3((c.d + 63) / 64, (c.k + 63) / 64), dim3(kCB), 0, s, g2);
+}
+
+template <typename TY>
+void split_t(const TY *Y, const CalibArgs &c, hipStream_t s) {
+  hipLaunchKernelGGL((split_t_kernel<TY>), dim3(c.dp / 64, (c.k + 63) / 64), dim3(kCB), 0, s, Y, c.vt3, c.d, c.k,
+                     c.dp);
+}
+
 template <typename T>
 hipError_t run(const CalibArgs &c, hipStream_t s) {
   const T *A = static_cast<const T *>(c.A);
-  convert(static_cast<const T *>(c.V0), c.vw, (size_t)c.d * c.k, s);
+  if (c.mfma) {
+    hipLaunchKernelGGL(transpose_pad_kernel, dim3(c.np / 64, (c.d + 63) / 64), dim3(kCB), 0, s,
+                       reinterpret_cast<const uint16_t *>(A), c.at,
+                       static_cast<uint32_t *>(const_cast<void *>(c.zeros)), c.n, c.d, c.np);
+    split_t(static_cast<const T *>(c.V0), c, s);
+  } else {
+    convert(static_cast<const T *>(c.V0), c.vw, (size_t)c.d * c.k, s);
+  }
   for (int it = 0; it < c.iters; ++it) {
-    gemm<T, float, float, float, false>(A, c.vw, c.z, c.n, c.k, c.d, s);    // Z = A V      [n][k]
-    gemm<T, float, double, float, true>(A, c.z, c.y, c.d, c.k, c.n, s);     // Y = A^T Z    [d][k]
+    if (c.mfma) {
+      mfma_products(c, s);
+    } else {
+      gemm<T, float, float, float, false>(A, c.vw, c.z, c.n, c.k, c.d, s);    // Z = A V      [n][k]
+      gemm<T, float, double, float, true>(A, c.z, c.y, c.d, c.k, c.n, s);     // Y = A^T Z    [d][k]
+    }
     cholqr_pass(c.y, c.y2, c.g, c.r, c.dinv, c.gpart, c.d, c.k, c.status, s);  // y2 = Q(y)
     cholqr_pass(c.y2, c.y, c.g, c.r, c.dinv, c.gpart, c.d, c.k, c.status, s);  // y = Q(y2): orthogonal to rounding
-    if (it + 1 < c.iters) convert(c.y, c.vw, (size_t)c.d * c.k, s);
+    if (it + 1 < c.iters) {
+      if (c.mfma)
+        split_t(c.y, c, s);
+      else
+        convert(c.y, c.vw, (size_t)c.d * c.k, s);
+    }
   }
   if (c.iters == 0)
     convert(static_cast<const T *>(c.V0), static_cast<T *>(c.V), (size_t)c.d * c.k, s);
