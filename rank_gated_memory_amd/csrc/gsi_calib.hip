@@ -366,140 +366,151 @@ __device__ __forceinline__ void acc_to_tile(double (*T)[kLd], const double (&acc
     for (int y = 0; y < 4; ++y) T[ti + x][tj + y] = acc[x][y];
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Unblocked Cholesky (upper) of the 64 x 64 tile S on wavefront 0, without
+// barriers: lane c holds column c in registers, and step j takes the pivot
+// S[j][j] and the multipliers S[j][i] from the lanes that hold them.  Only
+// upper entries ever cross lanes, so whatever the lower part of a column
+// turns into stays in its lane; it is written back as zero.
+__device__ void chol_tile_wave(double (*S)[kLd], const double *diag0, int *bad) {
+  const int c = threadIdx.x;
+  double col[kNb];
+#pragma unroll
+  for (int r = 0; r < kNb; ++r) col[r] = S[r][c];
+  int badj = 0;
+#pragma unroll
+  for (int j = 0; j < kNb; ++j) {
+    double p = readlane_f64(col[j], j);
+    if (!(p > 1e-12 * diag0[j])) {
+      badj = 1;
+      p = 1.0;
+    }
+    const double rjj = sqrt(p);
+    if (c == j)
+      col[j] = rjj;
+    else if (c > j)
+      col[j] = col[j] / rjj;
+#pragma unroll
+    for (int i = j + 1; i < kNb; ++i) col[i] = fma(-readlane_f64(col[j], i), col[j], col[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < kNb; ++r) S[r][c] = r <= c ? col[r] : 0.0;
+  if (c == 0 && badj) *bad = 1;
+}
+
 // R (upper, [k][k]) with G = R^T R, by the left-looking blocked Cholesky
-// (one workgroup; 64 x 64 blocks): for block row J,
-//     S = G_JJ - sum_{I<J} R_IJ^T R_IJ,   R_JJ = chol(S)      (in LDS)
-//     R_JL = R_JJ^-T (G_JL - sum_{I<J} R_IJ^T R_IL)  for L > J.
+// (64 x 64 blocks), one block row J at a time in two launches:
+//     chol_diag_kernel (one workgroup):
+//         S = G_JJ - sum_{I<J} R_IJ^T R_IJ,   R_JJ = chol(S)      (in LDS)
+//     chol_panel_kernel (one workgroup per block L > J):
+//         R_JL = R_JJ^-T (G_JL - sum_{I<J} R_IJ^T R_IL)
 // The inverse of each diagonal block goes to Dinv[J] (64 x 64, upper): the
-// solve for Q = Y R^-1 needs only those.  A pivot that keeps at most 1e-12
-// of its column's squared norm (G_jj) means the block is numerically rank
-// deficient (the fp32 products leave ~1e-14 there): status <- 1.
-__global__ void __launch_bounds__(kCB) chol_kernel(const double *G, double *R, double *Dinv, int k,
-                                                   uint32_t *status) {
-  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
+// panel and the solve for Q = Y R^-1 need only those.  A pivot that keeps
+// at most 1e-12 of its column's squared norm (G_jj) means the block is
+// numerically rank deficient (the fp32 products leave ~1e-14 there):
+// status <- 1.
+__global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double *R, double *Dinv, int k, int J,
+                                                        uint32_t *status) {
+  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd];
   __shared__ double diag0[kNb];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int ti = tile_ti(), tj = tile_tj();
-  const int nbk = (k + kNb - 1) / kNb;
+  const int c0 = J * kNb, nJ = min(kNb, k - c0);
   if (tid == 0) s_bad = 0;
-  for (int J = 0; J < nbk; ++J) {
-    const int c0 = J * kNb, nJ = min(kNb, k - c0);
+  load_tile(S, G, k, c0, c0, nJ, nJ);
+  __syncthreads();
+  if (tid < kNb) diag0[tid] = S[tid][tid];
+  double acc[4][4];
+  acc_from_tile(acc, S);
+  for (int I = 0; I < J; ++I) {
     __syncthreads();
-    load_tile(S, G, k, c0, c0, nJ, nJ);
+    load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
     __syncthreads();
-    if (tid < kNb) diag0[tid] = S[tid][tid];
-    double acc[4][4];
-    acc_from_tile(acc, S);
-    for (int I = 0; I < J; ++I) {
-      __syncthreads();
-      load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
-      __syncthreads();
-      sub_atb(acc, Ta, Ta);
-    }
-    __syncthreads();
-    acc_to_tile(S, acc);
-    __syncthreads();
-    // unblocked Cholesky of S (upper)
-    for (int j = 0; j < nJ; ++j) {
-      if (tid == 0) {
-        double p = S[j][j];
-        if (!(p > 1e-12 * diag0[j])) {
-          s_bad = 1;
-          p = 1.0;
-        }
-        S[j][j] = sqrt(p);
-      }
-      __syncthreads();
-      const double rjj = S[j][j];
-      for (int l = j + 1 + tid; l < nJ; l += kCB) S[j][l] /= rjj;
-      __syncthreads();
-      // trailing update of the upper part: thread (a, b) takes rows j+1+a,
-      // j+1+a+16, ... and columns j+1+b, j+1+b+16, ...
-      const int a0 = tid >> 4, b0 = tid & 15;
-      for (int i = j + 1 + a0; i < nJ; i += 16) {
-        const double sji = S[j][i];
-        for (int l = j + 1 + b0; l < nJ; l += 16)
-          if (l >= i) S[i][l] = fma(-sji, S[j][l], S[i][l]);
-      }
-      __syncthreads();
-    }
-    // strictly lower part and the padding of a partial block: zero, with an
-    // identity diagonal so that the inverse is defined
-    for (int e = tid; e < kNb * kNb; e += kCB) {
-      const int r = e / kNb, c = e % kNb;
-      if (r > c || c >= nJ) S[r][c] = (r == c) ? 1.0 : 0.0;
-    }
-    __syncthreads();
-    // Di = S^-1 (upper): row i on thread i (rows are independent), read S only
-    if (tid < kNb) {
-      const int i = tid;
-      for (int j = 0; j < kNb; ++j) {
-        double x = 0.0;
-        if (j == i) {
-          x = 1.0 / S[j][j];
-        } else if (j > i) {
-          // four partial sums: the loads run ahead of the dependent adds
-          double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-          int l = i;
-          for (; l + 4 <= j; l += 4) {
-            s0 = fma(Di[i][l], S[l][j], s0);
-            s1 = fma(Di[i][l + 1], S[l + 1][j], s1);
-            s2 = fma(Di[i][l + 2], S[l + 2][j], s2);
-            s3 = fma(Di[i][l + 3], S[l + 3][j], s3);
-          }
-          for (; l < j; ++l) s0 = fma(Di[i][l], S[l][j], s0);
-          x = -((s0 + s1) + (s2 + s3)) / S[j][j];
-        }
-        Di[i][j] = x;
-      }
-    }
-    __syncthreads();
-    // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
-    for (int e = tid; e < kNb * kNb; e += kCB) {
-      const int r = e / kNb, c = e % kNb;
-      if (r < nJ && c < nJ) R[(size_t)(c0 + r) * k + c0 + c] = S[r][c];
-      Dinv[(size_t)J * kNb * kNb + e] = (r < nJ && c < nJ) ? Di[r][c] : 0.0;
-    }
-    // the block row J right of the diagonal
-    for (int L = J + 1; L < nbk; ++L) {
-      const int l0 = L * kNb, nL = min(kNb, k - l0);
-      __syncthreads();
-      load_tile(S, G, k, c0, l0, nJ, nL);
-      __syncthreads();
-      acc_from_tile(acc, S);
-      for (int I = 0; I < J; ++I) {
-        __syncthreads();
-        load_tiles2(Ta, R, k, I * kNb, c0, kNb, nJ, Tb, R, k, I * kNb, l0, kNb, nL);
-        __syncthreads();
-        sub_atb(acc, Ta, Tb);
-      }
-      __syncthreads();
-      acc_to_tile(S, acc);
-      __syncthreads();
-      // R_JL = Di^T S: out[r][c] = sum_{i <= r} Di[i][r] S[i][c]
-      double out[4][4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
-      for (int i = 0; i < kNb; ++i) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) out[x][y] = fma(Di[i][ti + x], S[i][tj + y], out[x][y]);
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          if (ti + x < nJ && tj + y < nL) R[(size_t)(c0 + ti + x) * k + l0 + tj + y] = out[x][y];
-    }
-    // R's block row J is read back by later block rows: its stores land first
-    __builtin_amdgcn_s_waitcnt(0);
+    sub_atb(acc, Ta, Ta);
   }
   __syncthreads();
+  acc_to_tile(S, acc);
+  __syncthreads();
+  // a partial block is padded with the identity, so that its factor is
+  // chol(S) beside an identity block and every step below is uniform
+  for (int e = tid; e < kNb * kNb; e += kCB) {
+    const int r = e / kNb, c = e % kNb;
+    if (r >= nJ || c >= nJ) S[r][c] = (r == c) ? 1.0 : 0.0;
+  }
+  if (tid < kNb && tid >= nJ) diag0[tid] = 1.0;
+  __syncthreads();
+  if (tid < kNb) chol_tile_wave(S, diag0, &s_bad);
+  __syncthreads();
+  // Di = S^-1 (upper) on wavefront 0: lane c solves S x = e_c by back
+  // substitution in registers (x[r] = 0 below the diagonal comes out by
+  // itself), the S[r][l] it needs read as LDS broadcasts
+  if (tid < kNb) {
+    const int c = tid;
+    double x[kNb];
+#pragma unroll
+    for (int r = kNb - 1; r >= 0; --r) {
+      double t = r == c ? 1.0 : 0.0;
+#pragma unroll
+      for (int l = r + 1; l < kNb; ++l) t = fma(-S[r][l], x[l], t);
+      x[r] = t / S[r][r];
+    }
+#pragma unroll
+    for (int r = 0; r < kNb; ++r) Di[r][c] = x[r];
+  }
+  __syncthreads();
+  // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
+  for (int e = tid; e < kNb * kNb; e += kCB) {
+    const int r = e / kNb, c = e % kNb;
+    if (r < nJ && c < nJ) R[(size_t)(c0 + r) * k + c0 + c] = S[r][c];
+    Dinv[(size_t)J * kNb * kNb + e] = (r < nJ && c < nJ) ? Di[r][c] : 0.0;
+  }
   if (tid == 0 && s_bad) *status = 1u;
+}
+
+__global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double *R, const double *Dinv, int k,
+                                                         int J) {
+  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
+  const int tid = threadIdx.x;
+  const int ti = tile_ti(), tj = tile_tj();
+  const int c0 = J * kNb, nJ = min(kNb, k - c0);
+  const int L = J + 1 + blockIdx.x;
+  const int l0 = L * kNb, nL = min(kNb, k - l0);
+  load_tiles2(S, G, k, c0, l0, nJ, nL, Di, Dinv + (size_t)J * kNb * kNb, kNb, 0, 0, kNb, kNb);
+  __syncthreads();
+  double acc[4][4];
+  acc_from_tile(acc, S);
+  for (int I = 0; I < J; ++I) {
+    __syncthreads();
+    load_tiles2(Ta, R, k, I * kNb, c0, kNb, nJ, Tb, R, k, I * kNb, l0, kNb, nL);
+    __syncthreads();
+    sub_atb(acc, Ta, Tb);
+  }
+  __syncthreads();
+  acc_to_tile(S, acc);
+  __syncthreads();
+  // R_JL = Di^T S: out[r][c] = sum_{i <= r} Di[i][r] S[i][c]
+  double out[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
+  for (int i = 0; i < kNb; ++i) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) out[x][y] = fma(Di[i][ti + x], S[i][tj + y], out[x][y]);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+      if (ti + x < nJ && tj + y < nL) R[(size_t)(c0 + ti + x) * k + l0 + tj + y] = out[x][y];
 }
 
 // Q = Y R^-1 ([d][k]) by a blocked forward substitution over the block
@@ -653,7 +664,11 @@ void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv,
   int rb = (int)(((size_t)k * k + kCB - 1) / kCB);
   if (rb > 2048) rb = 2048;
   hipLaunchKernelGGL(gram_reduce_kernel, dim3(rb), dim3(kCB), 0, s, P, G, k, S);
-  hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, status);
+  const int nbk = (k + kNb - 1) / kNb;
+  for (int J = 0; J < nbk; ++J) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, J, status);
+    if (J + 1 < nbk) hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - J - 1), dim3(kCB), 0, s, G, R, Dinv, k, J);
+  }
   hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
 
