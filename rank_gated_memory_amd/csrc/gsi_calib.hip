@@ -447,18 +447,20 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
   __syncthreads();
   if (tid < kNb) chol_tile_wave(S, diag0, &s_bad);
   __syncthreads();
-  // Di = S^-1 (upper) on wavefront 0: lane c solves S x = e_c by back
-  // substitution in registers (x[r] = 0 below the diagonal comes out by
-  // itself), the S[r][l] it needs read as LDS broadcasts
+  // Di = S^-1 (upper) on wavefront 0: lane c solves S x = e_c in registers
+  // by the column sweep of back substitution (x[r] /= S[r][r], then
+  // x[i] -= S[i][r] x[r] for every i < r: independent updates, whose S[i][r]
+  // are LDS broadcasts that can be read ahead).  Rows below c stay zero.
   if (tid < kNb) {
     const int c = tid;
     double x[kNb];
 #pragma unroll
-    for (int r = kNb - 1; r >= 0; --r) {
-      double t = r == c ? 1.0 : 0.0;
+    for (int r = 0; r < kNb; ++r) x[r] = r == c ? 1.0 : 0.0;
 #pragma unroll
-      for (int l = r + 1; l < kNb; ++l) t = fma(-S[r][l], x[l], t);
-      x[r] = t / S[r][r];
+    for (int r = kNb - 1; r >= 0; --r) {
+      x[r] = x[r] / S[r][r];
+#pragma unroll
+      for (int i = 0; i < r; ++i) x[i] = fma(-S[i][r], x[r], x[i]);
     }
 #pragma unroll
     for (int r = 0; r < kNb; ++r) Di[r][c] = x[r];
