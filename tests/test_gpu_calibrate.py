@@ -38,6 +38,11 @@ def samples(d, k, n, key, gap=4.0, tail=64, frame=None):
     (1024, 256, 16, torch.float32, 3, 2e-4),
     (600, 520, 40, torch.float32, 1, 2e-4),
     (2048, 4096, 256, torch.bfloat16, 3, 2e-2),
+    # bf16 samples, d a multiple of 8 (matrix-core products) with n, d and k
+    # all off the 64-wide tiles, so every zero-padded edge is used
+    (600, 520, 40, torch.bfloat16, 2, 2e-2),
+    # bf16 samples with d not a multiple of 8 (fp32 FMA products)
+    (300, 260, 24, torch.bfloat16, 2, 2e-2),
 ])
 def test_calibrate_matches_oracle_iteration(n, d, k, dtype, iters, tol):
     A, _ = samples(d, k, n, (100, d, k))
