@@ -8,8 +8,9 @@
 //
 //   bproj_kernel : split-K GEMM G = X V_k with v_mfma_f32_16x16x32_bf16 and the
 //                  per-token ||x||^2; a V_k chunk is staged in LDS transposed
-//                  ([col][k]) so each lane reads its 8-element K slice as one
-//                  16-byte LDS read.  Partials [S][T][k] fp32.
+//                  ([col][k], swizzled by column group) so each lane reads
+//                  its 8-element K slice as one 16-byte LDS read.  Partials
+//                  [S][T][k] fp32.
 //   bgate_kernel : one workgroup per token: sums the S partials in a fixed
 //                  order, forms ||g||^2, rho and the gate, writes g as bf16
 //                  hi + lo (g = hi + lo to ~2^-16) for the fast GEMM.
@@ -17,11 +18,14 @@
 //                  launch.  Each workgroup compacts the tokens of each path
 //                  from the gate flags itself (deterministic order), then
 //                  loops over 64-column tiles: all of a path's tokens (256
-//                  per pass) against the tile with v_mfma_f32_32x32x16_bf16
-//                  over K chunks of 64, register-staged prefetch, y leaving
-//                  through LDS in 16-byte pieces (see below).
+//                  per pass, eight wavefronts of 32) against the tile with
+//                  v_mfma_f32_32x32x16_bf16 over K chunks of 64, register-
+//                  staged prefetch, y leaving through LDS in 16-byte pieces
+//                  (see below).
 //   bthin_kernel : both paths' outputs with 1 to kThin tokens: the matrix is
-//                  streamed by 16-row blocks (v_mfma_f32_16x16x32_bf16).
+//                  streamed by blocks of 16 (fast) or 32 (slow) rows
+//                  (v_mfma_f32_16x16x32_bf16).
+//   bprep_kernel : the image M = W V_k (once per map).
 //
 // MFMA operand layouts (checked on the device): for 32x32x16, lane l holds
 // A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32], e = 0..7, and

@@ -7,11 +7,12 @@
 // One sweep: Z = A V (fp32 accumulation), Y = A^T Z (fp32 accumulation,
 // stored fp64), then Y = QR by CholeskyQR2 in fp64: G = Y^T Y, G = R^T R
 // (blocked Cholesky), Y <- Y R^-1 (blocked substitution), and the same once
-// more to restore
-// orthogonality to rounding.  The Q factor with a positive diagonal R is
-// unique, so this is the same basis that Gram-Schmidt (DGKS) gives.
-// Everything runs on the device; a Cholesky breakdown (a rank-deficient
-// block) sets the workspace status word.
+// more to restore orthogonality to rounding.  The Q factor with a positive
+// diagonal R is unique, so this is the same basis that Gram-Schmidt (DGKS)
+// gives.  With bf16 samples the two products run on the matrix cores (the
+// fp32 operand as three bf16 parts, see mgemm_kernel), otherwise on fp32 FMA
+// tiles.  Everything runs on the device; a Cholesky breakdown (a
+// rank-deficient block) sets the workspace status word.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
