@@ -586,8 +586,8 @@ def ctypes_calib(n, d, k):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("this build runs on one GPU only: --gpus must be 1 (the path would shard by output "
-              "rows or tokens across GPUs, see the design notes)", file=sys.stderr)
+        print("the library runs on one GPU only: --gpus must be 1 (the path would shard by output "
+              "rows or tokens across GPUs; only the one-GPU share is built and measured)", file=sys.stderr)
         sys.exit(2)
     if args.workload == "batched-t256":
         bench_batched(args)
