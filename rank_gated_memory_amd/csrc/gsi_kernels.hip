@@ -791,6 +791,7 @@ struct Sched {
   uint32_t tp;    // projection ticket held
   uint32_t to;    // output ticket held
   uint64_t open;  // last open word seen for wave w
+  int fresh;      // first pass after entering wave w
 };
 
 // Tickets of a wave: the first of each kind is the workgroup's index; the
@@ -871,6 +872,7 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
       st.last_out = 0;
       st.slot = 0;
       st.open = 0;
+      st.fresh = 1;
     }
     const int p0 = a.wave_tab[w];
     const int np = a.wave_tab[w + 1] - p0;
@@ -889,8 +891,15 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
     const uint32_t to = bcast(st.to);
     const int q0 = a.wave_tab[a.n_waves + 1 + w];
     const uint32_t ncalls = (uint32_t)(a.wave_tab[a.n_waves + 2 + w] - q0);
-    // (once every gate of the wave is open the cached open word is final)
-    if (to >= (uint32_t)(st.open & kLow40) && (uint32_t)(st.open >> 40) != ncalls) st.open = load_open(a, w);
+    // (once every gate of the wave is open the cached open word is final;
+    // the first pass after entering the wave skips the reload: gates open
+    // only as projection units finish, so a workgroup that has just entered
+    // runs its projection ticket first, and one without a ticket reloads on
+    // its next pass)
+    const int fresh = st.fresh;
+    st.fresh = 0;
+    if (!fresh && to >= (uint32_t)(st.open & kLow40) && (uint32_t)(st.open >> 40) != ncalls)
+      st.open = load_open(a, w);
     if (to < (uint32_t)(st.open & kLow40)) {
       // ---- output unit: find the open call that covers ticket `to` ----
       const int nopen = (int)(st.open >> 40);
