@@ -86,28 +86,43 @@ __device__ __forceinline__ float rho_of(float xx, float gg) {
 
 namespace {
 
-// Inclusive workgroup scan of two counters at once (Hillis-Steele in LDS)
-// over the NT threads of the workgroup.
+// Inclusive workgroup scan of two counters at once over the NT threads:
+// within each wavefront by shuffles, then the wavefront totals through LDS
+// (sh: NT / 64 entries), so the whole scan waits on one barrier.  Returns
+// the thread's inclusive prefix; *tot receives the workgroup totals.
 template <int NT>
-__device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int2 u = tid >= off ? sh[tid - off] : make_int2(0, 0);
-    __syncthreads();
-    sh[tid].x += u.x;
-    sh[tid].y += u.y;
-    __syncthreads();
+__device__ __forceinline__ int2 block_scan2(int2 v, int2 *sh, int2 *tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ux = __shfl_up(v.x, off, 64), uy = __shfl_up(v.y, off, 64);
+    if (lane >= off) {
+      v.x += ux;
+      v.y += uy;
+    }
   }
-  return sh[tid];
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  int2 before = make_int2(0, 0), all = make_int2(0, 0);
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int2 t = sh[w];
+    if (w < wave) {
+      before.x += t.x;
+      before.y += t.y;
+    }
+    all.x += t.x;
+    all.y += t.y;
+  }
+  *tot = all;
+  return make_int2(v.x + before.x, v.y + before.y);
 }
 
 // Tokens of each path in increasing order, from the gate flags: the fast
 // tokens in idx[0, nf), the slow ones in idx[nf, n).  Every output
 // workgroup (NT threads) compacts the n flags itself (one load per thread at
-// n = 256 and a scan in LDS), so the gate needs no grid-wide step.  Returns
-// (nf, ns).
+// n = 256 and a two-counter scan; scan: NT / 64 entries), so the gate needs
+// no grid-wide step.  Returns (nf, ns).
 template <int NT>
 __device__ __forceinline__ int2 path_lists(const BArgs &a, int16_t *idx, int2 *scan) {
   const int tid = threadIdx.x;
@@ -122,8 +137,8 @@ __device__ __forceinline__ int2 path_lists(const BArgs &a, int16_t *idx, int2 *s
     mine.x += fl[i] == 0;
     mine.y += fl[i] == 1;
   }
-  const int2 inc = block_scan2<NT>(mine, scan);
-  const int2 tot = scan[NT - 1];
+  int2 tot;
+  const int2 inc = block_scan2<NT>(mine, scan, &tot);
   int wf = inc.x - mine.x, ws = tot.x + inc.y - mine.y;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -435,7 +450,7 @@ struct OutLds {
   u32x4_t Bs[2][8][64];                          // double-buffered 64-wide K chunk: [k group][column]
   u32x4_t As[kOutWaves][2 * kOutTok * kOutArow];  // each wavefront's A chunk
   int16_t idx[kMaxBatch];                        // tokens of both paths (path_lists)
-  int2 scan[kOutThreads];
+  int2 scan[kOutWaves];                          // wavefront totals of the compaction scan
 };
 
 template <int PATH>
@@ -745,7 +760,7 @@ __device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinP
 __global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
   __shared__ u32x4_t lds[kWaves][kThinPieces];
   __shared__ int16_t idx[kMaxBatch];
-  __shared__ int2 scan[kBlock];
+  __shared__ int2 scan[kWaves];
   __shared__ int toks[2][kThin];
   const int2 cnt = path_lists<kBlock>(a, idx, scan);
   const int tid = threadIdx.x;
