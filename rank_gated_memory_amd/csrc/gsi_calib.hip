@@ -374,40 +374,50 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// Unblocked Cholesky (upper) of the 64 x 64 tile S on wavefront 0, without
-// barriers: lane c holds column c in registers, and step j takes the pivot
-// S[j][j] and the multipliers S[j][i] from the lanes that hold them.  Only
-// upper entries ever cross lanes, so whatever the lower part of a column
-// turns into stays in its lane; it is written back as zero.
-__device__ void chol_tile_wave(double (*S)[kLd], const double *diag0, int *bad) {
-  const int c = threadIdx.x;
-  double col[kNb];
+// Unblocked Cholesky (upper) of the 64 x 64 tile S by the four wavefronts
+// (256 threads): wavefront q holds rows 16q .. 16q+15 in registers, lane c
+// column c.  At step j the wavefront holding row j takes the pivot from lane
+// j, scales the row and publishes it in LDS (two alternating row buffers),
+// and after one barrier every wavefront updates its rows below j with it.
+// Only upper entries are ever read across lanes (the pivot, and S[j][i] for
+// i > j), so whatever the lower part of a row turns into stays put; it is
+// written back as zero.
+__device__ void chol_tile(double (*S)[kLd], const double *diag0, double (*rowbuf)[kNb], int *bad) {
+  constexpr int kRows = kNb / (kCB / 64);  // rows per wavefront
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  double reg[kRows];
 #pragma unroll
-  for (int r = 0; r < kNb; ++r) col[r] = S[r][c];
+  for (int m = 0; m < kRows; ++m) reg[m] = S[kRows * q + m][c];
   int badj = 0;
 #pragma unroll
   for (int j = 0; j < kNb; ++j) {
-    double p = readlane_f64(col[j], j);
-    if (!(p > 1e-12 * diag0[j])) {
-      badj = 1;
-      p = 1.0;
+    if (q == j / kRows) {
+      double p = readlane_f64(reg[j % kRows], j);
+      if (!(p > 1e-12 * diag0[j])) {
+        badj = 1;
+        p = 1.0;
+      }
+      const double rjj = sqrt(p);
+      if (c == j)
+        reg[j % kRows] = rjj;
+      else if (c > j)
+        reg[j % kRows] = reg[j % kRows] / rjj;
+      rowbuf[j & 1][c] = reg[j % kRows];
     }
-    const double rjj = sqrt(p);
-    if (c == j)
-      col[j] = rjj;
-    else if (c > j)
-      col[j] = col[j] / rjj;
+    __syncthreads();
+    const double sjc = rowbuf[j & 1][c];
 #pragma unroll
-    for (int i = j + 1; i < kNb; ++i) col[i] = fma(-readlane_f64(col[j], i), col[j], col[i]);
+    for (int m = 0; m < kRows; ++m)
+      if (kRows * q + m > j) reg[m] = fma(-rowbuf[j & 1][kRows * q + m], sjc, reg[m]);
   }
 #pragma unroll
-  for (int r = 0; r < kNb; ++r) S[r][c] = r <= c ? col[r] : 0.0;
+  for (int m = 0; m < kRows; ++m) S[kRows * q + m][c] = kRows * q + m <= c ? reg[m] : 0.0;
   if (c == 0 && badj) *bad = 1;
 }
 
 // R (upper, [k][k]) with G = R^T R, by the left-looking blocked Cholesky
 // (64 x 64 blocks), one block row J at a time in two launches:
-//     chol_diag_kernel (one workgroup):
+//     chol_diag_kernel (one workgroup; chol_tile, then the block's inverse):
 //         S = G_JJ - sum_{I<J} R_IJ^T R_IJ,   R_JJ = chol(S)      (in LDS)
 //     chol_panel_kernel (one workgroup per block L > J):
 //         R_JL = R_JJ^-T (G_JL - sum_{I<J} R_IJ^T R_IL)
@@ -420,6 +430,7 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
                                                         uint32_t *status) {
   __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd];
   __shared__ double diag0[kNb];
+  __shared__ double rowbuf[2][kNb];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
@@ -446,7 +457,7 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
   }
   if (tid < kNb && tid >= nJ) diag0[tid] = 1.0;
   __syncthreads();
-  if (tid < kNb) chol_tile_wave(S, diag0, &s_bad);
+  chol_tile(S, diag0, rowbuf, &s_bad);
   __syncthreads();
   // Di = S^-1 (upper) on wavefront 0: lane c solves S x = e_c in registers
   // by the column sweep of back substitution (x[r] /= S[r][r], then
