@@ -490,7 +490,6 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
 __global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double *R, const double *Dinv, int k,
                                                          int J) {
   __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
-  const int tid = threadIdx.x;
   const int ti = tile_ti(), tj = tile_tj();
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
   const int L = J + 1 + blockIdx.x;

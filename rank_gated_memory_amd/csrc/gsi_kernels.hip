@@ -1021,7 +1021,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0};
   int cur = -1, cur_slow = 0;
   for (;;) {
     if (tid < 64) next_job(a, st, s_job);
