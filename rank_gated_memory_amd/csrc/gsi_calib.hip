@@ -596,14 +596,30 @@ __global__ void __launch_bounds__(kCB) gram_split_kernel(const double *__restric
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  for (int t0 = r0; t0 < r1; t0 += KC) {
-    for (int e = tid; e < KC * 64; e += kCB) {
-      const int r = e / 64, c = e % 64;
+  // the next slab of rows is loaded into registers while this one is
+  // multiplied (KC * 64 / kCB elements of each tile per thread)
+  constexpr int PL = KC * 64 / kCB;
+  double px[PL], py[PL];
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int e = tid + q * kCB, r = e / 64, c = e % 64;
       const bool ok = t0 + r < r1;
-      Xs[r][c] = (ok && i0 + c < k) ? Y[(size_t)(t0 + r) * k + i0 + c] : 0.0;
-      Ys[r][c] = (ok && j0 + c < k) ? Y[(size_t)(t0 + r) * k + j0 + c] : 0.0;
+      px[q] = (ok && i0 + c < k) ? Y[(size_t)(t0 + r) * k + i0 + c] : 0.0;
+      py[q] = (ok && j0 + c < k) ? Y[(size_t)(t0 + r) * k + j0 + c] : 0.0;
+    }
+  };
+  if (r0 < r1) load(r0);
+  for (int t0 = r0; t0 < r1; t0 += KC) {
+    __syncthreads();  // the previous slab's products are done
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int e = tid + q * kCB;
+      Xs[e / 64][e % 64] = px[q];
+      Ys[e / 64][e % 64] = py[q];
     }
     __syncthreads();
+    if (t0 + KC < r1) load(t0 + KC);
 #pragma unroll 4
     for (int r = 0; r < KC; ++r) {
       double xv[4], yv[4];
@@ -616,7 +632,6 @@ __global__ void __launch_bounds__(kCB) gram_split_kernel(const double *__restric
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = fma(xv[x], yv[y], acc[x][y]);
     }
-    __syncthreads();
   }
   double *Pr = P + (size_t)blockIdx.y * k * k;
 #pragma unroll
