@@ -313,58 +313,85 @@ __device__ __forceinline__ void load_tiles2(double (*da)[kLd], const double *Ma,
   }
 }
 
-// This thread's 4 x 4 outputs of a 64 x 64 tile: rows ti.., columns tj..
-__device__ __forceinline__ int tile_ti() { return (threadIdx.x >> 4) * 4; }
-__device__ __forceinline__ int tile_tj() { return (threadIdx.x & 15) * 4; }
+// Products of 64 x 64 fp64 tiles in LDS on the matrix cores
+// (v_mfma_f64_16x16x4f64: each operand value a lane loads from LDS serves 16
+// products, against 2 per value for 4 x 4 register tiles of FMAs, which left
+// these kernels bound by LDS bandwidth).  Wavefront w owns the 32 x 32 block
+// at rows 32 (w / 2), columns 32 (w % 2), as 2 x 2 accumulators of 16 x 16.
+// Lane layout (checked on the device): lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16] of a 16 x 4 by 4 x 16 step, and element e of its
+// accumulator is C[4 e + l / 16][l % 16].
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+struct Blk {
+  f64x4_t c[2][2];
+};
+__device__ __forceinline__ int blk_r0() { return 32 * (threadIdx.x >> 7); }
+__device__ __forceinline__ int blk_c0() { return 32 * ((threadIdx.x >> 6) & 1); }
+// row and column in the tile of element e of accumulator (bi, bj) of this lane
+__device__ __forceinline__ int blk_row(int bi, int e) { return blk_r0() + 16 * bi + 4 * e + ((threadIdx.x & 63) >> 4); }
+__device__ __forceinline__ int blk_col(int bj) { return blk_c0() + 16 * bj + (threadIdx.x & 15); }
 
-// acc -= A^T B over the 64 rows of A and B (A^T: A read by columns).
-__device__ __forceinline__ void sub_atb(double (&acc)[4][4], const double (*A)[kLd], const double (*B)[kLd]) {
-  const int ti = tile_ti(), tj = tile_tj();
+__device__ __forceinline__ void blk_zero(Blk &b) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) b.c[bi][bj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+}
+
+__device__ __forceinline__ void blk_load(Blk &b, const double (*T)[kLd]) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b.c[bi][bj][e] = T[blk_row(bi, e)][blk_col(bj)];
+}
+
+__device__ __forceinline__ void blk_store(double (*T)[kLd], const Blk &b) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[blk_row(bi, e)][blk_col(bj)] = b.c[bi][bj][e];
+}
+
+// b += s A^T B over the first K rows of A and B: C[r][c] += s sum_t A[t][r] B[t][c]
+// (s = +1 or -1, applied to A's values exactly).
+template <int K>
+__device__ __forceinline__ void blk_atb(Blk &b, const double (*A)[kLd], const double (*B)[kLd], double s) {
+  const int l = threadIdx.x & 63, r0 = blk_r0(), c0 = blk_c0();
 #pragma unroll 4
-  for (int i = 0; i < kNb; ++i) {
-    double av[4], bv[4];
+  for (int t = 0; t < K; t += 4) {
+    const int tr = t + (l >> 4);
+    double a[2], bv[2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) av[x] = A[i][ti + x];
+    for (int i = 0; i < 2; ++i) a[i] = s * A[tr][r0 + 16 * i + (l & 15)];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) bv[y] = B[i][tj + y];
+    for (int j = 0; j < 2; ++j) bv[j] = B[tr][c0 + 16 * j + (l & 15)];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = fma(-av[x], bv[y], acc[x][y]);
+      for (int j = 0; j < 2; ++j) b.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], b.c[i][j], 0, 0, 0);
   }
 }
 
-// acc -= A B (A read by rows).
-__device__ __forceinline__ void sub_ab(double (&acc)[4][4], const double (*A)[kLd], const double (*B)[kLd]) {
-  const int ti = tile_ti(), tj = tile_tj();
+// b += s A B: C[r][c] += s sum_t A[r][t] B[t][c], t < 64.
+__device__ __forceinline__ void blk_ab(Blk &b, const double (*A)[kLd], const double (*B)[kLd], double s) {
+  const int l = threadIdx.x & 63, r0 = blk_r0(), c0 = blk_c0();
 #pragma unroll 4
-  for (int i = 0; i < kNb; ++i) {
-    double av[4], bv[4];
+  for (int t = 0; t < kNb; t += 4) {
+    const int tc = t + (l >> 4);
+    double a[2], bv[2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) av[x] = A[ti + x][i];
+    for (int i = 0; i < 2; ++i) a[i] = s * A[r0 + 16 * i + (l & 15)][tc];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) bv[y] = B[i][tj + y];
+    for (int j = 0; j < 2; ++j) bv[j] = B[tc][c0 + 16 * j + (l & 15)];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = fma(-av[x], bv[y], acc[x][y]);
+      for (int j = 0; j < 2; ++j) b.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], b.c[i][j], 0, 0, 0);
   }
-}
-
-__device__ __forceinline__ void acc_from_tile(double (&acc)[4][4], const double (*T)[kLd]) {
-  const int ti = tile_ti(), tj = tile_tj();
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = T[ti + x][tj + y];
-}
-
-__device__ __forceinline__ void acc_to_tile(double (*T)[kLd], const double (&acc)[4][4]) {
-  const int ti = tile_ti(), tj = tile_tj();
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) T[ti + x][tj + y] = acc[x][y];
 }
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
@@ -438,16 +465,16 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
   load_tile(S, G, k, c0, c0, nJ, nJ);
   __syncthreads();
   if (tid < kNb) diag0[tid] = S[tid][tid];
-  double acc[4][4];
-  acc_from_tile(acc, S);
+  Blk acc;
+  blk_load(acc, S);
   for (int I = 0; I < J; ++I) {
     __syncthreads();
     load_tile(Ta, R, k, I * kNb, c0, kNb, nJ);
     __syncthreads();
-    sub_atb(acc, Ta, Ta);
+    blk_atb<kNb>(acc, Ta, Ta, -1.0);
   }
   __syncthreads();
-  acc_to_tile(S, acc);
+  blk_store(S, acc);
   __syncthreads();
   // a partial block is padded with the identity, so that its factor is
   // chol(S) beside an identity block and every step below is uniform
@@ -490,40 +517,35 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
 __global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double *R, const double *Dinv, int k,
                                                          int J) {
   __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
-  const int ti = tile_ti(), tj = tile_tj();
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
   const int L = J + 1 + blockIdx.x;
   const int l0 = L * kNb, nL = min(kNb, k - l0);
   load_tiles2(S, G, k, c0, l0, nJ, nL, Di, Dinv + (size_t)J * kNb * kNb, kNb, 0, 0, kNb, kNb);
   __syncthreads();
-  double acc[4][4];
-  acc_from_tile(acc, S);
+  Blk acc;
+  blk_load(acc, S);
   for (int I = 0; I < J; ++I) {
     __syncthreads();
     load_tiles2(Ta, R, k, I * kNb, c0, kNb, nJ, Tb, R, k, I * kNb, l0, kNb, nL);
     __syncthreads();
-    sub_atb(acc, Ta, Tb);
+    blk_atb<kNb>(acc, Ta, Tb, -1.0);
   }
   __syncthreads();
-  acc_to_tile(S, acc);
+  blk_store(S, acc);
   __syncthreads();
   // R_JL = Di^T S: out[r][c] = sum_{i <= r} Di[i][r] S[i][c]
-  double out[4][4];
+  Blk out;
+  blk_zero(out);
+  blk_atb<kNb>(out, Di, S, 1.0);
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
-  for (int i = 0; i < kNb; ++i) {
+    for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) out[x][y] = fma(Di[i][ti + x], S[i][tj + y], out[x][y]);
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-      if (ti + x < nJ && tj + y < nL) R[(size_t)(c0 + ti + x) * k + l0 + tj + y] = out[x][y];
+      for (int e = 0; e < 4; ++e) {
+        const int r = blk_row(bi, e), c = blk_col(bj);
+        if (r < nJ && c < nL) R[(size_t)(c0 + r) * k + l0 + c] = out.c[bi][bj][e];
+      }
 }
 
 // Q = Y R^-1 ([d][k]) by a blocked forward substitution over the block
@@ -532,7 +554,6 @@ __global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double
 __global__ void __launch_bounds__(kCB) trsm_kernel(const double *Y, const double *R, const double *Dinv,
                                                    double *Q, int d, int k) {
   __shared__ double Ta[kNb][kLd], Tb[kNb][kLd];
-  const int ti = tile_ti(), tj = tile_tj();
   const int r0 = blockIdx.x * kNb, nr = min(kNb, d - r0);
   const int nbk = (k + kNb - 1) / kNb;
   for (int J = 0; J < nbk; ++J) {
@@ -540,34 +561,30 @@ __global__ void __launch_bounds__(kCB) trsm_kernel(const double *Y, const double
     __syncthreads();
     load_tile(Ta, Y, k, r0, c0, nr, nJ);
     __syncthreads();
-    double acc[4][4];
-    acc_from_tile(acc, Ta);
+    Blk acc;
+    blk_load(acc, Ta);
     for (int I = 0; I < J; ++I) {
       __syncthreads();
       load_tiles2(Ta, Q, k, r0, I * kNb, nr, kNb, Tb, R, k, I * kNb, c0, kNb, nJ);
       __syncthreads();
-      sub_ab(acc, Ta, Tb);
+      blk_ab(acc, Ta, Tb, -1.0);
     }
     __syncthreads();
-    acc_to_tile(Ta, acc);
+    blk_store(Ta, acc);
     load_tile(Tb, Dinv + (size_t)J * kNb * kNb, kNb, 0, 0, kNb, kNb);
     __syncthreads();
-    double out[4][4];
+    Blk out;
+    blk_zero(out);
+    blk_ab(out, Ta, Tb, 1.0);
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) out[x][y] = 0.0;
-    for (int i = 0; i < kNb; ++i) {
+      for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) out[x][y] = fma(Ta[ti + x][i], Tb[i][tj + y], out[x][y]);
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        if (ti + x < nr && tj + y < nJ) Q[(size_t)(r0 + ti + x) * k + c0 + tj + y] = out[x][y];
+        for (int e = 0; e < 4; ++e) {
+          const int r = blk_row(bi, e), c = blk_col(bj);
+          if (r < nr && c < nJ) Q[(size_t)(r0 + r) * k + c0 + c] = out.c[bi][bj][e];
+        }
     // this block column of Q is read back for the next ones
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -590,12 +607,8 @@ __global__ void __launch_bounds__(kCB) gram_split_kernel(const double *__restric
   const int i0 = bi * 64, j0 = (bi + b) * 64;
   const int r0 = blockIdx.y * chunk, r1 = min(d, r0 + chunk);
   const int tid = threadIdx.x;
-  const int ti = (tid >> 4) * 4, tj = (tid & 15) * 4;
-  double acc[4][4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  Blk acc;
+  blk_zero(acc);
   // the next slab of rows is loaded into registers while this one is
   // multiplied (KC * 64 / kCB elements of each tile per thread)
   constexpr int PL = KC * 64 / kCB;
@@ -620,27 +633,18 @@ __global__ void __launch_bounds__(kCB) gram_split_kernel(const double *__restric
     }
     __syncthreads();
     if (t0 + KC < r1) load(t0 + KC);
-#pragma unroll 4
-    for (int r = 0; r < KC; ++r) {
-      double xv[4], yv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) xv[x] = Xs[r][ti + x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) yv[y] = Ys[r][tj + y];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(xv[x], yv[y], acc[x][y]);
-    }
+    blk_atb<KC>(acc, Xs, Ys, 1.0);
   }
   double *Pr = P + (size_t)blockIdx.y * k * k;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int i = i0 + ti + x, j = j0 + tj + y;
-      if (i < k && j < k) Pr[(size_t)i * k + j] = acc[x][y];
-    }
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + blk_row(bi, e), j = j0 + blk_col(bj);
+        if (i < k && j < k) Pr[(size_t)i * k + j] = acc.c[bi][bj][e];
+      }
 }
 
 // G = sum of the S partials in range order, on the upper-triangle tiles
