@@ -388,6 +388,13 @@ def bench_batched(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "batched-t256: T=256, d=4096, d_out=16384, value at k=256, 10% slow",
                    "cells": cells, "prepare": prep},
+        # the whole gsi_linear call of the head cell (projection GEMM, gate,
+        # wide and row-streaming output kernels) against the HBM roof: its
+        # algorithmic bytes (V_k, X, Y, M once if any token is fast, W once
+        # if any is slow) over the call time
+        "roofline": {"bound": "hbm", "kernel": "gsi_linear (bproj, bgate, bout, bthin)",
+                     "achieved": head["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": head["gbps"] / PEAK_HBM_GBPS, "traffic": None},
     }), flush=True)
 
 
