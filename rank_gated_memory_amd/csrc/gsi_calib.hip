@@ -408,57 +408,135 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // and after one barrier every wavefront updates its rows below j with it.
 // Only upper entries are ever read across lanes (the pivot, and S[j][i] for
 // i > j), so whatever the lower part of a row turns into stays put; it is
-// written back as zero.
-__device__ void chol_tile(double (*S)[kLd], const double *diag0, double (*rowbuf)[kNb], int *bad) {
+// written back as zero.  The steps run as a loop over the four row groups
+// with the sixteen steps of a group unrolled (register indices must be
+// static): the whole sweep unrolled is far larger than the instruction
+// cache, and straight-line code that runs once is then fetched line by line
+// from L2.
+// 1/sqrt(p) for p > 0: the hardware estimate, then two Newton steps for
+// f(y) = 1/y^2 - p, y <- y (3 - p y^2) / 2, each of which about doubles the
+// number of correct bits.
+__device__ __forceinline__ double rsqrt_f64(double p) {
+  double y = __builtin_amdgcn_rsq(p);
+  const double h = 0.5 * p;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = fma(y, fma(-h * y, y, 0.5), y);
+  return y;
+}
+
+__device__ __forceinline__ void chol_tile(double (*S)[kLd], const double *diag0, double *rdiag,
+                                          double (*rowbuf)[kNb], int *bad) {
   constexpr int kRows = kNb / (kCB / 64);  // rows per wavefront
-  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   double reg[kRows];
 #pragma unroll
   for (int m = 0; m < kRows; ++m) reg[m] = S[kRows * q + m][c];
   int badj = 0;
+#pragma unroll 1
+  for (int jb = 0; jb < kNb / kRows; ++jb) {
 #pragma unroll
-  for (int j = 0; j < kNb; ++j) {
-    if (q == j / kRows) {
-      double p = readlane_f64(reg[j % kRows], j);
-      if (!(p > 1e-12 * diag0[j])) {
-        badj = 1;
-        p = 1.0;
+    for (int jj = 0; jj < kRows; ++jj) {
+      const int j = jb * kRows + jj;
+      if (q == jb) {
+        double p = readlane_f64(reg[jj], j);
+        if (!(p > 1e-12 * diag0[j])) {
+          badj = 1;
+          p = 1.0;
+        }
+        // R_jj = sqrt(p) and the row scaled by 1/R_jj, which is kept for
+        // the inverse: one estimate-and-refine on the step's critical path
+        // instead of a square root followed by a division
+        const double y = rsqrt_f64(p);
+        if (c == j)
+          reg[jj] = p * y;
+        else if (c > j)
+          reg[jj] = reg[jj] * y;
+        if (c == 0) rdiag[j] = y;
+        // the published row is zero left of the pivot, so the update below
+        // leaves rows above j as they are (fma(-0, v, x) == x for finite v)
+        rowbuf[j & 1][c] = c >= j ? reg[jj] : 0.0;
       }
-      const double rjj = sqrt(p);
-      if (c == j)
-        reg[j % kRows] = rjj;
-      else if (c > j)
-        reg[j % kRows] = reg[j % kRows] / rjj;
-      rowbuf[j & 1][c] = reg[j % kRows];
-    }
-    __syncthreads();
-    const double sjc = rowbuf[j & 1][c];
+      __syncthreads();
+      const double sjc = rowbuf[j & 1][c];
 #pragma unroll
-    for (int m = 0; m < kRows; ++m)
-      if (kRows * q + m > j) reg[m] = fma(-rowbuf[j & 1][kRows * q + m], sjc, reg[m]);
+      for (int m = 0; m < kRows; ++m)
+        if (m != jj) reg[m] = fma(-rowbuf[j & 1][kRows * q + m], sjc, reg[m]);
+      if (q != jb) reg[jj] = fma(-rowbuf[j & 1][kRows * q + jj], sjc, reg[jj]);
+    }
   }
 #pragma unroll
   for (int m = 0; m < kRows; ++m) S[kRows * q + m][c] = kRows * q + m <= c ? reg[m] : 0.0;
   if (c == 0 && badj) *bad = 1;
 }
 
+// X = U^-1 for the upper triangular 64 x 64 tile U (LDS; rdiag[j] = 1/U[j][j]), by the four
+// wavefronts: wavefront q holds rows 16q .. 16q+15 of X in registers (lane c
+// column c), starting from the identity.  Back substitution by rows, from
+// the last: at step j row j of X has had every term with index above j
+// taken out, so scaling it by 1/U[j][j] makes it final; it is published in
+// LDS and, after one barrier, each row i < j takes U[i][j] times it away.
+// Rows of X below the diagonal stay zero.  Same loop shape as chol_tile; U
+// must hold zeros below its diagonal (chol_tile writes them).
+__device__ __forceinline__ void tri_inverse(const double (*U)[kLd], const double *rdiag, double (*X)[kLd],
+                                            double (*rowbuf)[kNb]) {
+  constexpr int kRows = kNb / (kCB / 64);
+  const int c = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  double x[kRows];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) x[m] = kRows * q + m == c ? 1.0 : 0.0;
+#pragma unroll 1
+  for (int jb = kNb / kRows - 1; jb >= 0; --jb) {
+#pragma unroll
+    for (int jj = kRows - 1; jj >= 0; --jj) {
+      const int j = jb * kRows + jj;
+      if (q == jb) {
+        x[jj] = x[jj] * rdiag[j];
+        rowbuf[j & 1][c] = x[jj];
+      }
+      __syncthreads();
+      // U is zero below its diagonal, so rows below j take nothing away;
+      // only row j itself is left out
+      const double xjc = rowbuf[j & 1][c];
+#pragma unroll
+      for (int m = 0; m < kRows; ++m)
+        if (m != jj) x[m] = fma(-U[kRows * q + m][j], xjc, x[m]);
+      if (q != jb) x[jj] = fma(-U[kRows * q + jj][j], xjc, x[jj]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kRows; ++m) X[kRows * q + m][c] = x[m];
+}
+
 // R (upper, [k][k]) with G = R^T R, by the left-looking blocked Cholesky
-// (64 x 64 blocks), one block row J at a time in two launches:
-//     chol_diag_kernel (one workgroup; chol_tile, then the block's inverse):
+// (64 x 64 blocks), one block row J at a time:
+//     the diagonal block (diag_block, one workgroup; chol_tile, then the
+//     block's inverse):
 //         S = G_JJ - sum_{I<J} R_IJ^T R_IJ,   R_JJ = chol(S)      (in LDS)
-//     chol_panel_kernel (one workgroup per block L > J):
+//     the panel (chol_panel_kernel, one workgroup per block L > J):
 //         R_JL = R_JJ^-T (G_JL - sum_{I<J} R_IJ^T R_IL)
+// Block 0's diagonal is a launch of its own (chol_diag_kernel); every later
+// diagonal block is factored by the panel launch before it, in the
+// workgroup that writes the last block it needs, so a block row is one launch.
 // The inverse of each diagonal block goes to Dinv[J] (64 x 64, upper): the
 // panel and the solve for Q = Y R^-1 need only those.  A pivot that keeps
 // at most 1e-12 of its column's squared norm (G_jj) means the block is
 // numerically rank deficient (the fp32 products leave ~1e-14 there):
 // status <- 1.
-__global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double *R, double *Dinv, int k, int J,
-                                                        uint32_t *status) {
-  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd];
-  __shared__ double diag0[kNb];
-  __shared__ double rowbuf[2][kNb];
-  __shared__ int s_bad;
+// LDS of one diagonal block's factorisation.
+struct DiagLds {
+  double diag0[kNb];
+  double rdiag[kNb];
+  double rowbuf[2][kNb];
+  int bad;
+};
+
+// Block row J's diagonal block: S = G_JJ - sum_{I<J} R_IJ^T R_IJ, R_JJ =
+// chol(S), Dinv[J] = R_JJ^-1 (one workgroup; S, Di, Ta: 64 x 64 LDS tiles).
+__device__ __forceinline__ void diag_block(const double *G, double *R, double *Dinv, int k, int J, uint32_t *status,
+                           double (*S)[kLd], double (*Di)[kLd], double (*Ta)[kLd], DiagLds &D) {
+  double *diag0 = D.diag0;
+  auto &rowbuf = D.rowbuf;
+  int &s_bad = D.bad;
   const int tid = threadIdx.x;
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
   if (tid == 0) s_bad = 0;
@@ -484,26 +562,9 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
   }
   if (tid < kNb && tid >= nJ) diag0[tid] = 1.0;
   __syncthreads();
-  chol_tile(S, diag0, rowbuf, &s_bad);
+  chol_tile(S, diag0, D.rdiag, rowbuf, &s_bad);
   __syncthreads();
-  // Di = S^-1 (upper) on wavefront 0: lane c solves S x = e_c in registers
-  // by the column sweep of back substitution (x[r] /= S[r][r], then
-  // x[i] -= S[i][r] x[r] for every i < r: independent updates, whose S[i][r]
-  // are LDS broadcasts that can be read ahead).  Rows below c stay zero.
-  if (tid < kNb) {
-    const int c = tid;
-    double x[kNb];
-#pragma unroll
-    for (int r = 0; r < kNb; ++r) x[r] = r == c ? 1.0 : 0.0;
-#pragma unroll
-    for (int r = kNb - 1; r >= 0; --r) {
-      x[r] = x[r] / S[r][r];
-#pragma unroll
-      for (int i = 0; i < r; ++i) x[i] = fma(-S[i][r], x[r], x[i]);
-    }
-#pragma unroll
-    for (int r = 0; r < kNb; ++r) Di[r][c] = x[r];
-  }
+  tri_inverse(S, D.rdiag, Di, rowbuf);
   __syncthreads();
   // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
   for (int e = tid; e < kNb * kNb; e += kCB) {
@@ -514,9 +575,17 @@ __global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double 
   if (tid == 0 && s_bad) *status = 1u;
 }
 
-__global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double *R, const double *Dinv, int k,
-                                                         int J) {
+__global__ void __launch_bounds__(kCB) chol_diag_kernel(const double *G, double *R, double *Dinv, int k, int J,
+                                                        uint32_t *status) {
+  __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd];
+  __shared__ DiagLds D;
+  diag_block(G, R, Dinv, k, J, status, S, Di, Ta, D);
+}
+
+__global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double *R, double *Dinv, int k, int J,
+                                                         uint32_t *status) {
   __shared__ double S[kNb][kLd], Di[kNb][kLd], Ta[kNb][kLd], Tb[kNb][kLd];
+  __shared__ DiagLds D;
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
   const int L = J + 1 + blockIdx.x;
   const int l0 = L * kNb, nL = min(kNb, k - l0);
@@ -546,6 +615,14 @@ __global__ void __launch_bounds__(kCB) chol_panel_kernel(const double *G, double
         const int r = blk_row(bi, e), c = blk_col(bj);
         if (r < nJ && c < nL) R[(size_t)(c0 + r) * k + l0 + c] = out.c[bi][bj][e];
       }
+  // Block J+1's diagonal needs R_{I,J+1} for I <= J only, of which R_{J,J+1}
+  // is the block this workgroup has just written: the workgroup of L = J+1
+  // factors it here, which saves a launch per block row.
+  if (blockIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // R_{J,J+1} is read back below
+    __syncthreads();
+    diag_block(G, R, Dinv, k, J + 1, status, S, Di, Ta, D);
+  }
 }
 
 // Q = Y R^-1 ([d][k]) by a blocked forward substitution over the block
@@ -697,10 +774,9 @@ void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv,
   if (rb > 2048) rb = 2048;
   hipLaunchKernelGGL(gram_reduce_kernel, dim3(rb), dim3(kCB), 0, s, P, G, k, S);
   const int nbk = (k + kNb - 1) / kNb;
-  for (int J = 0; J < nbk; ++J) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, J, status);
-    if (J + 1 < nbk) hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - J - 1), dim3(kCB), 0, s, G, R, Dinv, k, J);
-  }
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kCB), 0, s, G, R, Dinv, k, 0, status);
+  for (int J = 0; J + 1 < nbk; ++J)  // block row J's panel, then block J+1's diagonal
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(nbk - J - 1), dim3(kCB), 0, s, G, R, Dinv, k, J, status);
   hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
 
