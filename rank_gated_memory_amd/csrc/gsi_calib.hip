@@ -401,18 +401,6 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// Unblocked Cholesky (upper) of the 64 x 64 tile S by the four wavefronts
-// (256 threads): wavefront q holds rows 16q .. 16q+15 in registers, lane c
-// column c.  At step j the wavefront holding row j takes the pivot from lane
-// j, scales the row and publishes it in LDS (two alternating row buffers),
-// and after one barrier every wavefront updates its rows below j with it.
-// Only upper entries are ever read across lanes (the pivot, and S[j][i] for
-// i > j), so whatever the lower part of a row turns into stays put; it is
-// written back as zero.  The steps run as a loop over the four row groups
-// with the sixteen steps of a group unrolled (register indices must be
-// static): the whole sweep unrolled is far larger than the instruction
-// cache, and straight-line code that runs once is then fetched line by line
-// from L2.
 // 1/sqrt(p) for p > 0: the hardware estimate, then two Newton steps for
 // f(y) = 1/y^2 - p, y <- y (3 - p y^2) / 2, each of which about doubles the
 // number of correct bits.
@@ -424,87 +412,105 @@ __device__ __forceinline__ double rsqrt_f64(double p) {
   return y;
 }
 
-__device__ __forceinline__ void chol_tile(double (*S)[kLd], const double *diag0, double *rdiag,
-                                          double (*rowbuf)[kNb], int *bad) {
-  constexpr int kRows = kNb / (kCB / 64);  // rows per wavefront
+// The diagonal 64 x 64 tile is worked on by the four wavefronts of the
+// workgroup (256 threads), wavefront q holding rows 16q .. 16q+15 in
+// registers, lane c column c; both routines below go block row by block row
+// (16 rows), with one barrier per block row rather than one per row.
+constexpr int kTileRows = kNb / (kCB / 64);  // rows per wavefront
+
+// Cholesky (upper) of the tile S, right-looking by 16-row blocks.  Block jb
+// is factored by its own wavefront alone: at step j it takes the pivot from
+// lane j, scales row j by 1/R_jj (kept in rdiag for the inverse) and takes
+// row j away from its later rows, reading R[j][i] from lane i of row j's
+// register; no other wavefront is involved, so no barrier.  It then writes
+// the block's rows to S (zero left of the diagonal) and, after a barrier,
+// every wavefront with later rows subtracts the block's rank-16 product
+// R_b^T R_b from them, reading R_b from LDS.  Only upper entries are ever
+// read across lanes, so whatever the lower part of a row in registers turns
+// into stays put.  Each row takes its pivots' updates in pivot order, as in
+// the unblocked elimination.
+__device__ __forceinline__ void chol_tile(double (*S)[kLd], const double *diag0, double *rdiag, int *bad) {
+  constexpr int kR = kTileRows;
   const int c = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  double reg[kRows];
+  double reg[kR];
 #pragma unroll
-  for (int m = 0; m < kRows; ++m) reg[m] = S[kRows * q + m][c];
+  for (int m = 0; m < kR; ++m) reg[m] = S[kR * q + m][c];  // each wavefront reads and writes only its rows
   int badj = 0;
 #pragma unroll 1
-  for (int jb = 0; jb < kNb / kRows; ++jb) {
+  for (int jb = 0; jb < kNb / kR; ++jb) {
+    if (q == jb) {
 #pragma unroll
-    for (int jj = 0; jj < kRows; ++jj) {
-      const int j = jb * kRows + jj;
-      if (q == jb) {
+      for (int jj = 0; jj < kR; ++jj) {
+        const int j = jb * kR + jj;
         double p = readlane_f64(reg[jj], j);
         if (!(p > 1e-12 * diag0[j])) {
           badj = 1;
           p = 1.0;
         }
-        // R_jj = sqrt(p) and the row scaled by 1/R_jj, which is kept for
-        // the inverse: one estimate-and-refine on the step's critical path
-        // instead of a square root followed by a division
         const double y = rsqrt_f64(p);
         if (c == j)
           reg[jj] = p * y;
         else if (c > j)
           reg[jj] = reg[jj] * y;
         if (c == 0) rdiag[j] = y;
-        // the published row is zero left of the pivot, so the update below
-        // leaves rows above j as they are (fma(-0, v, x) == x for finite v)
-        rowbuf[j & 1][c] = c >= j ? reg[jj] : 0.0;
-      }
-      __syncthreads();
-      const double sjc = rowbuf[j & 1][c];
 #pragma unroll
-      for (int m = 0; m < kRows; ++m)
-        if (m != jj) reg[m] = fma(-rowbuf[j & 1][kRows * q + m], sjc, reg[m]);
-      if (q != jb) reg[jj] = fma(-rowbuf[j & 1][kRows * q + jj], sjc, reg[jj]);
+        for (int m = jj + 1; m < kR; ++m) reg[m] = fma(-readlane_f64(reg[jj], jb * kR + m), reg[jj], reg[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < kR; ++m) S[kR * jb + m][c] = kR * jb + m <= c ? reg[m] : 0.0;
+    }
+    __syncthreads();
+    if (q > jb) {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) {
+        const double rc = S[kR * jb + t][c];
+#pragma unroll
+        for (int m = 0; m < kR; ++m) reg[m] = fma(-S[kR * jb + t][kR * q + m], rc, reg[m]);
+      }
     }
   }
-#pragma unroll
-  for (int m = 0; m < kRows; ++m) S[kRows * q + m][c] = kRows * q + m <= c ? reg[m] : 0.0;
   if (c == 0 && badj) *bad = 1;
 }
 
-// X = U^-1 for the upper triangular 64 x 64 tile U (LDS; rdiag[j] = 1/U[j][j]), by the four
-// wavefronts: wavefront q holds rows 16q .. 16q+15 of X in registers (lane c
-// column c), starting from the identity.  Back substitution by rows, from
-// the last: at step j row j of X has had every term with index above j
-// taken out, so scaling it by 1/U[j][j] makes it final; it is published in
-// LDS and, after one barrier, each row i < j takes U[i][j] times it away.
-// Rows of X below the diagonal stay zero.  Same loop shape as chol_tile; U
-// must hold zeros below its diagonal (chol_tile writes them).
-__device__ __forceinline__ void tri_inverse(const double (*U)[kLd], const double *rdiag, double (*X)[kLd],
-                                            double (*rowbuf)[kNb]) {
-  constexpr int kRows = kNb / (kCB / 64);
+// X = U^-1 for the upper triangular tile U (LDS, zero below its diagonal;
+// rdiag[j] = 1/U[j][j]), by back substitution in 16-row blocks from the
+// last.  Rows of X start as the identity.  Block jb's wavefront finishes its
+// rows alone: at step j (from the block's last row up) row j has had every
+// term with a later index taken away, so scaling it by 1/U[j][j] makes it
+// final, and the block's earlier rows take U[i][j] times it away (all in
+// the wavefront's own lanes: column c of X stays in lane c).  It writes its
+// rows to X and, after a barrier, every wavefront with earlier rows
+// subtracts U[rows, block] X[block] from them.  Rows of X below the
+// diagonal stay zero.
+__device__ __forceinline__ void tri_inverse(const double (*U)[kLd], const double *rdiag, double (*X)[kLd]) {
+  constexpr int kR = kTileRows;
   const int c = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  double x[kRows];
+  double x[kR];
 #pragma unroll
-  for (int m = 0; m < kRows; ++m) x[m] = kRows * q + m == c ? 1.0 : 0.0;
+  for (int m = 0; m < kR; ++m) x[m] = kR * q + m == c ? 1.0 : 0.0;
 #pragma unroll 1
-  for (int jb = kNb / kRows - 1; jb >= 0; --jb) {
+  for (int jb = kNb / kR - 1; jb >= 0; --jb) {
+    if (q == jb) {
 #pragma unroll
-    for (int jj = kRows - 1; jj >= 0; --jj) {
-      const int j = jb * kRows + jj;
-      if (q == jb) {
+      for (int jj = kR - 1; jj >= 0; --jj) {
+        const int j = jb * kR + jj;
         x[jj] = x[jj] * rdiag[j];
-        rowbuf[j & 1][c] = x[jj];
-      }
-      __syncthreads();
-      // U is zero below its diagonal, so rows below j take nothing away;
-      // only row j itself is left out
-      const double xjc = rowbuf[j & 1][c];
 #pragma unroll
-      for (int m = 0; m < kRows; ++m)
-        if (m != jj) x[m] = fma(-U[kRows * q + m][j], xjc, x[m]);
-      if (q != jb) x[jj] = fma(-U[kRows * q + jj][j], xjc, x[jj]);
+        for (int m = 0; m < jj; ++m) x[m] = fma(-U[kR * jb + m][j], x[jj], x[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < kR; ++m) X[kR * jb + m][c] = x[m];
+    }
+    __syncthreads();
+    if (q < jb) {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) {
+        const double xc = X[kR * jb + t][c];
+#pragma unroll
+        for (int m = 0; m < kR; ++m) x[m] = fma(-U[kR * q + m][kR * jb + t], xc, x[m]);
+      }
     }
   }
-#pragma unroll
-  for (int m = 0; m < kRows; ++m) X[kRows * q + m][c] = x[m];
 }
 
 // R (upper, [k][k]) with G = R^T R, by the left-looking blocked Cholesky
@@ -526,7 +532,6 @@ __device__ __forceinline__ void tri_inverse(const double (*U)[kLd], const double
 struct DiagLds {
   double diag0[kNb];
   double rdiag[kNb];
-  double rowbuf[2][kNb];
   int bad;
 };
 
@@ -535,7 +540,6 @@ struct DiagLds {
 __device__ __forceinline__ void diag_block(const double *G, double *R, double *Dinv, int k, int J, uint32_t *status,
                            double (*S)[kLd], double (*Di)[kLd], double (*Ta)[kLd], DiagLds &D) {
   double *diag0 = D.diag0;
-  auto &rowbuf = D.rowbuf;
   int &s_bad = D.bad;
   const int tid = threadIdx.x;
   const int c0 = J * kNb, nJ = min(kNb, k - c0);
@@ -562,9 +566,9 @@ __device__ __forceinline__ void diag_block(const double *G, double *R, double *D
   }
   if (tid < kNb && tid >= nJ) diag0[tid] = 1.0;
   __syncthreads();
-  chol_tile(S, diag0, D.rdiag, rowbuf, &s_bad);
+  chol_tile(S, diag0, D.rdiag, &s_bad);
   __syncthreads();
-  tri_inverse(S, D.rdiag, Di, rowbuf);
+  tri_inverse(S, D.rdiag, Di);
   __syncthreads();
   // R_JJ and Dinv[J] out (padding rows/columns of a partial block excluded)
   for (int e = tid; e < kNb * kNb; e += kCB) {
