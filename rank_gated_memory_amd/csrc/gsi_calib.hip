@@ -185,12 +185,16 @@ struct MGemm {
 };
 
 constexpr int kMRow = 9;  // 16-byte pieces per staged 64-wide K row, padded (bank spread)
-
 // 64 x 64 tile of C per workgroup, four wavefronts of 32 x 32; K in chunks of
-// 64 through double-buffered LDS, the next chunk loaded into registers while
-// the current one is multiplied.  Pieces outside the operands read the zero
-// block.
-template <int NP, int NQ, int OUT>
+// 64 through double-buffered LDS.  The loads run DEPTH chunks ahead, in a
+// ring of register stages: the stage just written to LDS is refilled with
+// chunk ch + DEPTH.  A chunk's multiplications are far shorter than the
+// latency of its loads, which a deeper ring covers where the operand
+// traffic leaves room (Y = A^T Z: 113 -> 100 us per launch on average at
+// DEPTH 3); Z^T = V^T A^T re-reads the three parts of V^T once per 64
+// samples and gains nothing from it.  Pieces outside the operands read the
+// zero block.
+template <int NP, int NQ, int OUT, int DEPTH>
 __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
   __shared__ u32x4_t Ps[2][NP][64 * kMRow];
   __shared__ u32x4_t Qs[2][NQ][64 * kMRow];
@@ -198,20 +202,20 @@ __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
   const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
   const int wi = wave >> 1, wj = wave & 1;
   const u32x4_t *zero = g.zero + (lane & 15);
-  u32x4_t pr[NP][2], qr[NQ][2];
-  auto load = [&](int kk) {
+  u32x4_t pr[DEPTH][NP][2], qr[DEPTH][NQ][2];
+  auto load = [&](u32x4_t (&ps)[NP][2], u32x4_t (&qs)[NQ][2], int kk) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int v = tid + h * kCB, r = v >> 3, c = kk + (v & 7) * 8;
       const bool kok = c < g.K;
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        pr[p][h] = *((kok && i0 + r < g.M)
+        ps[p][h] = *((kok && i0 + r < g.M)
                          ? reinterpret_cast<const u32x4_t *>(g.P + p * g.sp + (size_t)(i0 + r) * g.ldp + c)
                          : zero);
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-        qr[q][h] = *((kok && j0 + r < g.N)
+        qs[q][h] = *((kok && j0 + r < g.N)
                          ? reinterpret_cast<const u32x4_t *>(g.Q + q * g.sq + (size_t)(j0 + r) * g.ldq + c)
                          : zero);
     }
@@ -220,31 +224,40 @@ __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   const int nch = (g.K + 63) / 64;
-  load(0);
-  for (int ch = 0; ch < nch; ++ch) {
-    const int b = ch & 1;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int v = tid + h * kCB, r = v >> 3, c = v & 7;
+  for (int st = 0; st < DEPTH; ++st)
+    if (st < nch) load(pr[st], qr[st], st * 64);
+  for (int ch0 = 0; ch0 < nch; ch0 += DEPTH) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) Ps[b][p][r * kMRow + c] = pr[p][h];
+    for (int st = 0; st < DEPTH; ++st) {
+      const int ch = ch0 + st;
+      if (ch >= nch) break;  // the same for every thread of the workgroup
+      const int b = ch & 1;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) Qs[b][q][r * kMRow + c] = qr[q][h];
-    }
-    if (ch + 1 < nch) load((ch + 1) * 64);
-    __syncthreads();
+      for (int h = 0; h < 2; ++h) {
+        const int v = tid + h * kCB, r = v >> 3, c = v & 7;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int pc = ks * 2 + (lane >> 5);
-      bf16x8_t a[NP], bq[NQ];
+        for (int p = 0; p < NP; ++p) Ps[b][p][r * kMRow + c] = pr[st][p][h];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) a[p] = __builtin_bit_cast(bf16x8_t, Ps[b][p][(32 * wi + (lane & 31)) * kMRow + pc]);
+        for (int q = 0; q < NQ; ++q) Qs[b][q][r * kMRow + c] = qr[st][q][h];
+      }
+      if (ch + DEPTH < nch) load(pr[st], qr[st], (ch + DEPTH) * 64);
+      __syncthreads();
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) bq[q] = __builtin_bit_cast(bf16x8_t, Qs[b][q][(32 * wj + (lane & 31)) * kMRow + pc]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int pc = ks * 2 + (lane >> 5);
+        bf16x8_t a[NP], bq[NQ];
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
+        for (int p = 0; p < NP; ++p)
+          a[p] = __builtin_bit_cast(bf16x8_t, Ps[b][p][(32 * wi + (lane & 31)) * kMRow + pc]);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p], bq[q], acc, 0, 0, 0);
+        for (int q = 0; q < NQ; ++q)
+          bq[q] = __builtin_bit_cast(bf16x8_t, Qs[b][q][(32 * wj + (lane & 31)) * kMRow + pc]);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p], bq[q], acc, 0, 0, 0);
+      }
     }
   }
   // accumulator e of lane l: C[8 (e / 4) + 4 (l / 32) + e % 4][l % 32] of the wavefront's block
@@ -800,7 +813,7 @@ void mfma_products(const CalibArgs &c, hipStream_t s) {
   g1.ldc = c.np;
   g1.sp = (size_t)c.k * c.dp;
   g1.sc = (size_t)c.k * c.np;
-  hipLaunchKernelGGL((mgemm_kernel<3, 1, 0>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
+  hipLaunchKernelGGL((mgemm_kernel<3, 1, 0, 1>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
   MGemm g2{};
   g2.P = c.at;
   g2.Q = c.zt3;
@@ -813,7 +826,7 @@ void mfma_products(const CalibArgs &c, hipStream_t s) {
   g2.ldq = c.np;
   g2.ldc = c.k;
   g2.sq = (size_t)c.k * c.np;
-  hipLaunchKernelGGL((mgemm_kernel<1, 3, 1>), dim3((c.d + 63) / 64, (c.k + 63) / 64), dim3(kCB), 0, s, g2);
+  hipLaunchKernelGGL((mgemm_kernel<1, 3, 1, 3>), dim3((c.d + 63) / 64, (c.k + 63) / 64), dim3(kCB), 0, s, g2);
 }
 
 template <typename TY>
