@@ -175,7 +175,9 @@ __global__ void __launch_bounds__(kCB) split_t_kernel(const TY *__restrict__ Y, 
 // stride sp), Q rows j < N (NQ parts, part stride sq), rows along K with
 // strides ldp, ldq (multiples of 8).  OUT 0: C as three bf16 parts
 // [3][M][ldc] (part stride sc), columns up to ldc written (zero past N);
-// OUT 1: C fp64 [M][ldc], columns below N.
+// OUT 1: C fp64 [M][ldc], columns below N; OUT 2: the fp32 partial sum over
+// blockIdx.z's share of the K chunks, [gridDim.z][M][ldc], columns up to
+// ldc.
 struct MGemm {
   const uint16_t *P, *Q;
   void *C;
@@ -223,10 +225,12 @@ __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
   f32x16_t acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  const int nch = (g.K + 63) / 64;
+  const int nch_all = (g.K + 63) / 64, per = (nch_all + gridDim.z - 1) / gridDim.z;
+  const int cb = blockIdx.z * per;  // first K chunk of this workgroup
+  const int nch = max(0, min(per, nch_all - cb));
 #pragma unroll
   for (int st = 0; st < DEPTH; ++st)
-    if (st < nch) load(pr[st], qr[st], st * 64);
+    if (st < nch) load(pr[st], qr[st], (cb + st) * 64);
   for (int ch0 = 0; ch0 < nch; ch0 += DEPTH) {
 #pragma unroll
     for (int st = 0; st < DEPTH; ++st) {
@@ -241,7 +245,7 @@ __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) Qs[b][q][r * kMRow + c] = qr[st][q][h];
       }
-      if (ch + DEPTH < nch) load(pr[st], qr[st], (ch + DEPTH) * 64);
+      if (ch + DEPTH < nch) load(pr[st], qr[st], (cb + ch + DEPTH) * 64);
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -275,6 +279,8 @@ __global__ void __launch_bounds__(kCB) mgemm_kernel(MGemm g) {
         C[g.sc] = pt[1];
         C[2 * g.sc] = pt[2];
       }
+    } else if (OUT == 2) {
+      if (j < g.ldc) static_cast<float *>(g.C)[((size_t)blockIdx.z * g.M + i) * g.ldc + j] = acc[e];
     } else if (j < g.N) {
       static_cast<double *>(g.C)[(size_t)i * g.ldc + j] = (double)acc[e];
     }
@@ -797,8 +803,28 @@ void cholqr_pass(const double *Y, double *Q, double *G, double *R, double *Dinv,
   hipLaunchKernelGGL(trsm_kernel, dim3((d + kNb - 1) / kNb), dim3(kCB), 0, s, Y, R, Dinv, Q, d, k);
 }
 
+// C = sum of the `splits` fp32 partials [splits][count] (part stride count),
+// as three bf16 parts (part stride count).
+__global__ void __launch_bounds__(kCB) zsum_split_kernel(const float *__restrict__ part, int splits,
+                                                         uint16_t *__restrict__ C, size_t count) {
+  const size_t e = (size_t)blockIdx.x * kCB + threadIdx.x;
+  if (e >= count) return;
+  float v = part[e];
+  for (int z = 1; z < splits; ++z) v += part[(size_t)z * count + e];
+  uint16_t pt[3];
+  split3(v, pt);
+  C[e] = pt[0];
+  C[count + e] = pt[1];
+  C[2 * count + e] = pt[2];
+}
+
 // One sweep's products on the matrix cores: Z^T = V^T A^T (as three bf16
-// parts), then Y = A^T Z (fp64).
+// parts), then Y = A^T Z (fp64).  Z^T has k x n outputs over K = d: with
+// one workgroup per 64 x 64 tile that is about one workgroup per CU, whose
+// LDS writes, barrier, LDS reads and matrix products follow one another
+// with nothing to fill the gaps, so K is split in two (two workgroups per
+// CU) where the fp32 partials fit in y2, which is not in use until the
+// factorisation; a small kernel adds them and splits the sum into parts.
 void mfma_products(const CalibArgs &c, hipStream_t s) {
   MGemm g1{};
   g1.P = c.vt3;
@@ -813,7 +839,16 @@ void mfma_products(const CalibArgs &c, hipStream_t s) {
   g1.ldc = c.np;
   g1.sp = (size_t)c.k * c.dp;
   g1.sc = (size_t)c.k * c.np;
-  hipLaunchKernelGGL((mgemm_kernel<3, 1, 0, 1>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
+  constexpr int kZSplits = 2;
+  if ((uint64_t)kZSplits * c.k * c.np * sizeof(float) <= (uint64_t)c.d * c.k * sizeof(double) && c.d >= 1024) {
+    g1.C = c.y2;
+    hipLaunchKernelGGL((mgemm_kernel<3, 1, 2, 1>), dim3((c.k + 63) / 64, c.np / 64, kZSplits), dim3(kCB), 0, s, g1);
+    const size_t count = (size_t)c.k * c.np;
+    hipLaunchKernelGGL(zsum_split_kernel, dim3((unsigned)((count + kCB - 1) / kCB)), dim3(kCB), 0, s,
+                       static_cast<const float *>(static_cast<void *>(c.y2)), kZSplits, c.zt3, count);
+  } else {
+    hipLaunchKernelGGL((mgemm_kernel<3, 1, 0, 1>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
+  }
   MGemm g2{};
   g2.P = c.at;
   g2.Q = c.zt3;

@@ -41,6 +41,10 @@ def samples(d, k, n, key, gap=4.0, tail=64, frame=None):
     # bf16 samples, d a multiple of 8 (matrix-core products) with n, d and k
     # all off the 64-wide tiles, so every zero-padded edge is used
     (600, 520, 40, torch.bfloat16, 2, 2e-2),
+    # bf16 samples with the padded sample count at most d: Z^T = V^T A^T is
+    # summed over two halves of K (the second ending inside a 64-wide
+    # chunk) and k leaves a partial row tile
+    (700, 1496, 72, torch.bfloat16, 2, 2e-2),
     # bf16 samples with d not a multiple of 8 (fp32 FMA products)
     (300, 260, 24, torch.bfloat16, 2, 2e-2),
 ])
