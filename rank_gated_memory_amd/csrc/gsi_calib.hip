@@ -822,9 +822,10 @@ __global__ void __launch_bounds__(kCB) zsum_split_kernel(const float *__restrict
 // parts), then Y = A^T Z (fp64).  Z^T has k x n outputs over K = d: with
 // one workgroup per 64 x 64 tile that is about one workgroup per CU, whose
 // LDS writes, barrier, LDS reads and matrix products follow one another
-// with nothing to fill the gaps, so K is split in two (two workgroups per
-// CU) where the fp32 partials fit in y2, which is not in use until the
-// factorisation; a small kernel adds them and splits the sum into parts.
+// with nothing to fill the gaps, so K is split (up to four ways, to two
+// workgroups per CU) where the fp32 partials fit in y2, which is not in use
+// until the factorisation; a small kernel adds them and splits the sum into
+// parts.
 void mfma_products(const CalibArgs &c, hipStream_t s) {
   MGemm g1{};
   g1.P = c.vt3;
@@ -839,13 +840,24 @@ void mfma_products(const CalibArgs &c, hipStream_t s) {
   g1.ldc = c.np;
   g1.sp = (size_t)c.k * c.dp;
   g1.sc = (size_t)c.k * c.np;
-  constexpr int kZSplits = 2;
-  if ((uint64_t)kZSplits * c.k * c.np * sizeof(float) <= (uint64_t)c.d * c.k * sizeof(double) && c.d >= 1024) {
+  // K splits: 1, 2 or 4, as many as bring the grid to two workgroups per
+  // CU, fewer where the partials would not fit in y2
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int64_t tiles = (int64_t)((c.k + 63) / 64) * (c.np / 64);
+  int splits = 1;
+  while (splits < 4 && tiles * splits < 2 * cus) splits *= 2;
+  while (splits > 1 && (uint64_t)splits * c.k * c.np * sizeof(float) > (uint64_t)c.d * c.k * sizeof(double))
+    splits /= 2;
+  if (c.d < 1024) splits = 1;
+  if (splits > 1) {
     g1.C = c.y2;
-    hipLaunchKernelGGL((mgemm_kernel<3, 1, 2, 1>), dim3((c.k + 63) / 64, c.np / 64, kZSplits), dim3(kCB), 0, s, g1);
+    hipLaunchKernelGGL((mgemm_kernel<3, 1, 2, 1>), dim3((c.k + 63) / 64, c.np / 64, splits), dim3(kCB), 0, s, g1);
     const size_t count = (size_t)c.k * c.np;
     hipLaunchKernelGGL(zsum_split_kernel, dim3((unsigned)((count + kCB - 1) / kCB)), dim3(kCB), 0, s,
-                       static_cast<const float *>(static_cast<void *>(c.y2)), kZSplits, c.zt3, count);
+                       static_cast<const float *>(static_cast<void *>(c.y2)), splits, c.zt3, count);
   } else {
     hipLaunchKernelGGL((mgemm_kernel<3, 1, 0, 1>), dim3((c.k + 63) / 64, c.np / 64), dim3(kCB), 0, s, g1);
   }
