@@ -127,6 +127,36 @@ def linear(W, V, M, X, eps: float, mode: int = GATED) -> dict:
     }
 
 
+def gate_batch(V, X, eps: float, mode: int = GATED) -> dict:
+    """Gates of T tokens ([T][d]) at once (GSI-TS §2.1-§2.2), the same
+    definitions as project / residual / residual_ratio / takes_slow_path
+    written with matrix products over the token rows:
+    G = X V_k (row t is g_t), R = X - G V_k^T (row t is r_t),
+    rho_t = ||R_t|| / ||X_t||, with rho_t := 0 for a zero row and NaN for a
+    row holding NaN or Inf; slow_t = not(rho_t < eps), or the forced mode.
+    For checking long token sequences (every gate of a decode run).
+    Returns g [T][k], rho [T], slow [T] (bool).
+    """
+    X = _f64(X)
+    V = _f64(V)
+    G = X @ V
+    R = X - G @ V.T
+    nx = np.linalg.norm(X, axis=1)
+    nr = np.linalg.norm(R, axis=1)
+    finite = np.isfinite(nx) & np.isfinite(nr)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rho = np.where(nx > 0.0, nr / np.where(nx > 0.0, nx, 1.0), 0.0)
+    rho = np.where(finite, rho, np.nan)
+    if mode == FORCE_FAST:
+        slow = np.zeros(X.shape[0], dtype=bool)
+    elif mode == FORCE_SLOW:
+        slow = np.ones(X.shape[0], dtype=bool)
+    else:
+        with np.errstate(invalid="ignore"):
+            slow = ~(rho < eps)
+    return {"g": G, "rho": rho, "slow": slow}
+
+
 def linear_rows(W_rows, V, x, eps: float, mode: int = GATED) -> dict:
     """One token, outputs restricted to a subset of rows of W.
 

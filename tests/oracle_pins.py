@@ -145,11 +145,14 @@ def pin_theorem4(orc):
     res = orc.linear(W, V, M, X, eps, orc.FORCE_FAST)
     gated = orc.linear(W, V, M, X, eps)
     assert not gated["slow"].any()
+    _close(orc.spectral_norm(W), w2, 1e-12, 0, "||W||_2 vs eigenvalues of W^T W")
     for t in range(len(xs)):
         err = np.linalg.norm(res["y"][t] - np.dot(W, X[t]))
         nx = np.linalg.norm(X[t])
-        assert err <= w2 * res["rho"][t] * nx * (1 + 1e-10) + 1e-14, (t, err)
-        assert err <= w2 * eps * nx
+        b = orc.theorem4_bound(W, X[t], res["rho"][t])
+        _close(b, w2 * res["rho"][t] * nx, 1e-12, 1e-300, f"bound of token {t}")
+        assert err <= b * (1 + 1e-10) + 1e-14, (t, err, b)
+        assert err <= orc.theorem4_bound(W, X[t], eps)
     # the bound is attained when the residual lies on W's top right-singular direction
     _, s, vt = np.linalg.svd(W)
     top = vt[0] - V @ (V.T @ vt[0])
@@ -162,8 +165,82 @@ def pin_theorem4(orc):
     err = np.linalg.norm(r["y"][0] - np.dot(W2, x))
     w22 = float(np.sqrt(np.max(np.linalg.eigvalsh(W2.T @ W2))))
     bound = w22 * r["rho"][0] * np.linalg.norm(x)
+    _close(orc.theorem4_bound(W2, x, r["rho"][0]), bound, 1e-12, 0, "nearly attained bound")
     assert err <= bound * (1 + 1e-10)
     assert err >= 0.5 * bound, (err, bound)
+
+
+def pin_spectral_norm(orc):
+    """||W||_2 in closed form: max |w_ii| for a diagonal W, ||a|| ||b|| for a
+    rank-one W = a b^T, the scale for a scaled orthogonal W, and the square
+    root of the largest eigenvalue of W^T W for a Gaussian W (independent of
+    the oracle's SVD); the Theorem-4 bound is that norm times rho ||x||
+    (GSI-TS §2.2)."""
+    rng = _rng(31)
+    D = np.diag([0.5, -3.25, 2.0, 1.0, 0.0])
+    _close(orc.spectral_norm(D), 3.25, 1e-14, 0, "diagonal")
+    a, b = rng.standard_normal(7), rng.standard_normal(11)
+    _close(orc.spectral_norm(np.outer(a, b)), np.linalg.norm(a) * np.linalg.norm(b), 1e-13, 0, "rank one")
+    Q = _orthonormal(rng, 9, 9)
+    _close(orc.spectral_norm(2.5 * Q), 2.5, 1e-13, 0, "scaled orthogonal")
+    G = rng.standard_normal((13, 6))
+    _close(orc.spectral_norm(G), np.sqrt(np.max(np.linalg.eigvalsh(G.T @ G))), 1e-12, 0, "gaussian")
+    x = np.array([3.0, 0.0, 4.0, 0.0, 0.0])
+    _close(orc.theorem4_bound(D, x, 0.1), 3.25 * 0.1 * 5.0, 1e-14, 0, "bound of a diagonal map")
+    _close(orc.theorem4_bound(D, 2.0 * x, 0.1), 3.25 * 0.1 * 10.0, 1e-14, 0, "bound scales with ||x||")
+    assert orc.theorem4_bound(D, x, 0.0) == 0.0
+
+
+def pin_gate_batch(orc):
+    """The matrix form of the gate against closed forms (GSI-TS §2.1-§2.2):
+    the identity basis (g = x[:k], rho = ||x[k:]|| / ||x||), tokens inside
+    and orthogonal to the subspace (rho 0 and 1), constructed ratios, the
+    least-squares residual, a zero token (rho 0, fast), NaN and Inf tokens
+    (rho NaN, slow), the strict tie and the forced modes."""
+    rng = _rng(32)
+    d, k = 12, 4
+    I = np.eye(d)[:, :k]
+    X = rng.standard_normal((7, d))
+    X[:3, k:] *= 1e-3
+    X[5] = 0.0
+    X[6, 2] = np.inf
+    r = orc.gate_batch(I, X, 0.05)
+    _close(r["g"][:6], X[:6, :k], 1e-15, 0, "identity g")
+    want = np.array([np.linalg.norm(x[k:]) / np.linalg.norm(x) for x in X[:5]] + [0.0])
+    _close(r["rho"][:6], want, 1e-13, 0, "identity rho")
+    assert np.isnan(r["rho"][6])
+    assert list(r["slow"]) == [False, False, False, True, True, False, True], r["slow"]
+    # in span / orthogonal / constructed ratio
+    Q = _orthonormal(rng, 30, 9)
+    V, U = Q[:, :6], Q[:, 6:]
+    z = rng.standard_normal(6)
+    w = rng.standard_normal(3)
+    rhos = [0.02, 0.3]
+    toks = [V @ z, U @ w, np.full(30, np.nan)]
+    for rho in rhos:
+        c = rho * np.linalg.norm(z) / (np.linalg.norm(w) * np.sqrt(1 - rho * rho))
+        toks.append(V @ z + c * (U @ w))
+    r = orc.gate_batch(V, np.stack(toks), 0.05)
+    assert r["rho"][0] < 1e-14 and not r["slow"][0]
+    _close(r["g"][1], np.zeros(6), 0, 1e-14, "orthogonal g")
+    _close(r["rho"][1], 1.0, 1e-14, 0, "orthogonal rho")
+    assert np.isnan(r["rho"][2]) and r["slow"][2]
+    _close(r["rho"][3:], rhos, 1e-12, 0, "constructed rho")
+    assert list(r["slow"][3:]) == [False, True]
+    # least squares (brute force) on a generic basis
+    Y = rng.standard_normal((5, 30))
+    r = orc.gate_batch(V, Y, 0.05)
+    for t in range(5):
+        sol, rss, _, _ = np.linalg.lstsq(V, Y[t], rcond=None)
+        _close(r["g"][t], sol, 1e-12, 1e-14, "g vs lstsq")
+        _close(r["rho"][t], np.sqrt(rss[0]) / np.linalg.norm(Y[t]), 1e-12, 0, "rho vs lstsq")
+    # strict tie and forced modes
+    x = (V @ z + 0.01 * (U @ w))[None]
+    rho = float(orc.gate_batch(V, x, 0.5)["rho"][0])
+    assert orc.gate_batch(V, x, rho)["slow"][0]
+    assert not orc.gate_batch(V, x, float(np.nextafter(rho, np.inf)))["slow"][0]
+    assert not orc.gate_batch(V, Y, 0.05, orc.FORCE_FAST)["slow"].any()
+    assert orc.gate_batch(V, x, 0.5, orc.FORCE_SLOW)["slow"].all()
 
 
 def pin_invariance(orc):
@@ -476,4 +553,5 @@ ALL_PINS = [
     pin_decomposition, pin_theorem4, pin_invariance, pin_least_squares, pin_gate_tie,
     pin_zero_token, pin_nonfinite, pin_modes, pin_batching, pin_norm_identity, pin_nested_bases,
     pin_storage_rounding, pin_chain, pin_gram_identity, pin_dgks_orth, pin_subspace_iteration,
+    pin_spectral_norm, pin_gate_batch,
 ]

@@ -63,7 +63,49 @@ MUTANTS = {
     "dgks_single_pass": ("dgks_orth", None),
     "dgks_unnormalised": ("dgks_orth", None),
     "iteration_one_sided": ("subspace_iteration", None),
+    # Theorem-4 diagnostics: Frobenius instead of spectral norm, smallest
+    # singular value, ||x|| squared or dropped in the bound
+    "spectral_as_frobenius": ("spectral_norm", lambda W: float(np.linalg.norm(f64(W)))),
+    "spectral_smallest": ("spectral_norm", lambda W: float(np.linalg.norm(f64(W), -2))),
+    "bound_x_squared": ("theorem4_bound", lambda W, x, rho: float(np.linalg.norm(f64(W), 2)) * rho
+                        * float(np.dot(f64(x), f64(x)))),
+    "bound_drops_x": ("theorem4_bound", lambda W, x, rho: float(np.linalg.norm(f64(W), 2)) * rho),
+    "bound_frobenius": ("theorem4_bound", lambda W, x, rho: float(np.linalg.norm(f64(W))) * rho
+                        * float(np.linalg.norm(f64(x)))),
+    # matrix-form gate: dropped basis column,
+    # squared ratio, zero rows not guarded, tie sent fast, modes ignored
+    "batch_gate_drop_column": ("gate_batch", None),
+    "batch_gate_squared": ("gate_batch", None),
+    "batch_gate_no_zero_guard": ("gate_batch", None),
+    "batch_gate_tie_fast": ("gate_batch", None),
+    "batch_gate_ignores_modes": ("gate_batch", None),
 }
+
+
+def _mutant_gate_batch(how):
+    def gate_batch(V, X, eps, mode=0):
+        X, V = f64(X), f64(V)
+        Vu = V[:, :-1] if how == "drop" else V
+        G = X @ V
+        R = X - (X @ Vu) @ Vu.T
+        nx = np.linalg.norm(X, axis=1)
+        nr = np.linalg.norm(R, axis=1)
+        with np.errstate(all="ignore"):
+            if how == "noguard":
+                rho = nr / nx
+            else:
+                rho = np.where(nx > 0, nr / np.where(nx > 0, nx, 1.0), 0.0)
+            rho = np.where(np.isfinite(nx) & np.isfinite(nr), rho, np.nan)
+            if how == "squared":
+                rho = rho * rho
+            slow = (rho > eps) if how == "tie" else ~(rho < eps)
+        if how != "modes":
+            if mode == 1:
+                slow = np.zeros_like(slow)
+            elif mode == 2:
+                slow = np.ones_like(slow)
+        return {"g": G, "rho": rho, "slow": slow}
+    return gate_batch
 
 
 def _mutant_dgks(how):
@@ -166,6 +208,10 @@ def test_pins_catch_mutant(name):
         fn = _mutant_dgks("unnormalised" if name == "dgks_unnormalised" else "single")
     elif name == "iteration_one_sided":
         fn = _mutant_iteration(mod)
+    elif name.startswith("batch_gate_"):
+        fn = _mutant_gate_batch({"batch_gate_drop_column": "drop", "batch_gate_squared": "squared",
+                                 "batch_gate_no_zero_guard": "noguard", "batch_gate_tie_fast": "tie",
+                                 "batch_gate_ignores_modes": "modes"}[name])
     elif name.startswith("chain_"):
         fn = _mutant_chain(mod, {"chain_unrounded_input": "unrounded", "chain_ignores_offset": "no_offset",
                                  "chain_reads_previous_call": "previous"}[name])
