@@ -5,16 +5,24 @@ Workload (default): a GPT-J-6B-shaped stack of 28 layers x 4 linear maps
 (QKV 4096->12288, out 4096->4096, fc_in 4096->16384 with k=256, fc_out
 16384->4096 with k=512), bf16 weights, per-layer bases that follow a depth
 cascade, eps=0.05 and exactly 5% slow tokens per map over 512 synthetic
-decode steps.  One step = one token through all 112 maps (one gsi_stack
-call = a projection launch and an output launch).  Inputs are synthetic and
-resident in HBM before timing starts.
+decode steps.  One step = one token through all 112 maps: one gsi_stack
+call, i.e. one launch of stack_kernel (projection, gate and the chosen
+path's output of every map).  Inputs are synthetic and resident in HBM
+before timing starts.
 
 Prints one JSON line (rank 0, N=1):
   value        decode steps (= tokens at batch 1) per second, wall clock
-  roofline     the output kernel (apply_kernel, the larger byte mover at 5%
-               slow): algorithmic bytes per launch / mean launch time from HIP
-               events on the launch stream, against 8 TB/s
-  cpu_baseline the fp64 oracle on a bounded sample of the same workload
+  roofline     stack_kernel: algorithmic bytes per launch (averaged over the
+               timed steps) / its mean launch time from HIP events recorded
+               on the launch stream around the timed region, against 8 TB/s
+  status       the stack's device status word after the timed region and
+               after the per-launch pass (0: every wait finished; the run
+               exits with status 3 otherwise)
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
+               all host threads and on one thread
+Other workloads (--workload): the chained stack, the 13B-shaped stack, the
+batched T=256 map, single GPT-J-shaped maps at T=1, the operating-point
+sweep and the basis calibration.
 """
 from __future__ import annotations
 
@@ -200,11 +208,7 @@ def cpu_baseline_chained(wl, seconds):
 
     from oracle import gsi_oracle as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+    cores = blas_threads()
     d = 4096
     host = []
     for l in range(2):
@@ -252,6 +256,42 @@ def cpu_baseline_chained(wl, seconds):
                       f"(8 of {maps_total} maps), fp64 numpy, {el:.1f}s; step time scaled by {maps_total}/8 maps"}
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count (context of the CPU baseline)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        return os.cpu_count()
+
+
+def with_single_thread(fn, wl, seconds):
+    """fn's CPU baseline on every BLAS thread, then again limited to one thread."""
+    full = fn(wl, seconds)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = fn(wl, seconds / 2)
+        full["single_thread"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
+    except ImportError:
+        full["single_thread"] = None
+    full.update(host_cpu())
+    return full
+
+
 def cpu_baseline(wl, seconds):
     """The fp64 oracle on a bounded sample: two layers' maps, tokens in step order."""
     import numpy as np
@@ -259,11 +299,7 @@ def cpu_baseline(wl, seconds):
 
     from oracle import gsi_oracle as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+    cores = blas_threads()
     layers = wl["layers"]
     pick = [0, layers // 2] if layers > 1 else [0]
     host = []
@@ -639,18 +675,32 @@ def main():
     del a, b
     log(f"torch copy: {copy_gbps:.0f} GB/s (read+write)")
 
-    # ---- timed region: K decode steps, gated ----
+    offsets = sorted({p.status_offset for p in plans})
+
+    def status_word():
+        torch.cuda.synchronize()
+        w = 0
+        for o in offsets:
+            w |= int(ws[o:o + 4].cpu().view(torch.int32)[0])
+        return w
+
+    # ---- timed region: K decode steps, gated; HIP events on the launch stream ----
     for i in range(args.warmup):
         gsi.gsi_stack(plans[i % S], gsi.GATED, ws)
     torch.cuda.synchronize()
     K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(K):
         gsi.gsi_stack(plans[i % S], gsi.GATED, ws)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t_launch = ev0.elapsed_time(ev1) * 1e-3 / K
     tok_s = K / wall
-    log(f"gated: {K} steps in {wall * 1e3:.1f} ms -> {tok_s:.1f} tokens/s")
+    status_timed = status_word()
+    log(f"gated: {K} steps in {wall * 1e3:.1f} ms -> {tok_s:.1f} tokens/s; status word {status_timed:#x}")
 
     # gates of every (step, map): deterministic, written by every run
     slow = torch.stack([S_ for row in wl["outs"] for (_, _, S_) in row], dim=1).cpu().numpy()
@@ -660,6 +710,9 @@ def main():
     idx = np.arange(K) % S
     total_bytes = float((proj_b[idx] + apply_b[idx]).sum())
     step_gbps = total_bytes / wall / 1e9
+    step_b = proj_b[idx] + apply_b[idx]
+    stack_gbps = float(step_b.mean() / t_launch / 1e9)
+    log(f"stack_kernel mean over the timed region {t_launch * 1e6:.1f} us, {stack_gbps:.0f} GB/s")
 
     # ---- per-launch pass: HIP events around each gsi_stack on the launch stream ----
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -669,9 +722,9 @@ def main():
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     t_stack = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    step_b = proj_b[idx] + apply_b[idx]
-    stack_gbps = float(step_b.sum() / t_stack.sum() / 1e9)
-    log(f"stack_kernel mean {t_stack.mean() * 1e6:.1f} us, {stack_gbps:.0f} GB/s")
+    status_pass = status_word()
+    log(f"per-launch events: stack_kernel mean {t_stack.mean() * 1e6:.1f} us, "
+        f"{float(step_b.sum() / t_stack.sum() / 1e9):.0f} GB/s; status word {status_pass:#x}")
     two_launch = None
     if not chained:
         # the same steps as two launches (projection, then outputs): context
@@ -724,8 +777,9 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = (cpu_baseline_chained if chained else cpu_baseline)(wl, args.cpu_seconds)
-        log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+        cpu = with_single_thread(cpu_baseline_chained if chained else cpu_baseline, wl, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads, "
+            f"{(cpu['single_thread'] or {}).get('value', float('nan')):.3f} on one ({cpu['model']})")
 
     maps_per_step = sum(len(r) for r in wl["data"])
     out = {
@@ -752,8 +806,11 @@ def main():
             "layers": wl["layers"],
             "maps": [[n, d, o, k] for n, d, o, k in wl["roles"]],
             "distinct_steps": S,
-            "slow_share": float(slow.mean()),
+            "timed_steps": K,
+            # share of slow calls over the steps the timed region ran
+            "slow_share": float(slow[idx].mean()),
         },
+        "status": {"timed": status_timed, "per_launch_pass": status_pass},
         "hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "bytes_per_step": total_bytes / K,
@@ -767,7 +824,8 @@ def main():
             "traffic": measured_traffic(args.workload + ("-shared" if args.shared_bases else ""),
                                         "stack_kernel"),
             "bytes_per_launch": float(step_b.mean()),
-            "mean_launch_us": float(t_stack.mean() * 1e6),
+            "mean_launch_us": float(t_launch * 1e6),
+            "per_launch_events_mean_us": float(t_stack.mean() * 1e6),
         },
         "two_launch": two_launch,
         "dense_tokens_per_s": dense_tok_s,
@@ -777,6 +835,9 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    if status_timed or status_pass:
+        log("a device-side wait ran out during the run: the outputs were incomplete, the figures invalid")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

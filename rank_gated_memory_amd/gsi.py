@@ -12,7 +12,9 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_void_p
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsi.so")
+# GSI_LIBRARY names another build of the same library (the host-sanitizer
+# build of build.build_sanitized, for the CPU-side argument tests).
+LIB_PATH = os.environ.get("GSI_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsi.so")
 
 GSI_FP32, GSI_BF16 = 0, 1
 GATED, FORCE_FAST, FORCE_SLOW = 0, 1, 2
@@ -242,17 +244,42 @@ class Stack:
         o = self.status_offset
         return int(ws[o:o + 4].cpu().view(torch.int32)[0])
 
-    def run(self, mode: int = GATED, ws=None, stream=None):
+    def run(self, mode: int = GATED, ws=None, stream=None, check: bool = False):
+        """Enqueue the plan's launch; with check=True wait for the stream and
+        raise StackIncomplete if the launch left its status word set."""
         if ws is None:
             ws = workspace(self.ws_bytes, self.dev.device)
-        gsi_stack(self, mode, ws, stream)
+        gsi_stack(self, mode, ws, stream, check=check)
         return ws
 
 
-def gsi_stack(plan: Stack, mode: int, ws: torch.Tensor, stream=None):
+class StackIncomplete(RuntimeError):
+    """A stack launch ended with a device-side wait that ran out of its bound:
+    the outputs of that run are incomplete (include/gsi.h, gsi_stack)."""
+
+    def __init__(self, word: int):
+        self.word = word
+        super().__init__(f"gsi_stack: a device-side wait ran out (status word {word:#x}); outputs incomplete")
+
+
+def gsi_stack(plan: Stack, mode: int, ws: torch.Tensor, stream=None, check: bool = False):
+    """Run a plan (one launch).  gsi_stack returns GSI_OK once the launch is
+    enqueued; whether every device-side wait finished is only known from the
+    workspace's status word after the stream has run, which check=True
+    reads (synchronising the stream) and turns into StackIncomplete."""
     st = lib().gsi_stack(_ptr(plan.host), _ptr(plan.dev), int(mode), _ptr(ws),
                          ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "gsi_stack")
+    if check:
+        if stream is None:
+            torch.cuda.current_stream().synchronize()
+        elif hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize()
+        word = plan.status(ws)
+        if word != 0:
+            raise StackIncomplete(word)
 
 
 def gsi_stack_phase(plan: Stack, mode: int, phase: int, ws: torch.Tensor, stream=None):

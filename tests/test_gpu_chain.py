@@ -174,14 +174,13 @@ def test_exhausted_wait_bound_drains_and_recovers(monkeypatch):
     st, outs, calls = build_chain(torch.float32, layers=3, chains=4)
     ws = gsi.workspace(st.ws_bytes, DEV)
     monkeypatch.setenv("GSI_SPIN_LIMIT", "0")
-    gsi.gsi_stack(st, gsi.GATED, ws)
-    sync()
+    with pytest.raises(gsi.StackIncomplete):
+        gsi.gsi_stack(st, gsi.GATED, ws, check=True)
     assert st.status(ws) != 0, "no wait ran out with a zero bound"
     ws[st.status_offset:st.status_offset + 4] = 0
     monkeypatch.delenv("GSI_SPIN_LIMIT")
     for o in outs:
         o[3].fill_(float("nan"))
-    gsi.gsi_stack(st, gsi.GATED, ws)
-    sync()
+    gsi.gsi_stack(st, gsi.GATED, ws, check=True)
     assert st.status(ws) == 0
     check_chain(outs, orc.chain(calls, "fp32"), torch.float32, "after recovery")
