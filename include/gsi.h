@@ -140,6 +140,30 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
                       int32_t mode, float *rho, uint8_t *slow, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* ---- gsi_linear without caller memory ----
+ * For callers that cannot allocate: code under HIP graph capture, serving
+ * loops that may not call hipMalloc, harnesses that forbid allocation.
+ * gsi_linear_static is gsi_linear (same kernels, same results) with its
+ * workspace in a device array of the library, GSI_STATIC_SCRATCH_BYTES
+ * (64 MiB) per device, held from library load until the process ends.  It
+ * allocates nothing and calls no allocating routine.
+ *   - A call whose gsi_linear_workspace(map, T) exceeds the array returns
+ *     GSI_E_WORKSPACE and enqueues nothing (e.g. T = 256 fits up to
+ *     d = 16384, k = 512; larger batches can be split by the caller).
+ *   - Each call first clears the part of the array it uses with a fill
+ *     kernel on `stream` (no memset node), then enqueues gsi_linear's
+ *     kernels; all arguments but the workspace are as for gsi_linear.
+ *   - Every call on one device shares that device's array: calls that may
+ *     overlap on one device (different streams without ordering) race and
+ *     must not be issued. */
+#define GSI_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* Bytes of the library's device array (GSI_STATIC_SCRATCH_BYTES). */
+size_t gsi_static_scratch_bytes(void);
+
+gsi_status gsi_linear_static(const gsi_map *map, const void *x, void *y, int32_t T, float eps,
+                             int32_t mode, float *rho, uint8_t *slow, void *stream);
+
 /* ---- stacks: every linear map of a decode step in one launch (GSI-TS §3) ----
  * A stack plan is built once on the host from an array of calls and copied
  * by the caller to device memory; running the plan is one kernel launch.

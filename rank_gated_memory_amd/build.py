@@ -8,7 +8,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "gsi_api.cpp"), os.path.join(PKG, "csrc", "gsi_kernels.hip"),
-           os.path.join(PKG, "csrc", "gsi_batched.hip"), os.path.join(PKG, "csrc", "gsi_calib.hip")]
+           os.path.join(PKG, "csrc", "gsi_batched.hip"), os.path.join(PKG, "csrc", "gsi_calib.hip"),
+           os.path.join(PKG, "csrc", "gsi_noalloc.hip")]
 OUT = os.path.join(PKG, "libgsi.so")
 
 COMMON = [

@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.gsi_calibrate_status_offset.argtypes = []
         L.gsi_calibrate.restype = c_int32
         L.gsi_calibrate.argtypes = [POINTER(GsiCalibStruct), c_void_p, c_size_t, c_void_p]
+        L.gsi_static_scratch_bytes.restype = c_size_t
+        L.gsi_static_scratch_bytes.argtypes = []
+        L.gsi_linear_static.restype = c_int32
+        L.gsi_linear_static.argtypes = [POINTER(GsiMapStruct), c_void_p, c_void_p, c_int32, c_float,
+                                        c_int32, c_void_p, c_void_p, c_void_p]
         L.gsi_stack_phase.restype = c_int32
         L.gsi_stack_phase.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
                                       c_void_p]
@@ -206,6 +211,33 @@ def gsi_linear(m: Map, x: torch.Tensor, eps: float, mode: int = GATED, y=None, r
                           _stream(stream))
     _check(st, "gsi_linear")
     return y, rho, slow
+
+
+def gsi_linear_static(m: Map, x: torch.Tensor, eps: float, mode: int = GATED, y=None, rho=None,
+                      slow=None, stream=None):
+    """gsi_linear with the library's own device scratch (no workspace, no
+    allocation by the library); y, rho and slow are allocated here only if
+    not given."""
+    if x.dim() == 1:
+        x = x[None]
+    T = x.shape[0]
+    if x.dtype != m.W.dtype or not x.is_contiguous() or x.shape[1] != m.d:
+        raise ValueError("x must be a contiguous [T][d] tensor in the map's dtype")
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, m.d_out), dtype=x.dtype, device=dev)
+    if rho is None:
+        rho = torch.empty(T, dtype=torch.float32, device=dev)
+    if slow is None:
+        slow = torch.empty(T, dtype=torch.uint8, device=dev)
+    st = lib().gsi_linear_static(ctypes.byref(m.struct), _ptr(x), _ptr(y), int(T), float(eps), int(mode),
+                                 _ptr(rho), _ptr(slow), _stream(stream))
+    _check(st, "gsi_linear_static")
+    return y, rho, slow
+
+
+def gsi_static_scratch_bytes() -> int:
+    return int(lib().gsi_static_scratch_bytes())
 
 
 class Stack:
