@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default="gptj6b-28L",
                    choices=["gptj6b-28L", "gptj6b-28L-chained", "llama13b-40L", "batched-t256", "sweep",
-                            "calibrate-gptj6b-28L"])
+                            "calibrate-gptj6b-28L", "gptj-maps-t1"])
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--exact-rho", action="store_true",
                    help="every map caches E = V^T V - I and gates on the exact residual ratio")
@@ -359,8 +359,14 @@ def bench_batched(args):
 
     Prints one JSON line: tokens/s per cell (whole gsi_linear call: projection
     GEMM, gate, compacted fast and slow GEMMs), algorithmic GB/s, and the
-    matrix-core fraction of the whole call at each cell.
+    matrix-core fraction of the whole call at each cell.  Each cell is timed
+    twice: cache-hot (the same map and tokens every call: the ~155 MB
+    working set of a call fits in the 256 MB MALL) and rotated (call i reads
+    replica i mod R of V_k, M and X and replica i mod R_w of W, >= 1 GB of
+    each, so every call reads its bytes from HBM); the rotated figure is the
+    HBM one.
     """
+    import numpy as np
     import torch
 
     from rank_gated_memory_amd import gsi, synth
@@ -371,6 +377,7 @@ def bench_batched(args):
     if args.cells:
         grid = [(int(c.split(":")[0]), float(c.split(":")[1])) for c in args.cells.split(",")]
     prep = []
+    GB = 1.0e9
     for k, frac in grid:
         mi = synth.config5(k, frac, device=dev, w_device=dev)
         m = gsi.Map(mi.W, mi.V)
@@ -395,42 +402,236 @@ def bench_batched(args):
         rho = torch.empty(T, device=dev)
         sl = torch.empty(T, dtype=torch.uint8, device=dev)
         ws = gsi.workspace(gsi.gsi_linear_workspace(m, T), dev)
-        for _ in range(args.warmup):
-            gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+        gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / args.steps * 1e3
         ns = int(sl.sum())
         nf = T - ns
         d, do = mi.d, mi.d_out
         byts = 2 * (d * k + T * d + T * do) + (2 * do * k if nf else 0) + (2 * d * do if ns else 0)
         flops = 2 * T * d * k + 2 * 2 * nf * do * k + 2 * ns * d * do
+        # replicas for the rotated timing
+        vmx = mi.V.numel() * 2 + m.M.numel() + mi.X.numel() * 2
+        R = int(min(256, max(2, np.ceil(1.0 * GB / vmx))))
+        Rw = int(max(2, np.ceil(1.0 * GB / (mi.W.numel() * 2)))) if ns else 1
+        Ws = [mi.W] + replicas(mi.W, Rw - 1)
+        Vs = [mi.V] + replicas(mi.V, R - 1)
+        Ms = [m.M] + replicas(m.M, R - 1)
+        Xs = [mi.X] + replicas(mi.X, R - 1)
+        rot = [gsi.Map(Ws[j % Rw], Vs[j], M=Ms[j]) for j in range(R)]
+        timing = {}
+        for place in ("hot", "rotated"):
+            def call(i):
+                if place == "hot":
+                    gsi.gsi_linear(m, mi.X, 0.05, y=y, rho=rho, slow=sl, ws=ws)
+                else:
+                    gsi.gsi_linear(rot[i % R], Xs[i % R], 0.05, y=y, rho=rho, slow=sl, ws=ws)
+            for i in range(args.warmup):
+                call(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                call(i)
+            e1.record()
+            torch.cuda.synchronize()
+            timing[place] = e0.elapsed_time(e1) / args.steps * 1e3
+            assert int(sl.sum()) == ns, "gates changed between replicas"
+        us = timing["rotated"]
         cells.append({"k": k, "slow_share": frac, "slow_tokens": ns, "us_per_call": us,
                       "tokens_per_s": T / (us * 1e-6), "gbps": byts / us / 1e3,
-                      "tflops": flops / us / 1e6, "mfma_frac": flops / us / 1e6 / PEAK_BF16_TFLOPS})
-        log(f"k={k} slow={frac}: {us:.1f} us, {T / us * 1e6:.0f} tokens/s")
-        del m, mi, ws, y
+                      "tflops": flops / us / 1e6, "mfma_frac": flops / us / 1e6 / PEAK_BF16_TFLOPS,
+                      "bytes_per_call": byts, "replicas": [R, Rw],
+                      "hot_us_per_call": timing["hot"], "hot_gbps": byts / timing["hot"] / 1e3})
+        log(f"k={k} slow={frac}: rotated {us:.1f} us ({byts / us / 1e3:.0f} GB/s), "
+            f"cache-hot {timing['hot']:.1f} us, {T / us * 1e6:.0f} tokens/s")
+        del m, mi, ws, y, rot, Ws, Vs, Ms, Xs
+        torch.cuda.empty_cache()
     heads = [c for c in cells if c["k"] == 256 and c["slow_share"] == 0.1]
     head = heads[0] if heads else cells[0]
+    cpu = None if args.no_cpu else with_single_thread(cpu_baseline_batched, head, args.cpu_seconds)
     print(json.dumps({
         "metric": "GSI batched gated linear tokens/s (T=256, d=4096 -> 16384)",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["us_per_call"] / 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "batched-t256: T=256, d=4096, d_out=16384, value at k=256, 10% slow",
+        "config": {"workload": "batched-t256: T=256, d=4096, d_out=16384, value at k=256, 10% slow, "
+                               "calls rotated over >= 1 GB of map and token replicas",
                    "cells": cells, "prepare": prep},
         # the whole gsi_linear call of the head cell (projection GEMM, gate,
-        # wide and row-streaming output kernels) against the HBM roof: its
-        # algorithmic bytes (V_k, X, Y, M once if any token is fast, W once
-        # if any is slow) over the call time
+        # output kernels) against the HBM roof: its algorithmic bytes (V_k,
+        # X, Y, M once if any token is fast, W once if any is slow) over the
+        # rotated call time
         "roofline": {"bound": "hbm", "kernel": "gsi_linear (bproj, bgate, bout, bthin)",
                      "achieved": head["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_HBM_GBPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
+def cpu_baseline_batched(head, seconds):
+    """The fp64 oracle on the head cell's map (k=256, 10 % slow): its tokens
+    one by one through orc.linear_token until the time budget is spent."""
+    import torch
+
+    from oracle import gsi_oracle as orc
+    from rank_gated_memory_amd import synth
+
+    mi = synth.config5(head["k"], head["slow_share"], device="cpu", w_device="cpu")
+    W = mi.W.double().numpy()
+    V = mi.V.double().numpy()
+    M = orc.prepare(W, V)
+    X = mi.X.double().numpy()
+    cores = blas_threads()
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        orc.linear_token(W, V, M, X[done % X.shape[0]], 0.05)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} tokens of the k={head['k']}, {head['slow_share'] * 100:.0f}%-slow cell "
+                      f"(the same recipe drawn on the host; tokens in order, wrapping), one token at "
+                      f"a time, fp64 numpy, {el:.1f}s"}
+
+
+def replicas(t, n):
+    """n independent copies of tensor t (same values, distinct memory)."""
+    return [t.clone() for _ in range(n)]
+
+
+def bench_single_maps(args):
+    """Each GPT-J-shaped map alone at batch 1: 1000 sequential single-token
+    gsi_linear calls (50 slow at seeded positions, eps = 0.05), per map.
+
+    Two placements of the map's bytes:
+      * cache-hot: every call reads the same V_k, M (and W for the slow
+        tokens); M + V_k of a map (4-21 MB) stay in the 256 MB MALL, so this
+        is not an HBM figure;
+      * rotated: token t reads replica t mod R of (V_k, M) and replica
+        t mod R mod R_w of W, the replicas together >= 1 GB for each of the
+        two kinds, so successive calls miss the caches: the HBM figure.
+    Each placement runs its 1000 calls issued from the host one by one, and
+    as one captured HIP graph (the graph's replays are checked bitwise
+    against the eager outputs).  Two entry points: gsi_linear at T = 1 (a
+    projection launch and an output launch per token) and, rotated, a
+    one-call gsi_stack plan per token (one launch per token).  Bytes per token: 2k(d + d_out) + 2d + 2d_out
+    fast, + 2 d d_out slow.  The dense line is the same calls forced slow.
+    """
+    import numpy as np
+    import torch
+
+    from rank_gated_memory_amd import accounting as acc
+    from rank_gated_memory_amd import gsi, synth
+
+    dev = torch.device("cuda:0")
+    T, eps = 1000, 0.05
+    GB = 1.0e9
+    results = []
+    stream = torch.cuda.Stream()
+    for role in synth.GPTJ_MAPS:
+        mi = synth.config2(T=T, device=dev, w_device=dev, maps=[role])[0]
+        base = gsi.Map(mi.W, mi.V)
+        gsi.gsi_prepare(base)
+        vm_bytes = base.V.numel() * 2 + base.M.numel()
+        R = max(1, int(np.ceil(1.0 * GB / vm_bytes)))
+        Rw = max(1, int(np.ceil(1.0 * GB / (mi.W.numel() * 2))))
+        Ws = [mi.W] + replicas(mi.W, Rw - 1)
+        Vs = [mi.V] + replicas(mi.V, R - 1)
+        Ms = [base.M] + replicas(base.M, R - 1)
+        rot = [gsi.Map(Ws[j % Rw], Vs[j], M=Ms[j]) for j in range(R)]
+        y = torch.empty((T, mi.d_out), dtype=torch.bfloat16, device=dev)
+        rho = torch.empty(T, dtype=torch.float32, device=dev)
+        sl = torch.empty(T, dtype=torch.uint8, device=dev)
+        ws = gsi.workspace(gsi.gsi_linear_workspace(base, 1), dev)
+
+        plans = {}
+        for place, maps_of in (("hot", lambda t: base), ("rotated", lambda t: rot[t % R])):
+            plans[place] = [gsi.Stack([(maps_of(t), mi.X[t], y[t], eps, rho[t:t + 1], sl[t:t + 1])], device=dev)
+                            for t in range(T)]
+        ws1 = gsi.workspace(max(p.ws_bytes for pl in plans.values() for p in pl), dev)
+
+        def issue(maps_of, mode=gsi.GATED, kind="gsi_linear", place="hot"):
+            if kind == "gsi_stack":
+                for t in range(T):
+                    gsi.gsi_stack(plans[place][t], mode, ws1, stream=stream)
+                return
+            for t in range(T):
+                gsi.gsi_linear(maps_of(t), mi.X[t:t + 1], eps, mode=mode, y=y[t:t + 1], rho=rho[t:t + 1],
+                               slow=sl[t:t + 1], ws=ws, stream=stream)
+
+        cell = {"map": role[0], "d": mi.d, "d_out": mi.d_out, "k": mi.k, "tokens": T,
+                "replicas_vk_m": R, "replicas_w": Rw}
+        for place, maps_of, kind in (("hot", lambda t: base, "gsi_linear"),
+                                     ("rotated", lambda t: rot[t % R], "gsi_linear"),
+                                     ("rotated", lambda t: rot[t % R], "gsi_stack")):
+            for mode, tag in ((gsi.GATED, "gated"), (gsi.FORCE_SLOW, "dense")):
+                with torch.cuda.stream(stream):
+                    issue(maps_of, mode, kind, place)
+                    stream.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    issue(maps_of, mode, kind, place)
+                    e1.record(stream)
+                    stream.synchronize()
+                eager_us = e0.elapsed_time(e1) * 1e3 / T
+                ref = (y.clone(), rho.clone(), sl.clone())
+                slow = ref[2].cpu().numpy().astype(bool)
+                byts = sum(acc.token_bytes(mi.d, mi.d_out, mi.k, 2, bool(s_)) for s_ in slow)
+                # the same calls captured once as a graph, replayed
+                g = torch.cuda.CUDAGraph()
+                y.zero_()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=stream):
+                    issue(maps_of, mode, kind, place)
+                reps = 3
+                ok = True
+                times = []
+                for _ in range(reps):
+                    y.zero_()
+                    sl.fill_(7)
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    with torch.cuda.stream(stream):
+                        # the graph's kernels run on the stream it is replayed on
+                        e0.record(stream)
+                        g.replay()
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) * 1e3 / T)
+                    ok = ok and torch.equal(y.view(torch.int16), ref[0].view(torch.int16)) and torch.equal(sl, ref[2])
+                del g
+                graph_us = float(np.median(times))
+                key = f"{place}_{tag}" + ("_single_launch" if kind == "gsi_stack" else "")
+                cell[key] = {"us_per_token_eager": eager_us, "us_per_token_graph": graph_us,
+                             "slow_tokens": int(slow.sum()), "bytes_per_token": byts / T,
+                             "gbps_graph": byts / T / graph_us / 1e3,
+                             "hbm_frac_graph": byts / T / graph_us / 1e3 / PEAK_HBM_GBPS,
+                             "graph_replays_match_eager": bool(ok)}
+                log(f"{role[0]} {key}: eager {eager_us:.2f} us/token, graph {graph_us:.2f} us/token, "
+                    f"{byts / T / graph_us / 1e3:.0f} GB/s, replays match {ok}")
+                if not ok:
+                    raise SystemExit(f"graph replay of {role[0]} {key} differs from the eager outputs")
+        cell["speedup_vs_dense_rotated_graph"] = (cell["rotated_dense"]["us_per_token_graph"]
+                                                 / cell["rotated_gated"]["us_per_token_graph"])
+        results.append(cell)
+        del rot, Ws, Vs, Ms, base, mi, y, ws, plans, ws1
+        torch.cuda.empty_cache()
+    qkv = results[0]
+    print(json.dumps({
+        "metric": "GSI single-map batch-1 latency: us per token per GPT-J-shaped map (rotated, HBM)",
+        "value": qkv["rotated_gated"]["us_per_token_graph"], "unit": "us/token", "n_gpus": 1, "steps": T,
+        "warmup": T, "ms_per_step": qkv["rotated_gated"]["us_per_token_graph"] / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gptj-maps-t1: QKV 4096->12288, out 4096->4096, fc_in 4096->16384 (k=256), "
+                               "fc_out 16384->4096 (k=512); 1000 sequential single-token calls per map, "
+                               "50 slow, eps=0.05; value: QKV, rotated over >= 1 GB of replicas, graph replay",
+                   "maps": results},
+        "roofline": {"bound": "hbm", "kernel": "gsi_linear T=1 (proj_kernel + apply_kernel)",
+                     "achieved": qkv["rotated_gated"]["gbps_graph"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": qkv["rotated_gated"]["hbm_frac_graph"], "traffic": None},
     }), flush=True)
 
 
@@ -637,6 +838,9 @@ def main():
         return
     if args.workload == "sweep":
         bench_sweep(args)
+        return
+    if args.workload == "gptj-maps-t1":
+        bench_single_maps(args)
         return
     if args.workload == "calibrate-gptj6b-28L":
         bench_calibrate(args)

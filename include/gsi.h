@@ -178,7 +178,16 @@ gsi_status gsi_linear_static(const gsi_map *map, const void *x, void *y, int32_t
  * dependency-chained stack such as the layers of a decoder: the QKV and
  * fc_in maps of a GPT-J block in one wave, out and fc_out in the next).
  * The barriers between waves are kept on the device (no host round trip).
- * With every wave number equal, all calls are independent. */
+ * With every wave number equal, all calls are independent.
+ *
+ * Why a plan, and why batch 1: a decode step runs the same maps on the same
+ * buffers every token, so the call array is validated and laid out once
+ * (gsi_stack_plan) and each step is then a single launch with no host-side
+ * work (gsi_stack).  A call is one token: at batch 1 every map's bytes are
+ * only microseconds of HBM time, so the maps of a step have to overlap in
+ * one persistent launch.  For T >= 2 tokens per map, gsi_linear's batched
+ * path reads each map once for all its tokens; T tokens through n maps with
+ * batch-1 semantics are n * T calls of one plan. */
 
 /* Bytes of the host plan for these n calls (0 if n < 0 or n > 4096, or if
  * a call is invalid; gsi_stack_plan reports which check failed). */

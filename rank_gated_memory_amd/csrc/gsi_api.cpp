@@ -71,22 +71,9 @@ int cu_count() {
   return cached[dev];
 }
 
-// Bytes of V_k one projection unit aims at, given the total projection
-// bytes of a launch: enough units to fill 256 CUs several times over, each
-// large enough to keep a workgroup streaming.
-#ifndef GSI_PROJ_UNIT_KB
-#define GSI_PROJ_UNIT_KB 768
-#endif
 #ifndef GSI_APPLY_BLOCKS_PER_CU
 #define GSI_APPLY_BLOCKS_PER_CU 32
 #endif
-
-int64_t proj_target_bytes(int64_t total_v_bytes) {
-  int64_t t = total_v_bytes / (256 * 4);
-  if (t < 16 * 1024) t = 16 * 1024;
-  if (t > GSI_PROJ_UNIT_KB * 1024) t = GSI_PROJ_UNIT_KB * 1024;
-  return t;
-}
 
 struct WsLayout {
   uint64_t gate_off, need_off, pref_off, float_off, ctl_off, gcnt_off, total;
@@ -169,10 +156,62 @@ gsi_status gsi_prepare(const gsi_map *map, void *stream) {
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;
 }
 
-static uint64_t linear_ws_bytes(const gsi_map *map, int64_t n) {
+// Bytes of V_k per projection unit of a stack plan: small enough that the
+// gates of a step open progressively (output work overlaps projection in
+// the single launch), large enough to amortise a unit's partial hand-off.
+#ifndef GSI_PLAN_PROJ_UNIT_KB
+#define GSI_PLAN_PROJ_UNIT_KB 384
+#endif
+static int64_t plan_proj_target(int64_t total_v_bytes) {
+  int64_t t = total_v_bytes / (256 * 4);
+  if (t < 16 * 1024) t = 16 * 1024;
+  if (t > GSI_PLAN_PROJ_UNIT_KB * 1024) t = GSI_PLAN_PROJ_UNIT_KB * 1024;
+  return t;
+}
+
+// Unit shapes of every call of a (validated) plan, chosen wave by wave.
+// A wave's projection units aim at (its V_k bytes) / 1024, clamped to
+// [16 KiB, GSI_PLAN_PROJ_UNIT_KB], and at most kMaxPartials per call (the
+// final sum of a call's partials is then one round of loads).  A wave whose fast
+// outputs make fewer than kFineUnits ordinary units is latency-bound (the
+// waves of a dependency-chained stack): it takes the smallest output units.
+constexpr int64_t kFineUnits = 1024;
+#ifndef GSI_PLAN_MAX_PARTIALS
+#define GSI_PLAN_MAX_PARTIALS 64
+#endif
+constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
+constexpr int64_t kTwoLevelUnitBytes = 64 * 1024;
+constexpr int64_t kMaxPartials2 = 256;
+
+// Unit shape of one call in a wave whose projection bytes total `wave_vbytes`
+// and whose fast outputs make `wave_fast_units` ordinary units (the rule
+// above).
+static UnitShape shape_in_wave(int32_t d, int32_t d_out, int32_t k, int es, int64_t wave_vbytes,
+                               int64_t wave_fast_units) {
+  const int64_t t = plan_proj_target(wave_vbytes);
+  const bool fine = wave_fast_units < kFineUnits;
+  const int64_t vi = (int64_t)d * k * es;
+  int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
+  // Where the cap of kMaxPartials one-level partials would make the units
+  // larger than the wave's target and than kTwoLevelUnitBytes (a wide V_k in
+  // a latency-bound wave), up to kMaxPartials2 smaller units are summed in
+  // two levels instead.
+  if (ti > t && ti > kTwoLevelUnitBytes)
+    ti = std::max<int64_t>({t, kTwoLevelUnitBytes, (vi + kMaxPartials2 - 1) / kMaxPartials2});
+  return unit_shape(d, d_out, k, es, ti, fine);
+}
+
+// Unit shape of the n tokens of one map in the batch-1 kernels: the n tokens
+// are n calls of one wave, shaped as a stack plan would shape them (a few
+// tokens are latency-bound and take the small units).
+static UnitShape linear_shape(const gsi_map *map, int64_t n) {
   const int es = esize_of(map->dtype);
-  const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
-                                  proj_target_bytes((int64_t)map->d * map->k * es * n));
+  const int64_t coarse = unit_shape(map->d, map->d_out, map->k, es, 1 << 20).fast_units;
+  return shape_in_wave(map->d, map->d_out, map->k, es, (int64_t)map->d * map->k * es * n, coarse * n);
+}
+
+static uint64_t linear_ws_bytes(const gsi_map *map, int64_t n) {
+  const UnitShape us = linear_shape(map, n);
   return ws_layout(n, n * (us.g_floats + us.part_floats), 0, n * us.a_units).total;
 }
 
@@ -258,8 +297,7 @@ gsi_status gsi_linear(const gsi_map *map, const void *x, void *y, int32_t T, flo
   // launch reuses the same workspace (stream order separates them).
   for (int32_t t0 = 0; t0 < T; t0 += kMaxCalls) {
     const int32_t n = (T - t0) < kMaxCalls ? (T - t0) : kMaxCalls;
-    const UnitShape us = unit_shape(map->d, map->d_out, map->k, es,
-                                    proj_target_bytes((int64_t)map->d * map->k * es * n));
+    const UnitShape us = linear_shape(map, n);
     const WsLayout wl = ws_layout(n, n * (us.g_floats + us.part_floats), 0, n * us.a_units);
     KArgs a{};
     a.table = nullptr;
@@ -346,33 +384,6 @@ static gsi_status check_wave_aliasing(const gsi_call *calls, int32_t b, int32_t 
   return GSI_OK;
 }
 
-// Bytes of V_k per projection unit of a stack plan: small enough that the
-// gates of a step open progressively (output work overlaps projection in
-// the single launch), large enough to amortise a unit's partial hand-off.
-#ifndef GSI_PLAN_PROJ_UNIT_KB
-#define GSI_PLAN_PROJ_UNIT_KB 384
-#endif
-static int64_t plan_proj_target(int64_t total_v_bytes) {
-  int64_t t = total_v_bytes / (256 * 4);
-  if (t < 16 * 1024) t = 16 * 1024;
-  if (t > GSI_PLAN_PROJ_UNIT_KB * 1024) t = GSI_PLAN_PROJ_UNIT_KB * 1024;
-  return t;
-}
-
-// Unit shapes of every call of a (validated) plan, chosen wave by wave.
-// A wave's projection units aim at (its V_k bytes) / 1024, clamped to
-// [16 KiB, GSI_PLAN_PROJ_UNIT_KB], and at most kMaxPartials per call (the
-// final sum of a call's partials is then one round of loads).  A wave whose fast
-// outputs make fewer than kFineUnits ordinary units is latency-bound (the
-// waves of a dependency-chained stack): it takes the smallest output units.
-constexpr int64_t kFineUnits = 1024;
-#ifndef GSI_PLAN_MAX_PARTIALS
-#define GSI_PLAN_MAX_PARTIALS 64
-#endif
-constexpr int64_t kMaxPartials = GSI_PLAN_MAX_PARTIALS;
-constexpr int64_t kTwoLevelUnitBytes = 64 * 1024;
-constexpr int64_t kMaxPartials2 = 256;
-
 // For each call, the earlier call of the same wave whose projection it
 // shares (same x, V_k, E, d and k: g, ||x|| and rho are then the same), or -1.
 static std::vector<int32_t> share_owners(const gsi_call *calls, int32_t n) {
@@ -401,18 +412,8 @@ static std::vector<UnitShape> call_shapes(const gsi_call *calls, int32_t n, int 
       if (owner[i] < 0) vbytes += (int64_t)calls[i].map.d * calls[i].map.k * es;
       fast_units += unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, 1 << 20).fast_units;
     }
-    const int64_t t = plan_proj_target(vbytes);
-    const bool fine = fast_units < kFineUnits;
     for (int32_t i = b; i < e; ++i) {
-      const int64_t vi = (int64_t)calls[i].map.d * calls[i].map.k * es;
-      int64_t ti = std::max<int64_t>(t, (vi + kMaxPartials - 1) / kMaxPartials);
-      // Where the cap of kMaxPartials one-level partials would make the
-      // units larger than the wave's target and than kTwoLevelUnitBytes
-      // (a wide V_k in a latency-bound wave), up to kMaxPartials2 smaller
-      // units are summed in two levels instead.
-      if (ti > t && ti > kTwoLevelUnitBytes)
-        ti = std::max<int64_t>({t, kTwoLevelUnitBytes, (vi + kMaxPartials2 - 1) / kMaxPartials2});
-      shapes[i] = unit_shape(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, ti, fine);
+      shapes[i] = shape_in_wave(calls[i].map.d, calls[i].map.d_out, calls[i].map.k, es, vbytes, fast_units);
       if (owner[i] >= 0) {  // projected by its owner
         shapes[i].a_units = 0;
         shapes[i].groups = 1;
