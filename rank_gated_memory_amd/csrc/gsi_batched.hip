@@ -445,7 +445,8 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
   }
 }
 
-// LDS of the wide kernel, sized for the fast path (two A matrices).
+// LDS of the wide kernel, sized for the fast path (two A matrices); the
+// fast items of wide_fast_item use Bs and As as one block.
 struct OutLds {
   u32x4_t Bs[2][8][64];                          // double-buffered 64-wide K chunk: [k group][column]
   u32x4_t As[kOutWaves][2 * kOutTok * kOutArow];  // each wavefront's A chunk
@@ -539,20 +540,170 @@ __device__ __forceinline__ void bout_path(const BArgs &a, OutLds &L, int tile, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide fast path (more than kThin fast tokens): Y_f = G_f M^T with g as the
+// two bf16 planes hi + lo.  K is small (k <= 1024), so an item is built to
+// have all of its loads in flight in a few rounds, not one round per 64 of
+// k.  An item is 64 fast tokens x 256 output rows: each of the eight
+// wavefronts owns 32 rows (one MFMA column block of a 64-row image tile)
+// for the 64 tokens (two 32-row blocks), v_mfma_f32_32x32x16_bf16.  The
+// tiled image is already in B-operand order (32 lanes read 512 contiguous
+// bytes of one k group), so M goes straight into registers, eight k-steps
+// of 16 per stage, the next stage in flight while one is multiplied.  g's
+// planes for the 64 tokens go through LDS 256 of k per pass (coalesced
+// 512-byte token rows), stored as [plane][k group][token ^ k group] so that
+// the stores and the operand reads (32 consecutive tokens of one k group)
+// spread over the banks.
+// ---------------------------------------------------------------------------
+constexpr int kWideTok = 64;                    // fast tokens of an item
+constexpr int kWideRows = kOutWaves * 32;       // output rows of an item
+constexpr int kWideKc = 256;                    // k of g per LDS pass
+constexpr int kWideStage = 8;                   // k-steps of 16 per register stage of M
+constexpr int kWideStagesPerPass = kWideKc / 16 / kWideStage;
+struct WideLds {
+  u32x4_t A[2][kWideKc / 8][kWideTok];  // [plane][k group][token ^ k group]
+};
+static_assert(kWideStagesPerPass == 2, "a pass of g spans the two stages of the ring");
+
+__device__ __forceinline__ void wide_load_b(u32x4_t (&b)[kWideStage], const BArgs &a, int tile, int cb,
+                                            int tiles, int step0, const u32x4_t *zero) {
+  const int lane = threadIdx.x & 63;
+  const int kg8 = a.k / 8;
+#pragma unroll
+  for (int s = 0; s < kWideStage; ++s) {
+    const int q = 2 * (step0 + s) + (lane >> 5);  // k group of this lane
+    const bool ok = tile < tiles && q < kg8;
+    b[s] = *(ok ? static_cast<const u32x4_t *>(a.M) + ((size_t)tile * kg8 + q) * 64 + cb * 32 + (lane & 31)
+                : zero);
+  }
+}
+
+__device__ __forceinline__ void wide_mma(const u32x4_t (&b)[kWideStage], const WideLds &L, int step0, int steps,
+                                         f32x16_t (&acc)[2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < kWideStage; ++s) {
+    if (step0 + s < steps) {
+      const int q = 2 * ((step0 + s) % (kWideKc / 16)) + (lane >> 5);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int m = tb * 32 + (lane & 31);
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(L.A[0][q][m ^ q]), as_bf16x8(b[s]), acc[tb], 0,
+                                                          0, 0);
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(L.A[1][q][m ^ q]), as_bf16x8(b[s]), acc[tb], 0,
+                                                          0, 0);
+      }
+    }
+  }
+}
+
+// g's planes of tokens list[0..count) (count <= 64), k in [kc0, kc0 + 256),
+// into L.A (zero outside the tokens and from kpad on).  Every thread issues
+// its loads before its first store.
+__device__ __forceinline__ void wide_stage_a(WideLds &L, const BArgs &a, const int16_t *list, int count, int kc0,
+                                             const u32x4_t *zero) {
+  constexpr int kGroups = kWideKc / 8;
+  constexpr int kPieces = 2 * kGroups * kWideTok / kOutThreads;  // 8 per thread
+  const int tid = threadIdx.x;
+  u32x4_t v[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int p = tid + i * kOutThreads;
+    const int plane = p / (kGroups * kWideTok), rem = p % (kGroups * kWideTok);
+    const int m = rem / kGroups, q = rem % kGroups;
+    const int kk = kc0 + 8 * q;
+    const bool ok = m < count && kk < a.kpad;
+    const uint16_t *src = plane == 0 ? a.ghi : a.glo;
+    v[i] = *(ok ? reinterpret_cast<const u32x4_t *>(src + (size_t)list[ok ? m : 0] * a.kpad + kk) : zero);
+  }
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int p = tid + i * kOutThreads;
+    const int plane = p / (kGroups * kWideTok), rem = p % (kGroups * kWideTok);
+    const int m = rem / kGroups, q = rem % kGroups;
+    L.A[plane][q][m ^ q] = v[i];
+  }
+}
+
+// One item: fast tokens list[0..count) (count <= 64) x output rows
+// [256 rg, 256 rg + 256).  lds: at least sizeof(WideLds) bytes.
+__device__ __forceinline__ void wide_fast_item(const BArgs &a, unsigned char *lds, const int16_t *list, int count,
+                                               int rg) {
+  WideLds &L = *reinterpret_cast<WideLds *>(lds);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
+  const int tiles = (a.d_out + 63) / 64;
+  const int tile = rg * (kWideRows / 64) + (wave >> 1), cb = wave & 1;
+  const int steps = a.kpad / 16;  // k-steps of 16
+  const int nstage = (steps + kWideStage - 1) / kWideStage;
+  f32x16_t acc[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
+  u32x4_t b0[kWideStage], b1[kWideStage];
+  wide_load_b(b0, a, tile, cb, tiles, 0, zero);
+  // stages g (b0) and g + 1 (b1) make one pass of g's planes
+  for (int g = 0; g < nstage; g += 2) {
+    __syncthreads();  // the previous pass's operand reads are done
+    wide_stage_a(L, a, list, count, (g / kWideStagesPerPass) * kWideKc, zero);
+    __syncthreads();
+    if (g + 1 < nstage) wide_load_b(b1, a, tile, cb, tiles, (g + 1) * kWideStage, zero);
+    wide_mma(b0, L, g * kWideStage, steps, acc);
+    if (g + 1 < nstage) {
+      if (g + 2 < nstage) wide_load_b(b0, a, tile, cb, tiles, (g + 2) * kWideStage, zero);
+      wide_mma(b1, L, (g + 1) * kWideStage, steps, acc);
+    }
+  }
+  // y through LDS: each wavefront's 64 tokens x 32 rows as bf16 rows of 40
+  // (padded), then 16-byte pieces of token rows
+  __syncthreads();  // every wavefront is done with L.A
+  constexpr int kYrow = 40;
+  uint16_t *yt = reinterpret_cast<uint16_t *>(lds) + wave * kWideTok * kYrow;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = tb * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
+      yt[m * kYrow + (lane & 31)] = f2bf(acc[tb][i]);
+    }
+  wave_lds_fence();
+  uint16_t *Y = static_cast<uint16_t *>(a.y);
+  const int o0 = tile * 64 + cb * 32;
+#pragma unroll
+  for (int q = 0; q < kWideTok * 4 / 64; ++q) {
+    const int pc = q * 64 + lane;  // piece: token pc / 4, rows 8 (pc % 4) ..
+    const int m = pc >> 2, c8 = (pc & 3) * 8;
+    if (m < count && tile < tiles && o0 + c8 < a.d_out)
+      *reinterpret_cast<u32x4_t *>(Y + (size_t)list[m] * a.d_out + o0 + c8) =
+          *reinterpret_cast<const u32x4_t *>(yt + m * kYrow + c8);
+  }
+  __syncthreads();  // the staged rows are read before the LDS is reused
+}
+
 // Both paths in one launch: the workgroups (about one per CU) walk the
 // 64-column tiles of every path with more than kThin tokens, fast path
 // first; with no such path they leave after the compaction.
 __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
   __shared__ __align__(16) OutLds L;
+  static_assert(sizeof(WideLds) <= sizeof(L.Bs) + sizeof(L.As) &&
+                    kOutWaves * kWideTok * 40 * 2 <= sizeof(L.Bs) + sizeof(L.As),
+                "the fast items use Bs and As as one block");
   const int2 cnt = path_lists<kOutThreads>(a, L.idx, L.scan);
   const int tiles = (a.d_out + 63) / 64;
-  const int nf = cnt.x > kThin ? tiles : 0;
+  // the fast path in items of 64 tokens x 256 rows, then the slow path's tiles
+  const int rgs = (a.d_out + kWideRows - 1) / kWideRows;
+  const int nf = cnt.x > kThin ? ((cnt.x + kWideTok - 1) / kWideTok) * rgs : 0;
   const int ns = cnt.y > kThin ? tiles : 0;
   for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
-    if (it < nf)
-      bout_path<0>(a, L, it, L.idx, cnt.x);
-    else
+    if (it < nf) {
+      const int tr = it / rgs;
+      wide_fast_item(a, reinterpret_cast<unsigned char *>(&L.Bs[0][0][0]), L.idx + tr * kWideTok,
+                     min(kWideTok, cnt.x - tr * kWideTok), it % rgs);
+    } else {
       bout_path<1>(a, L, it - nf, L.idx + cnt.x, cnt.y);
+    }
   }
 }
 
