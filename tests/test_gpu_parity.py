@@ -612,3 +612,45 @@ def test_many_projection_units(dtype):
         two = [tuple(t.clone() for t in o[3:]) for o in outs]
         assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(two, one))
     assert st1.status(ws1) == 0
+
+
+# ------------------------------------------------------------- maximum sizes -
+
+@pytest.mark.parametrize("dtype,d,d_out,k", [
+    (torch.bfloat16, 16384, 1032, 1024),   # d * 2 bytes = the 32 KiB row limit, k = the basis limit
+    (torch.float32, 8192, 520, 1024),      # d * 4 bytes = the 32 KiB row limit
+])
+def test_maximum_sizes_every_entry_point(dtype, d, d_out, k):
+    """The largest row (d * element size = 32 KiB) and basis (k = 1024) the
+    library takes, through the single-token path, the batched path (bf16:
+    a wide and a row-streaming output kernel; fp32: the batch-1 kernels) and
+    a stack, against the oracle; every gate exact, every output within the
+    bar."""
+    W = synth.gaussian_weight(d_out, d, (97, d, k, 0), dtype=dtype)
+    v, u = synth.orthonormal_frame(d, k, 16, (97, d, k, 1))
+    mask = torch.zeros(48, dtype=torch.bool)
+    mask[::6] = True  # 8 slow tokens (row stream), 40 fast (wide kernel)
+    X, _ = synth.tokens(v, u, mask, (97, d, k))
+    V = v.to(dtype)
+    X = X.to(dtype)
+    m = new_map(W, V)
+    rt = "norm" if dtype == torch.bfloat16 else 1e-4
+    Wf, Vf, Xf = f64(W), f64(V), f64(X)
+    M = orc.prepare(Wf, Vf)
+    Xd = X.to(DEV)
+    y, rho, slow = gsi.gsi_linear(m, Xd, 0.05)
+    sync()
+    assert torch.equal(slow.bool().cpu(), mask)
+    compare_tokens(Wf, Vf, Xf, 0.05, f64(y), slow.cpu().numpy(), f64(rho), dtype, M=M, rho_tol=rt,
+                   what=f"max batched {d}x{k}")
+    ys, rs, ss = zip(*[gsi.gsi_linear(m, Xd[t:t + 1], 0.05) for t in range(4)])
+    sync()
+    compare_tokens(Wf, Vf, Xf[:4], 0.05, np.concatenate([f64(a) for a in ys]), torch.cat(ss).cpu().numpy(),
+                   f64(torch.cat(rs)), dtype, M=M, rho_tol=rt, what=f"max single {d}x{k}")
+    Y = torch.empty((6, d_out), dtype=dtype, device=DEV)
+    R = torch.empty(6, dtype=torch.float32, device=DEV)
+    S = torch.empty(6, dtype=torch.uint8, device=DEV)
+    st = gsi.Stack([(m, Xd[t], Y[t], 0.05, R[t:t + 1], S[t:t + 1]) for t in range(6)])
+    st.run(check=True)
+    compare_tokens(Wf, Vf, Xf[:6], 0.05, f64(Y), S.cpu().numpy(), f64(R), dtype, M=M, rho_tol=rt,
+                   what=f"max stack {d}x{k}")
