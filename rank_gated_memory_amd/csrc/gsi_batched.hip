@@ -16,9 +16,12 @@
 //                  hi + lo (g = hi + lo to ~2^-16) for the fast GEMM.
 //   bout_kernel  : both paths' wide outputs (more than kThin tokens) in one
 //                  launch.  Each workgroup compacts the tokens of each path
-//                  from the gate flags itself (deterministic order), then
-//                  loops over 64-column tiles: all of a path's tokens (256
-//                  per pass, eight wavefronts of 32) against the tile with
+//                  from the gate flags itself (deterministic order).  Fast
+//                  path: items of 64 tokens x 256 output rows, the image
+//                  read straight from its tiled layout in MFMA operand order
+//                  and g's planes staged in LDS (wide_fast_item).  Slow path:
+//                  64-column tiles, all of the path's tokens (256 per pass,
+//                  eight wavefronts of 32) against the tile with
 //                  v_mfma_f32_32x32x16_bf16 over K chunks of 64, register-
 //                  staged prefetch, y leaving through LDS in 16-byte pieces
 //                  (see below).
@@ -317,7 +320,8 @@ __global__ void __launch_bounds__(kBlock) bgate_kernel(BArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Outputs: 64 columns x all tokens of one path per workgroup.
+// Outputs: 64 columns x all tokens of one path per workgroup (bout_path; the
+// launch uses it for the slow path, the fast path taking wide_fast_item).
 //
 // PATH 0 (fast): A = G as bf16 hi + lo [n][kpad], B = the image tile (M's
 // 64-row tile is already in MFMA order); PATH 1 (slow): A = X [n][d], B = 64
