@@ -58,6 +58,13 @@ gsi_status gsi_linear_static(const gsi_map *map, const void *x, void *y, int32_t
     return gsi_linear(map, x, y, T, eps, mode, rho, slow, nullptr, 0, stream);
   }
   if (need > kScratchBytes) return GSI_E_WORKSPACE;
+  // gsi_linear's own argument checks, before anything is enqueued (the
+  // clear below must not run for a call that is then rejected)
+  if (mode < GSI_GATED || mode > GSI_FORCE_SLOW) return GSI_E_ARG;
+  if (!x || !y) return GSI_E_NULL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16 ||
+      (rho && reinterpret_cast<uintptr_t>(rho) % 4))
+    return GSI_E_ALIGN;
   void *ws = nullptr;
   const gsi_status s = scratch_ptr(&ws);
   if (s != GSI_OK) return s;

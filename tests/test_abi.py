@@ -369,3 +369,23 @@ def test_calibrate_rejects_before_launch():
     assert L.gsi_calibrate_status_offset() == 0
     # workspace grows with the block
     assert L.gsi_calibrate_workspace(ctypes.byref(calib(n=4096, d=4096, k=256))) > need
+
+
+def test_static_entry_point_rejects_before_launch():
+    """gsi_linear_static checks its arguments (map, sizes, mode, pointers,
+    alignment) before it enqueues its clear of the scratch array."""
+    L = gsi.lib()
+    m = gsi.GsiMapStruct(256, 512, 16, gsi.GSI_FP32, 256, 512, 1024, 0)
+    assert L.gsi_static_scratch_bytes() == 64 << 20
+    st = lambda mm, x, y, T, mode=0, rho=0: L.gsi_linear_static(ctypes.byref(mm), x, y, T, ctypes.c_float(0.05),
+                                                              mode, rho, 0, 0)  # noqa: E731
+    assert st(m, 4096, 4096, 0) == 0                     # T = 0: nothing to do
+    assert st(m, 4096, 4096, -1) == 2                    # GSI_E_SHAPE
+    assert st(m, 4096, 4096, 4, mode=3) == 7             # GSI_E_ARG
+    assert st(m, 0, 4096, 4) == 1                        # GSI_E_NULL
+    assert st(m, 4104, 4096, 4) == 4                     # x not 16-byte aligned
+    assert st(m, 4096, 4096, 4, rho=4098) == 4           # rho not 4-byte aligned
+    bad = gsi.GsiMapStruct(255, 512, 16, gsi.GSI_FP32, 256, 512, 1024, 0)
+    assert st(bad, 4096, 4096, 4) == 2                   # d not a multiple of 8
+    big = gsi.GsiMapStruct(16384, 64, 1024, gsi.GSI_BF16, 256, 512, 1024, 0)
+    assert st(big, 4096, 4096, 4096) == 5                # workspace beyond the array
