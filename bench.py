@@ -62,6 +62,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cells", default=None,
                    help="batched-t256 only: run just these cells, 'k:slow_share,...' (for profiling)")
+    p.add_argument("--trace", action="store_true",
+                   help="stack workloads: per-job trace of three steps through the instrumented library "
+                        "(rank_gated_memory_amd/libgsi_trace.so, build.build_traced()); prints the "
+                        "summary instead of the bench line")
     return p.parse_args()
 
 
@@ -827,6 +831,167 @@ def ctypes_calib(n, d, k):
     return ctypes.byref(gsi.GsiCalibStruct(n, d, k, 1, 16, 16, 16, 1, 0))
 
 
+TRACE_KINDS = {1: "projection unit", 2: "output unit", 8: "choosing the next job (incl. waits)"}
+
+
+def trace_summary(rec, us_event, calls, slow):
+    """Summary of one traced step.  rec: records (n, 4) uint64 from
+    gsi_trace_read; calls: per call (d, d_out, k, wave, shares_projection);
+    slow: per call gate of the step."""
+    import numpy as np
+
+    t0, t1 = rec[:, 0].astype(np.int64), rec[:, 1].astype(np.int64)
+    meta, cu = rec[:, 2].astype(np.int64), rec[:, 3].astype(np.int64)
+    blk, kind = meta >> 32, (meta >> 8) & 0xff
+    call = cu >> 32
+    T0 = t0.min()
+    us = lambda x: (x - T0) * 10.0 / 1000.0  # 100 MHz constant clock
+    span = float(us(t1.max()))
+    out = {"workgroups": int(blk.max() + 1), "span_us": span, "event_us": float(us_event), "jobs": {}}
+    for k, name in TRACE_KINDS.items():
+        m = kind == k
+        d = (t1[m] - t0[m]) * 10.0 / 1000.0
+        if m.any():
+            out["jobs"][name] = {"count": int(m.sum()), "mean_us": float(d.mean()), "p50_us": float(np.median(d)),
+                                 "max_us": float(d.max()), "workgroup_us": float(d.sum())}
+    sl = (meta & 1).astype(bool)
+    for name, m in (("output unit, fast path", (kind == 2) & ~sl), ("output unit, slow path", (kind == 2) & sl)):
+        if m.any():
+            d = (t1[m] - t0[m]) * 10.0 / 1000.0
+            out["jobs"][name] = {"count": int(m.sum()), "mean_us": float(d.mean()), "p50_us": float(np.median(d)),
+                                 "max_us": float(d.max()), "workgroup_us": float(d.sum())}
+    # the first job of every workgroup: from the workgroup's start to its end
+    first = {}
+    for i in np.argsort(t0):
+        b = int(blk[i])
+        if kind[i] in (1, 2) and b not in first:
+            first[b] = i
+    fs = np.array([us(t0[i]) for i in first.values()])
+    if fs.size:
+        out["first_unit_start_us"] = {"min": float(fs.min()), "mean": float(fs.mean()), "max": float(fs.max())}
+    starts, exits = us(t0[kind == 9]), us(t0[kind == 7])
+    out["start_spread_us"] = float(starts.max() - starts.min())
+    out["exits_us"] = [float(exits.min()), float(exits.max())]
+    # algorithmic bytes of each unit: the call's V_k (projection) or chosen
+    # matrix (output) over the number of its units in the trace
+    C = len(calls)
+    d_, do_, k_ = (np.array([c[i] for c in calls], dtype=np.float64) for i in range(3))
+    npj = np.bincount(call[kind == 1], minlength=C)
+    nout = np.bincount(call[kind == 2], minlength=C)
+    vb = d_ * k_ * 2.0
+    ob = np.where(slow.astype(bool), d_ * do_ * 2.0, do_ * k_ * 2.0)
+    byt = np.zeros(len(rec))
+    m1, m2 = kind == 1, kind == 2
+    byt[m1] = (vb / np.maximum(npj, 1))[call[m1]]
+    byt[m2] = (ob / np.maximum(nout, 1))[call[m2]]
+    out["unit_bytes"] = float(byt.sum())
+    out["tb_per_s_over_span"] = float(byt.sum() / (span * 1e-6) / 1e12)
+    nb = int(span) + 2
+    bw, busy = np.zeros(nb), np.zeros(nb)
+    for i in np.nonzero(m1 | m2)[0]:
+        a, b = us(t0[i]), us(t1[i])
+        if b <= a:
+            continue
+        rate = byt[i] / (b - a)
+        for j in range(int(a), int(b) + 1):
+            ov = min(b, j + 1) - max(a, j)
+            if ov > 0:
+                bw[j] += rate * ov
+                busy[j] += ov
+    out["tb_per_s_by_10us"] = [round(float(bw[j:j + 10].mean() / 1e6), 2) for j in range(0, nb, 10)]
+    out["busy_workgroups_by_10us"] = [round(float(busy[j:j + 10].mean()), 0) for j in range(0, nb, 10)]
+    waves = np.array([c[3] for c in calls])
+    if waves.max() > 0:
+        # per wave: entry (first job of the wave starts) -> last projection
+        # unit ends -> last output unit ends
+        jw = np.where(m1 | m2, waves[np.minimum(call, C - 1)], -1)
+        ph, oph, tot, gap, fo, span_o = [], [], [], [], [], []
+        prev_end = None
+        for w in range(int(waves.max()) + 1):
+            mw = jw == w
+            if not mw.any():
+                continue
+            a = us(t0[mw].min())
+            pe = us(t1[mw & m1].max()) if (mw & m1).any() else a
+            e = us(t1[mw].max())
+            ph.append(pe - a)
+            oph.append(e - pe)
+            tot.append(e - a)
+            if (mw & m2).any():
+                o0 = us(t0[mw & m2].min())
+                fo.append(o0 - pe)
+                span_o.append(e - o0)
+            if prev_end is not None:
+                gap.append(a - prev_end)
+            prev_end = e
+        out["waves"] = {"count": len(tot), "mean_us": float(np.mean(tot)),
+                        "projection_phase_mean_us": float(np.mean(ph)),
+                        "after_last_projection_mean_us": float(np.mean(oph)),
+                        "last_projection_to_first_output_mean_us": float(np.mean(fo)) if fo else None,
+                        "first_output_to_last_output_mean_us": float(np.mean(span_o)) if span_o else None,
+                        "previous_wave_end_to_first_job_mean_us": float(np.mean(gap)) if gap else None}
+    return out
+
+
+def bench_trace(args):
+    """Per-job trace of three decode steps of a stack workload (instrumented
+    library; see gsi_kernels.hip)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from rank_gated_memory_amd import gsi
+
+    dev = torch.device("cuda:0")
+    L = gsi.lib()
+    if not hasattr(L, "gsi_trace_read"):
+        print(f"{gsi.LIB_PATH} is not the instrumented build: set GSI_LIBRARY to "
+              "rank_gated_memory_amd/libgsi_trace.so (build.build_traced())", file=sys.stderr)
+        sys.exit(2)
+    L.gsi_trace_read.restype = ctypes.c_int
+    L.gsi_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.gsi_trace_reset.restype = ctypes.c_int
+    chained = args.workload == "gptj6b-28L-chained"
+    if chained:
+        wl = build_chained_workload(args.layers, dev)
+    else:
+        wl = build_workload(args.workload, args.layers, dev, shared=args.shared_bases, exact=args.exact_rho)
+    plans = wl["plans"]
+    ws = gsi.workspace(max(p.ws_bytes for p in plans), dev)
+    calls = []
+    for li, row in enumerate(wl["data"]):
+        for ri, mi in enumerate(row):
+            wave = (2 * li + (1 if ri >= 2 else 0)) if chained else 0
+            calls.append((mi.d, mi.d_out, mi.k, wave, bool(getattr(mi, "shared", False))))
+    for i in range(8):
+        gsi.gsi_stack(plans[i], gsi.GATED, ws)
+    torch.cuda.synchronize()
+    buf = np.zeros((1024 * 512, 4), dtype=np.uint64)
+    steps = {}
+    for s_ in (3, 10, 17):
+        if L.gsi_trace_reset() != 0:
+            raise RuntimeError("gsi_trace_reset failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gsi.gsi_stack(plans[s_], gsi.GATED, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        word = plans[s_].status(ws)
+        if word != 0:
+            raise gsi.StackIncomplete(word)
+        n = L.gsi_trace_read(buf.ctypes.data, buf.shape[0])
+        if n <= 0:
+            raise RuntimeError(f"gsi_trace_read returned {n}")
+        rec = buf[:n][buf[:n, 0] != 0].copy()  # unused slots are zero
+        # the gates of this step, written by the traced run itself
+        slow_s = torch.stack([S_[s_] for row in wl["outs"] for (_, _, S_) in row]).cpu().numpy()
+        steps[f"step{s_}"] = trace_summary(rec, e0.elapsed_time(e1) * 1e3, calls, slow_s)
+        log(f"step {s_}: {len(rec)} records, {steps[f'step{s_}']['event_us']:.1f} us")
+    print(json.dumps({"workload": args.workload, "trace": "per-job, instrumented build", "steps": steps}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -844,6 +1009,9 @@ def main():
         return
     if args.workload == "calibrate-gptj6b-28L":
         bench_calibrate(args)
+        return
+    if args.trace:
+        bench_trace(args)
         return
     import numpy as np
     import torch

@@ -27,6 +27,10 @@ SAN_FLAGS = ["-O1", "-g", "-Werror", *COMMON,
              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 SAN_OUT = os.path.join(ROOT, "_build", "libgsi_hostsan.so")
+# The per-job trace of the single-launch stack (instrumented, slower): loaded
+# through GSI_LIBRARY by `bench.py --trace`; exports gsi_trace_read/_reset.
+TRACE_FLAGS = [*FLAGS, "-DGSI_TRACE=1"]
+TRACE_OUT = os.path.join(PKG, "libgsi_trace.so")
 
 
 def _compile(flags, out, verbose):
@@ -46,6 +50,11 @@ def _compile(flags, out, verbose):
 
 def build(verbose: bool = False) -> str:
     return _compile(FLAGS, OUT, verbose)
+
+
+def build_traced(verbose: bool = False) -> str:
+    """The instrumented build (TRACE_FLAGS) at TRACE_OUT."""
+    return _compile(TRACE_FLAGS, TRACE_OUT, verbose)
 
 
 def build_sanitized(verbose: bool = False) -> str:

@@ -52,6 +52,40 @@
 
 namespace gsi {
 
+// Per-job trace of stack_kernel, compiled only into the instrumented build
+// (-DGSI_TRACE=1; build.build_traced): thread 0 of each workgroup writes one
+// record per job into the workgroup's own slots (no shared counter, so
+// recording adds no contended atomics), {start, end, block << 32 | kind << 8
+// | slow, call << 32 | unit}, with times from the 100 MHz constant clock.
+// kind: 1 projection unit, 2 output unit, 7 leaving the job loop, 8 choosing
+// the next job (including any wait for a gate or a wave), 9 workgroup start;
+// unused slots stay zero.  A unit's end is taken after its memory operations
+// completed (s_waitcnt 0), which the product build does not wait for.  Read
+// back with gsi_trace_read, cleared with gsi_trace_reset (extern "C",
+// instrumented build only).
+#ifndef GSI_TRACE
+#define GSI_TRACE 0
+#endif
+#if GSI_TRACE
+constexpr unsigned kTraceBlocks = 1024;  // workgroups traced (by index)
+constexpr unsigned kTracePer = 512;      // records per workgroup
+__device__ unsigned long long g_trace[4ull * kTraceBlocks * kTracePer];
+__device__ __forceinline__ void trace_rec(unsigned &n, unsigned long long t0, unsigned long long t1, int kind,
+                                          int c, int u, int slow) {
+  if (blockIdx.x < kTraceBlocks && n < kTracePer) {
+    unsigned long long *r = g_trace + 4ull * (blockIdx.x * kTracePer + n);
+    r[0] = t0;
+    r[1] = t1;
+    r[2] = ((unsigned long long)blockIdx.x << 32) | ((unsigned long long)kind << 8) | (unsigned)slow;
+    r[3] = ((unsigned long long)(unsigned)c << 32) | (unsigned)u;
+  }
+  ++n;
+}
+#define GSI_TRACE_ONLY(...) __VA_ARGS__
+#else
+#define GSI_TRACE_ONLY(...)
+#endif
+
 struct bf16_t {
   uint16_t bits;
 };
@@ -1023,7 +1057,9 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
 
   Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0};
   int cur = -1, cur_slow = 0;
+  GSI_TRACE_ONLY(unsigned tn = 0; unsigned long long tj = wall_clock64(); if (tid == 0) trace_rec(tn, tj, tj, 9, 0, 0, 0);)
   for (;;) {
+    GSI_TRACE_ONLY(const unsigned long long tq = wall_clock64();)
     if (tid < 64) next_job(a, st, s_job);
     __syncthreads();
     const int kind = s_job[0];
@@ -1031,6 +1067,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
     const int u = s_job[2];
     const int slow = s_job[3];
     __syncthreads();  // s_job is rewritten only after every thread has read it
+    GSI_TRACE_ONLY(tj = wall_clock64(); if (tid == 0) trace_rec(tn, tq, tj, 8, 0, 0, 0);)
     if (kind == kJobDone) break;
     if (tid < 64) sched_prefetch(a, st);
     const CallDesc cd = a.table[c];
@@ -1097,7 +1134,9 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         __syncthreads();
       }
     }
+    GSI_TRACE_ONLY(__builtin_amdgcn_s_waitcnt(0); if (tid == 0) trace_rec(tn, tj, wall_clock64(), kind, c, u, slow);)
   }
+  GSI_TRACE_ONLY(if (tid == 0) { const unsigned long long te = wall_clock64(); trace_rec(tn, te, te, 7, 0, 0, 0); })
 
   // The last workgroup to leave clears the control words (all but the status
   // word) and the projection counters for the next launch on this workspace.
@@ -1335,3 +1374,24 @@ hipError_t launch_batch1(int dtype, const KArgs &a, int grid_b, int phases, hipS
 }
 
 }  // namespace gsi
+
+#if GSI_TRACE
+// Copies the record slots (4 x uint64 each; zero = unused), at most
+// max_entries of them, to host memory; returns the count copied, or a
+// negative value on a HIP error.
+extern "C" int gsi_trace_read(unsigned long long *host, int max_entries) {
+  size_t n = (size_t)gsi::kTraceBlocks * gsi::kTracePer;
+  if (max_entries < 0) max_entries = 0;
+  if (n > (size_t)max_entries) n = (size_t)max_entries;
+  if (n && hipMemcpyFromSymbol(host, HIP_SYMBOL(gsi::g_trace), n * 32) != hipSuccess) return -2;
+  return (int)n;
+}
+
+// Zeroes every slot (synchronous).
+extern "C" int gsi_trace_reset(void) {
+  void *p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(gsi::g_trace)) != hipSuccess || !p) return -1;
+  if (hipMemset(p, 0, sizeof(gsi::g_trace)) != hipSuccess) return -1;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+#endif
