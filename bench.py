@@ -1193,7 +1193,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": stack_gbps / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(args.workload + ("-shared" if args.shared_bases else ""),
+            "traffic": measured_traffic(args.workload + ("-shared" if args.shared_bases else "")
+                                        + ("-exact" if args.exact_rho else ""),
                                         "stack_kernel"),
             "bytes_per_launch": float(step_b.mean()),
             "mean_launch_us": float(t_launch * 1e6),
