@@ -465,7 +465,7 @@ def bench_batched(args):
         # output kernels) against the HBM roof: its algorithmic bytes (V_k,
         # X, Y, M once if any token is fast, W once if any is slow) over the
         # rotated call time
-        "roofline": {"bound": "hbm", "kernel": "gsi_linear (bproj, bgate, bout, bthin)",
+        "roofline": {"bound": "hbm", "kernel": "gsi_linear (bproj, bgate, bout)",
                      "achieved": head["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_HBM_GBPS, "traffic": None},
         "cpu_baseline": cpu,

@@ -14,20 +14,21 @@
 //   bgate_kernel : one workgroup per token: sums the S partials in a fixed
 //                  order, forms ||g||^2, rho and the gate, writes g as bf16
 //                  hi + lo (g = hi + lo to ~2^-16) for the fast GEMM.
-//   bout_kernel  : both paths' wide outputs (more than kThin tokens) in one
-//                  launch.  Each workgroup compacts the tokens of each path
-//                  from the gate flags itself (deterministic order).  Fast
-//                  path: items of 64 tokens x 256 output rows, the image
-//                  read straight from its tiled layout in MFMA operand order
-//                  and g's planes staged in LDS (wide_fast_item).  Slow path:
-//                  64-column tiles, all of the path's tokens (256 per pass,
-//                  eight wavefronts of 32) against the tile with
-//                  v_mfma_f32_32x32x16_bf16 over K chunks of 64, register-
-//                  staged prefetch, y leaving through LDS in 16-byte pieces
-//                  (see below).
-//   bthin_kernel : both paths' outputs with 1 to kThin tokens: the matrix is
-//                  streamed by blocks of 16 (fast) or 32 (slow) rows
-//                  (v_mfma_f32_16x16x32_bf16).
+//   bout_kernel  : every output of the call in one launch, one workgroup of
+//                  eight wavefronts per CU.  Each workgroup compacts the
+//                  tokens of each path from the gate flags itself
+//                  (deterministic order).  A path with 1 to kThin tokens is
+//                  a row stream: the matrix in blocks of 16 (fast) or 32
+//                  (slow) rows, two blocks at a time (one per half of the
+//                  workgroup), v_mfma_f32_16x16x32_bf16 (bthin_path).  A path
+//                  with more: fast, items of 64 tokens x 256 output rows,
+//                  the image read straight from its tiled layout in MFMA
+//                  operand order and g's planes staged in LDS
+//                  (wide_fast_item); slow, 64-column tiles, all of the
+//                  path's tokens (256 per pass, eight wavefronts of 32)
+//                  against the tile with v_mfma_f32_32x32x16_bf16 over K
+//                  chunks of 64, register-staged prefetch, y leaving through
+//                  LDS in 16-byte pieces (bout_path).
 //   bprep_kernel : the image M = W V_k (once per map).
 //
 // MFMA operand layouts (checked on the device): for 32x32x16, lane l holds
@@ -449,13 +450,222 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
   }
 }
 
+// ---------------------------------------------------------------------------
+// Outputs of a path with at most kThin tokens: streaming the matrix by rows.
+//
+// With few tokens the output GEMM is a stream of W (slow) or M (fast) and is
+// bound by HBM.  A row block is 16 RT output rows (RT tiles of 16), run by
+// four wavefronts (half of the output kernel's workgroup) that take a
+// quarter of K each and meet in LDS at the end, so there is no barrier in
+// the K loop.  v_mfma_f32_16x16x32_bf16 with A = 16
+// matrix rows and B = 16 tokens (kThin tokens are two B groups).  Every
+// workgroup reads all of the path's token rows, so more rows per workgroup
+// means fewer token bytes per matrix byte: with 32 rows (the slow path) the
+// CUs take in one byte of x per byte of W (with 16 rows, two).
+//
+// In the MFMA operand layout the 16 lanes of a quarter-wave hold 16 different
+// rows, so loading W rows or token rows in that layout touches 16 cache lines
+// per quarter-wave and the address unit, not HBM, sets the pace.  Each
+// wavefront therefore loads a stage (4 k-steps = 128 columns of K) with
+// row-contiguous 16-byte pieces (16 lanes cover 256 bytes of one row), writes
+// it to its own LDS region and reads it back in operand layout.  The image M
+// is stored in operand order already (64 rows x 16 bytes contiguous) and is
+// read directly.  One stage is in flight in registers while the previous one
+// goes through LDS and the matrix cores.
+// ---------------------------------------------------------------------------
+#ifndef GSI_THIN_RT_SLOW
+#define GSI_THIN_RT_SLOW 2
+#endif
+#ifndef GSI_THIN_RT_FAST
+#define GSI_THIN_RT_FAST 1
+#endif
+
+template <int PATH>
+struct ThinStage {
+  static constexpr int NB = PATH == 0 ? 2 : 1;  // B matrices: (g hi, g lo) or (x)
+  // 16-row tiles of a workgroup (the fast path's two B matrices leave no
+  // registers for a second tile at two wavefronts per SIMD)
+  static constexpr int RT = PATH == 0 ? GSI_THIN_RT_FAST : GSI_THIN_RT_SLOW;
+  static constexpr int kRows = 16 * RT;  // output rows of a workgroup
+  u32x4_t A[RT][4];  // slow: piece i * 64 + lane of row tile t (16 x 256 bytes); fast: k-step i of tile t of M
+  u32x4_t B[NB][8];  // piece i * 64 + lane of the 32 x 256-byte token tile
+};
+
+template <int PATH>
+struct ThinLds {
+  static constexpr int NB = ThinStage<PATH>::NB;
+  static constexpr int kRowA = PATH == 1 ? ThinStage<PATH>::kRows : 0;
+  // pieces of 16 bytes, rows padded by one piece so that the 16 rows read by a
+  // quarter-wave fall in different banks
+  static constexpr int kA = kRowA * 17;
+  static constexpr int kPieces = kA + NB * 32 * 17;
+};
+
+template <int PATH>
+__device__ __forceinline__ void thin_load(ThinStage<PATH> &st, const BArgs &a, int step0, int kend,
+                                          int r0, const int (&tk)[8], const u32x4_t *zero) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
+    if (PATH == 0) {
+      const int q = lane >> 4, row = r0 + 16 * t + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kg = (step0 + j) * 32 + 8 * q;
+        const bool ok = kg < kend && row < a.d_out;
+        const u32x4_t *p = static_cast<const u32x4_t *>(a.M) +
+                           ((size_t)(row / 64) * (a.k / 8) + kg / 8) * 64 + (row & 63);
+        st.A[t][j] = *(ok ? p : zero);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = i * 64 + lane;
+        const int row = r0 + 16 * t + (pc >> 4), kg = step0 * 32 + (pc & 15) * 8;
+        const bool ok = kg < kend && row < a.d_out;
+        const u32x4_t *p =
+            reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.W) + (size_t)row * a.d + kg);
+        st.A[t][i] = *(ok ? p : zero);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tok = tk[i], kg = step0 * 32 + (lane & 15) * 8;
+    const bool ok = kg < kend && tok >= 0;
+    if (PATH == 0) {
+      const size_t off = (size_t)tok * a.kpad + kg;
+      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.ghi + off) : zero);
+      st.B[ThinStage<PATH>::NB - 1][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.glo + off) : zero);
+    } else {
+      const size_t off = (size_t)tok * a.d + kg;
+      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) + off) : zero);
+    }
+  }
+}
+
+template <int PATH>
+__device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t *lds,
+                                             f32x4_t (&acc)[ThinStage<PATH>::RT][2]) {
+  constexpr int NB = ThinStage<PATH>::NB;
+  constexpr int kA = ThinLds<PATH>::kA;
+  const int lane = threadIdx.x & 63;
+  wave_lds_fence();  // the previous stage's reads are done before it is overwritten
+  if (PATH == 1) {
+#pragma unroll
+    for (int t = 0; t < ThinStage<PATH>::RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pc = i * 64 + lane;
+        lds[(16 * t + (pc >> 4)) * 17 + (pc & 15)] = st.A[t][i];
+      }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = i * 64 + lane;
+      lds[kA + b * 32 * 17 + (pc >> 4) * 17 + (pc & 15)] = st.B[b][i];
+    }
+  wave_lds_fence();
+  const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4_t B[2][NB];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) B[g][b] = lds[kA + b * 32 * 17 + (16 * g + r) * 17 + 4 * j + q];
+#pragma unroll
+    for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
+      const u32x4_t A = PATH == 1 ? lds[(16 * t + r) * 17 + 4 * j + q] : st.A[t][j];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(B[g][b]), acc[t][g], 0, 0, 0);
+    }
+  }
+}
+
+constexpr int kThinPieces = ThinLds<0>::kPieces > ThinLds<1>::kPieces ? ThinLds<0>::kPieces : ThinLds<1>::kPieces;
+static_assert(kThinPieces * 16 >= ThinStage<0>::RT * 2 * 4 * 64 * 4 && kThinPieces * 16 >= ThinStage<1>::RT * 2 * 4 * 64 * 4,
+              "the final sums reuse a wavefront's region");
+
+template <int PATH>
+__device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], const int *toks,
+                                           int rb) {
+  // four wavefronts (a workgroup of kBlock threads, or one half of the
+  // output kernel's eight, each half on its own row block: both halves
+  // pass the same barriers)
+  const int tid = threadIdx.x & (kBlock - 1);
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r0 = rb * ThinStage<PATH>::kRows;
+  // one zero piece per lane (a uniform fallback address becomes a branch)
+  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
+  const int K = PATH == 0 ? a.kpad : a.d;
+  const int steps = (K + 31) / 32;  // k-steps of 32
+  const int per = (steps + kWaves - 1) / kWaves;
+  const int s0 = wave * per;
+  const int s_end = min(steps, s0 + per);
+  const int kend = min(s_end * 32, PATH == 0 ? a.k : a.d);  // this wavefront's K ends here
+
+  int tk[8];  // token of each of this lane's 16-byte pieces of the token tile
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tk[i] = toks[(i * 64 + lane) >> 4];
+
+  f32x4_t acc[ThinStage<PATH>::RT][2];
+#pragma unroll
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  ThinStage<PATH> sa, sb;
+  thin_load<PATH>(sa, a, s0, kend, r0, tk, zero);
+  for (int st = s0; st < s_end; st += 8) {
+    thin_load<PATH>(sb, a, st + 4, kend, r0, tk, zero);
+    thin_consume<PATH>(sa, lds[wave], acc);
+    thin_load<PATH>(sa, a, st + 8, kend, r0, tk, zero);
+    thin_consume<PATH>(sb, lds[wave], acc);
+  }
+  // partial sums of the four K quarters, through each wavefront's own region:
+  // element ((t * 2 + g) * 4 + i) * 64 + lane
+  wave_lds_fence();
+  float *red = reinterpret_cast<float *>(lds[wave]);
+#pragma unroll
+  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((t * 2 + g) * 4 + i) * 64 + lane] = acc[t][g][i];
+  __syncthreads();
+  uint16_t *Y = static_cast<uint16_t *>(a.y);
+#pragma unroll
+  for (int h = 0; h < 2 * ThinStage<PATH>::RT; ++h) {
+    const int e = tid + h * kBlock;  // (tile, group, element, lane)
+    const int t = e >> 9, g = (e >> 8) & 1, i = (e >> 6) & 3, l = e & 63;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float *>(lds[w])[e];
+    const int tok = toks[g * 16 + (l & 15)];
+    const int r = r0 + 16 * t + 4 * (l >> 4) + i;
+    if (tok >= 0 && r < a.d_out) Y[(size_t)tok * a.d_out + r] = f2bf(v);
+  }
+  __syncthreads();  // every wavefront's region is free again
+}
+
 // LDS of the wide kernel, sized for the fast path (two A matrices); the
 // fast items of wide_fast_item use Bs and As as one block.
 struct OutLds {
-  u32x4_t Bs[2][8][64];                          // double-buffered 64-wide K chunk: [k group][column]
-  u32x4_t As[kOutWaves][2 * kOutTok * kOutArow];  // each wavefront's A chunk
-  int16_t idx[kMaxBatch];                        // tokens of both paths (path_lists)
-  int2 scan[kOutWaves];                          // wavefront totals of the compaction scan
+  union {
+    struct {
+      u32x4_t Bs[2][8][64];                          // double-buffered 64-wide K chunk: [k group][column]
+      u32x4_t As[kOutWaves][2 * kOutTok * kOutArow];  // each wavefront's A chunk
+    };
+    u32x4_t thin[2 * kWaves][kThinPieces];  // row-stream regions (two halves of four wavefronts)
+  };
+  int16_t idx[kMaxBatch];  // tokens of both paths (path_lists)
+  int2 scan[kOutWaves];    // wavefront totals of the compaction scan
+  int toks[2][kThin];      // tokens of each path with 1 to kThin tokens (-1: none)
 };
 
 template <int PATH>
@@ -686,252 +896,57 @@ __device__ __forceinline__ void wide_fast_item(const BArgs &a, unsigned char *ld
   __syncthreads();  // the staged rows are read before the LDS is reused
 }
 
-// Both paths in one launch: the workgroups (about one per CU) walk the
-// 64-column tiles of every path with more than kThin tokens, fast path
-// first; with no such path they leave after the compaction.
+// Every output of the call in one launch: the workgroups (one per CU) walk
+// the row-stream items of the paths with 1 to kThin tokens (pairs of row
+// blocks, one per half of the workgroup), then the wide items of the paths
+// with more (the fast path in items of 64 tokens x 256 rows, the slow
+// path's 64-column tiles).  A call with both kinds of path thus runs them in
+// one launch.  The two kinds are walked in two loops over the workgroup's
+// items (blockIdx.x, + gridDim.x, ...): within one loop the registers each
+// role keeps for its items would be live across the other's, which does not
+// fit (both roles use all 256).  With no work the workgroups leave after the
+// compaction.
 __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
   __shared__ __align__(16) OutLds L;
   static_assert(sizeof(WideLds) <= sizeof(L.Bs) + sizeof(L.As) &&
                     kOutWaves * kWideTok * 40 * 2 <= sizeof(L.Bs) + sizeof(L.As),
                 "the fast items use Bs and As as one block");
+  static_assert(kOutWaves == 2 * kWaves, "the row streams run as two halves of four wavefronts");
+  const int tid = threadIdx.x;
   const int2 cnt = path_lists<kOutThreads>(a, L.idx, L.scan);
-  const int tiles = (a.d_out + 63) / 64;
-  // the fast path in items of 64 tokens x 256 rows, then the slow path's tiles
-  const int rgs = (a.d_out + kWideRows - 1) / kWideRows;
-  const int nf = cnt.x > kThin ? ((cnt.x + kWideTok - 1) / kWideTok) * rgs : 0;
-  const int ns = cnt.y > kThin ? tiles : 0;
-  for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
-    if (it < nf) {
-      const int tr = it / rgs;
-      wide_fast_item(a, reinterpret_cast<unsigned char *>(&L.Bs[0][0][0]), L.idx + tr * kWideTok,
-                     min(kWideTok, cnt.x - tr * kWideTok), it % rgs);
-    } else {
-      bout_path<1>(a, L, it - nf, L.idx + cnt.x, cnt.y);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Outputs of a path with at most kThin tokens: streaming the matrix by rows.
-//
-// With few tokens the output GEMM is a stream of W (slow) or M (fast) and is
-// bound by HBM.  A workgroup owns 16 RT output rows (RT tiles of 16);
-// its four wavefronts take a quarter of K each and meet in LDS at the end, so
-// there is no barrier in the K loop.  v_mfma_f32_16x16x32_bf16 with A = 16
-// matrix rows and B = 16 tokens (kThin tokens are two B groups).  Every
-// workgroup reads all of the path's token rows, so more rows per workgroup
-// means fewer token bytes per matrix byte: with 32 rows (the slow path) the
-// CUs take in one byte of x per byte of W (with 16 rows, two).
-//
-// In the MFMA operand layout the 16 lanes of a quarter-wave hold 16 different
-// rows, so loading W rows or token rows in that layout touches 16 cache lines
-// per quarter-wave and the address unit, not HBM, sets the pace.  Each
-// wavefront therefore loads a stage (4 k-steps = 128 columns of K) with
-// row-contiguous 16-byte pieces (16 lanes cover 256 bytes of one row), writes
-// it to its own LDS region and reads it back in operand layout.  The image M
-// is stored in operand order already (64 rows x 16 bytes contiguous) and is
-// read directly.  One stage is in flight in registers while the previous one
-// goes through LDS and the matrix cores.
-// ---------------------------------------------------------------------------
-#ifndef GSI_THIN_RT_SLOW
-#define GSI_THIN_RT_SLOW 2
-#endif
-#ifndef GSI_THIN_RT_FAST
-#define GSI_THIN_RT_FAST 1
-#endif
-
-template <int PATH>
-struct ThinStage {
-  static constexpr int NB = PATH == 0 ? 2 : 1;  // B matrices: (g hi, g lo) or (x)
-  // 16-row tiles of a workgroup (the fast path's two B matrices leave no
-  // registers for a second tile at two wavefronts per SIMD)
-  static constexpr int RT = PATH == 0 ? GSI_THIN_RT_FAST : GSI_THIN_RT_SLOW;
-  static constexpr int kRows = 16 * RT;  // output rows of a workgroup
-  u32x4_t A[RT][4];  // slow: piece i * 64 + lane of row tile t (16 x 256 bytes); fast: k-step i of tile t of M
-  u32x4_t B[NB][8];  // piece i * 64 + lane of the 32 x 256-byte token tile
-};
-
-template <int PATH>
-struct ThinLds {
-  static constexpr int NB = ThinStage<PATH>::NB;
-  static constexpr int kRowA = PATH == 1 ? ThinStage<PATH>::kRows : 0;
-  // pieces of 16 bytes, rows padded by one piece so that the 16 rows read by a
-  // quarter-wave fall in different banks
-  static constexpr int kA = kRowA * 17;
-  static constexpr int kPieces = kA + NB * 32 * 17;
-};
-
-template <int PATH>
-__device__ __forceinline__ void thin_load(ThinStage<PATH> &st, const BArgs &a, int step0, int kend,
-                                          int r0, const int (&tk)[8], const u32x4_t *zero) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
-    if (PATH == 0) {
-      const int q = lane >> 4, row = r0 + 16 * t + (lane & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kg = (step0 + j) * 32 + 8 * q;
-        const bool ok = kg < kend && row < a.d_out;
-        const u32x4_t *p = static_cast<const u32x4_t *>(a.M) +
-                           ((size_t)(row / 64) * (a.k / 8) + kg / 8) * 64 + (row & 63);
-        st.A[t][j] = *(ok ? p : zero);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pc = i * 64 + lane;
-        const int row = r0 + 16 * t + (pc >> 4), kg = step0 * 32 + (pc & 15) * 8;
-        const bool ok = kg < kend && row < a.d_out;
-        const u32x4_t *p =
-            reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.W) + (size_t)row * a.d + kg);
-        st.A[t][i] = *(ok ? p : zero);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tok = tk[i], kg = step0 * 32 + (lane & 15) * 8;
-    const bool ok = kg < kend && tok >= 0;
-    if (PATH == 0) {
-      const size_t off = (size_t)tok * a.kpad + kg;
-      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.ghi + off) : zero);
-      st.B[ThinStage<PATH>::NB - 1][i] = *(ok ? reinterpret_cast<const u32x4_t *>(a.glo + off) : zero);
-    } else {
-      const size_t off = (size_t)tok * a.d + kg;
-      st.B[0][i] = *(ok ? reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) + off) : zero);
-    }
-  }
-}
-
-template <int PATH>
-__device__ __forceinline__ void thin_consume(const ThinStage<PATH> &st, u32x4_t *lds,
-                                             f32x4_t (&acc)[ThinStage<PATH>::RT][2]) {
-  constexpr int NB = ThinStage<PATH>::NB;
-  constexpr int kA = ThinLds<PATH>::kA;
-  const int lane = threadIdx.x & 63;
-  wave_lds_fence();  // the previous stage's reads are done before it is overwritten
-  if (PATH == 1) {
-#pragma unroll
-    for (int t = 0; t < ThinStage<PATH>::RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pc = i * 64 + lane;
-        lds[(16 * t + (pc >> 4)) * 17 + (pc & 15)] = st.A[t][i];
-      }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = i * 64 + lane;
-      lds[kA + b * 32 * 17 + (pc >> 4) * 17 + (pc & 15)] = st.B[b][i];
-    }
-  wave_lds_fence();
-  const int r = lane & 15, q = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4_t B[2][NB];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) B[g][b] = lds[kA + b * 32 * 17 + (16 * g + r) * 17 + 4 * j + q];
-#pragma unroll
-    for (int t = 0; t < ThinStage<PATH>::RT; ++t) {
-      const u32x4_t A = PATH == 1 ? lds[(16 * t + r) * 17 + 4 * j + q] : st.A[t][j];
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A), as_bf16x8(B[g][b]), acc[t][g], 0, 0, 0);
-    }
-  }
-}
-
-constexpr int kThinPieces = ThinLds<0>::kPieces > ThinLds<1>::kPieces ? ThinLds<0>::kPieces : ThinLds<1>::kPieces;
-static_assert(kThinPieces * 16 >= ThinStage<0>::RT * 2 * 4 * 64 * 4 && kThinPieces * 16 >= ThinStage<1>::RT * 2 * 4 * 64 * 4,
-              "the final sums reuse a wavefront's region");
-
-template <int PATH>
-__device__ __forceinline__ void bthin_path(const BArgs &a, u32x4_t (*lds)[kThinPieces], const int *toks,
-                                           int rb) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int r0 = rb * ThinStage<PATH>::kRows;
-  // one zero piece per lane (a uniform fallback address becomes a branch)
-  const u32x4_t *zero = static_cast<const u32x4_t *>(a.zeros) + (lane & 15);
-  const int K = PATH == 0 ? a.kpad : a.d;
-  const int steps = (K + 31) / 32;  // k-steps of 32
-  const int per = (steps + kWaves - 1) / kWaves;
-  const int s0 = wave * per;
-  const int s_end = min(steps, s0 + per);
-  const int kend = min(s_end * 32, PATH == 0 ? a.k : a.d);  // this wavefront's K ends here
-
-  int tk[8];  // token of each of this lane's 16-byte pieces of the token tile
-#pragma unroll
-  for (int i = 0; i < 8; ++i) tk[i] = toks[(i * 64 + lane) >> 4];
-
-  f32x4_t acc[ThinStage<PATH>::RT][2];
-#pragma unroll
-  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) acc[t][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  ThinStage<PATH> sa, sb;
-  thin_load<PATH>(sa, a, s0, kend, r0, tk, zero);
-  for (int st = s0; st < s_end; st += 8) {
-    thin_load<PATH>(sb, a, st + 4, kend, r0, tk, zero);
-    thin_consume<PATH>(sa, lds[wave], acc);
-    thin_load<PATH>(sa, a, st + 8, kend, r0, tk, zero);
-    thin_consume<PATH>(sb, lds[wave], acc);
-  }
-  // partial sums of the four K quarters, through each wavefront's own region:
-  // element ((t * 2 + g) * 4 + i) * 64 + lane
-  wave_lds_fence();
-  float *red = reinterpret_cast<float *>(lds[wave]);
-#pragma unroll
-  for (int t = 0; t < ThinStage<PATH>::RT; ++t)
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[((t * 2 + g) * 4 + i) * 64 + lane] = acc[t][g][i];
-  __syncthreads();
-  uint16_t *Y = static_cast<uint16_t *>(a.y);
-#pragma unroll
-  for (int h = 0; h < 2 * ThinStage<PATH>::RT; ++h) {
-    const int e = tid + h * kBlock;  // (tile, group, element, lane)
-    const int t = e >> 9, g = (e >> 8) & 1, i = (e >> 6) & 3, l = e & 63;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += reinterpret_cast<const float *>(lds[w])[e];
-    const int tok = toks[g * 16 + (l & 15)];
-    const int r = r0 + 16 * t + 4 * (l >> 4) + i;
-    if (tok >= 0 && r < a.d_out) Y[(size_t)tok * a.d_out + r] = f2bf(v);
-  }
-  __syncthreads();  // every wavefront's region is free again
-}
-
-// Both paths in one launch: the workgroups walk the row blocks of every path
-// with 1 to kThin tokens; with no such path they leave after the compaction.
-__global__ void __launch_bounds__(kBlock) bthin_kernel(BArgs a) {
-  __shared__ u32x4_t lds[kWaves][kThinPieces];
-  __shared__ int16_t idx[kMaxBatch];
-  __shared__ int2 scan[kWaves];
-  __shared__ int toks[2][kThin];
-  const int2 cnt = path_lists<kBlock>(a, idx, scan);
-  const int tid = threadIdx.x;
   if (tid < 2 * kThin) {
     const int p = tid / kThin, i = tid % kThin;
     const int c = p == 0 ? cnt.x : cnt.y;
-    toks[p][i] = i < c ? idx[(p == 0 ? 0 : cnt.x) + i] : -1;
+    L.toks[p][i] = i < c ? L.idx[(p == 0 ? 0 : cnt.x) + i] : -1;
   }
   __syncthreads();
-  const int nf = (cnt.x > 0 && cnt.x <= kThin) ? (a.d_out + ThinStage<0>::kRows - 1) / ThinStage<0>::kRows : 0;
-  const int ns = (cnt.y > 0 && cnt.y <= kThin) ? (a.d_out + ThinStage<1>::kRows - 1) / ThinStage<1>::kRows : 0;
-  for (int it = blockIdx.x; it < nf + ns; it += gridDim.x) {
-    if (it < nf)
-      bthin_path<0>(a, lds, toks[0], it);
+  // row-stream items: pairs of row blocks (a block past d_out reads zeros
+  // and writes nothing), fast path first
+  const int bf = (cnt.x > 0 && cnt.x <= kThin) ? (a.d_out + ThinStage<0>::kRows - 1) / ThinStage<0>::kRows : 0;
+  const int bs = (cnt.y > 0 && cnt.y <= kThin) ? (a.d_out + ThinStage<1>::kRows - 1) / ThinStage<1>::kRows : 0;
+  const int pf = (bf + 1) / 2;
+  const int nt = pf + (bs + 1) / 2;
+  // wide items
+  const int tiles = (a.d_out + 63) / 64;
+  const int rgs = (a.d_out + kWideRows - 1) / kWideRows;
+  const int nf = cnt.x > kThin ? ((cnt.x + kWideTok - 1) / kWideTok) * rgs : 0;
+  const int ns = cnt.y > kThin ? tiles : 0;
+  const int half = tid / kBlock;
+  int it = blockIdx.x;
+  for (; it < nt; it += gridDim.x) {
+    if (it < pf)
+      bthin_path<0>(a, L.thin + kWaves * half, L.toks[0], 2 * it + half);
     else
-      bthin_path<1>(a, lds, toks[1], it - nf);
+      bthin_path<1>(a, L.thin + kWaves * half, L.toks[1], 2 * (it - pf) + half);
+  }
+  for (; it < nt + nf + ns; it += gridDim.x) {
+    if (it < nt + nf) {
+      const int jt = it - nt, tr = jt / rgs;
+      wide_fast_item(a, reinterpret_cast<unsigned char *>(&L.Bs[0][0][0]), L.idx + tr * kWideTok,
+                     min(kWideTok, cnt.x - tr * kWideTok), jt % rgs);
+    } else {
+      bout_path<1>(a, L, it - nt - nf, L.idx + cnt.x, cnt.y);
+    }
   }
 }
 
@@ -1011,20 +1026,13 @@ hipError_t launch_batched(const BArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(bgate_kernel<2>, gg, dim3(kBlock), 0, s, a);
   else
     hipLaunchKernelGGL(bgate_kernel<0>, gg, dim3(kBlock), 0, s, a);
-  // Each path has a wide kernel (more than kThin tokens) and a row-streaming
-  // one (at most kThin); one launch holds the wide kernels of both paths,
-  // one the row-streaming ones.  Their grids are what fits on the chip at
-  // once: the workgroups loop over the work there is.
+  // one output launch: about one workgroup per CU (the LDS of the row
+  // streams leaves room for one), looping over the items of both paths
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, bthin_kernel, kBlock, 0) != hipSuccess || occ < 1)
-    occ = 1;
-  const int tiles = (a.d_out + 63) / 64, rbs = (a.d_out + 15) / 16;  // rbs: row blocks of the larger count
-  hipLaunchKernelGGL(bout_kernel, dim3(cus < 2 * tiles ? cus : 2 * tiles), dim3(kOutThreads), 0, s, a);
-  hipLaunchKernelGGL(bthin_kernel, dim3(occ * cus < 2 * rbs ? occ * cus : 2 * rbs), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(bout_kernel, dim3(cus), dim3(kOutThreads), 0, s, a);
   return hipGetLastError();
 }
 
