@@ -403,11 +403,14 @@ def test_batched_many_tokens_multiple_launches():
                    f64(rho)[sel], torch.bfloat16, what="batched T=4500")
 
 
-@pytest.mark.parametrize("T,n_slow", [(65, 32), (65, 33), (33, 0), (33, 33), (32, 32), (1, 1)])
+@pytest.mark.parametrize("T,n_slow", [(65, 32), (65, 33), (33, 0), (33, 33), (32, 32), (1, 1), (40, 20), (64, 32)])
 def test_batched_thin_and_wide_kernels(T, n_slow):
     """A path with at most 32 tokens streams its matrix by rows, a larger one
-    runs the wide kernel: both sides of that boundary, for both paths, with
-    d_out not a multiple of 16 and k not a multiple of 32."""
+    runs the wide items: both sides of that boundary, for both paths, and
+    both paths streaming by rows in one call (T = 40 and 64: the output
+    launch's row-stream items switch from the fast to the slow path), with
+    d_out not a multiple of 16 (an odd number of row blocks: the last pair's
+    second block lies past d_out) and k not a multiple of 32."""
     d, d_out, k = 1024, 200, 40
     W = synth.gaussian_weight(d_out, d, (97, T, n_slow, 0), dtype=torch.bfloat16)
     v, u = synth.orthonormal_frame(d, k, 16, (97, T, n_slow, 1))
