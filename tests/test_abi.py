@@ -35,6 +35,22 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), f"libgsi.so does not export {n}"
 
 
+TRACE_LIB = os.path.join(ROOT, "rank_gated_memory_amd", "libgsi_trace.so")
+
+
+@pytest.mark.skipif(not os.path.exists(TRACE_LIB), reason="instrumented build not built")
+def test_trace_build_exports_only_there():
+    """The per-job trace entry points live in the instrumented build only,
+    which also exports every declared symbol; the product library does not
+    have them."""
+    tr = ctypes.CDLL(TRACE_LIB)
+    assert hasattr(tr, "gsi_trace_read") and hasattr(tr, "gsi_trace_reset")
+    for n in declared_functions():
+        assert hasattr(tr, n), f"libgsi_trace.so does not export {n}"
+    L = gsi.lib()
+    assert not hasattr(L, "gsi_trace_read") and not hasattr(L, "gsi_trace_reset")
+
+
 def test_version_and_status_strings():
     assert gsi.gsi_abi_version() == 3
     m = re.search(r"#define GSI_ABI_VERSION (\d+)", open(HEADER).read())
