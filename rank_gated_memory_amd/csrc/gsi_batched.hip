@@ -457,11 +457,11 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
 // bound by HBM.  A row block is 16 RT output rows (RT tiles of 16), run by
 // four wavefronts (half of the output kernel's workgroup) that take a
 // quarter of K each and meet in LDS at the end, so there is no barrier in
-// the K loop.  v_mfma_f32_16x16x32_bf16 with A = 16
-// matrix rows and B = 16 tokens (kThin tokens are two B groups).  Every
-// workgroup reads all of the path's token rows, so more rows per workgroup
-// means fewer token bytes per matrix byte: with 32 rows (the slow path) the
-// CUs take in one byte of x per byte of W (with 16 rows, two).
+// the K loop.  v_mfma_f32_16x16x32_bf16 with A = 16 matrix rows and B = 16
+// tokens (kThin tokens are two B groups).  Every row block reads all of the
+// path's token rows, so more rows per block means fewer token bytes per
+// matrix byte: with 32 rows (the slow path) the CUs take in one byte of x
+// per byte of W (with 16 rows, two).
 //
 // In the MFMA operand layout the 16 lanes of a quarter-wave hold 16 different
 // rows, so loading W rows or token rows in that layout touches 16 cache lines
@@ -483,10 +483,10 @@ __device__ __forceinline__ void out_mma(const u32x4_t (*Bs)[64], const u32x4_t *
 template <int PATH>
 struct ThinStage {
   static constexpr int NB = PATH == 0 ? 2 : 1;  // B matrices: (g hi, g lo) or (x)
-  // 16-row tiles of a workgroup (the fast path's two B matrices leave no
+  // 16-row tiles of a row block (the fast path's two B matrices leave no
   // registers for a second tile at two wavefronts per SIMD)
   static constexpr int RT = PATH == 0 ? GSI_THIN_RT_FAST : GSI_THIN_RT_SLOW;
-  static constexpr int kRows = 16 * RT;  // output rows of a workgroup
+  static constexpr int kRows = 16 * RT;  // output rows of a row block
   u32x4_t A[RT][4];  // slow: piece i * 64 + lane of row tile t (16 x 256 bytes); fast: k-step i of tile t of M
   u32x4_t B[NB][8];  // piece i * 64 + lane of the 32 x 256-byte token tile
 };
