@@ -901,10 +901,10 @@ __device__ __forceinline__ void wide_fast_item(const BArgs &a, unsigned char *ld
 // blocks, one per half of the workgroup), then the wide items of the paths
 // with more (the fast path in items of 64 tokens x 256 rows, the slow
 // path's 64-column tiles).  A call with both kinds of path thus runs them in
-// one launch.  The two kinds are walked in two loops over the workgroup's
-// items (blockIdx.x, + gridDim.x, ...): within one loop the registers each
-// role keeps for its items would be live across the other's, which does not
-// fit (both roles use all 256).  With no work the workgroups leave after the
+// one launch.  Each role is walked in a loop of its own over the
+// workgroup's items (blockIdx.x, + gridDim.x, ...): within one loop the
+// registers each role keeps for its items would be live across the other's,
+// which does not fit (the roles use up to all 256).  With no work the workgroups leave after the
 // compaction.
 __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
   __shared__ __align__(16) OutLds L;
@@ -939,15 +939,12 @@ __global__ void __launch_bounds__(kOutThreads, 1) bout_kernel(BArgs a) {
     else
       bthin_path<1>(a, L.thin + kWaves * half, L.toks[1], 2 * (it - pf) + half);
   }
-  for (; it < nt + nf + ns; it += gridDim.x) {
-    if (it < nt + nf) {
-      const int jt = it - nt, tr = jt / rgs;
-      wide_fast_item(a, reinterpret_cast<unsigned char *>(&L.Bs[0][0][0]), L.idx + tr * kWideTok,
-                     min(kWideTok, cnt.x - tr * kWideTok), jt % rgs);
-    } else {
-      bout_path<1>(a, L, it - nt - nf, L.idx + cnt.x, cnt.y);
-    }
+  for (; it < nt + nf; it += gridDim.x) {
+    const int jt = it - nt, tr = jt / rgs;
+    wide_fast_item(a, reinterpret_cast<unsigned char *>(&L.Bs[0][0][0]), L.idx + tr * kWideTok,
+                   min(kWideTok, cnt.x - tr * kWideTok), jt % rgs);
   }
+  for (; it < nt + nf + ns; it += gridDim.x) bout_path<1>(a, L, it - nt - nf, L.idx + cnt.x, cnt.y);
 }
 
 // ---------------------------------------------------------------------------
