@@ -826,6 +826,20 @@ struct Sched {
   uint32_t to;    // output ticket held
   uint64_t open;  // last open word seen for wave w
   int fresh;      // first pass after entering wave w
+  int uc0;        // call of the first (static) projection ticket of wave w, or -1
+};
+
+// Descriptors of the calls of the current wave, copied to LDS when a
+// workgroup enters the wave (while it waits for the previous wave), for
+// waves of at most kCdCache calls: a latency-bound wave's jobs then read
+// their call from LDS instead of making a round trip to the plan.
+#ifndef GSI_CD_CACHE
+#define GSI_CD_CACHE 1
+#endif
+constexpr int kCdCache = 4;
+struct CdCache {
+  CallDesc cd[kCdCache];
+  int q0, n;  // first call of the wave and the count cached (0: none)
 };
 
 // Tickets of a wave: the first of each kind is the workgroup's index; the
@@ -873,7 +887,7 @@ __device__ __forceinline__ uint64_t load_open(const FArgs &a, int w) {
 // the last unit.  The first ticket of each kind in a wave is the workgroup's
 // own index (no atomic); the counters hand out the tickets from the grid
 // size on.
-__device__ void next_job(const FArgs &a, Sched &st, int *job) {
+__device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
   const int lane = threadIdx.x;
   st.pf = 0;
   int polls = 0;
@@ -882,6 +896,24 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
     const int w = st.w;
     uint32_t *wv = wave_ctl(a, w);
     if (!st.entered) {
+      // what this wave's first jobs need from the plan, fetched before the
+      // wait for the previous wave (plan data is never written in a launch)
+      {
+        const int p0e = a.wave_tab[w];
+        const int npe = a.wave_tab[w + 1] - p0e;
+        st.uc0 = (int)blockIdx.x < npe ? a.unit_call[p0e + blockIdx.x] : -1;
+        const int q0e = a.wave_tab[a.n_waves + 1 + w];
+        const int nqe = a.wave_tab[a.n_waves + 2 + w] - q0e;
+        const int ncache = GSI_CD_CACHE && nqe <= kCdCache ? nqe : 0;
+        constexpr int kWords = (int)(sizeof(CallDesc) / 4);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.table + q0e);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(cc->cd);
+        for (int i = lane; i < ncache * kWords; i += 64) dst[i] = src[i];
+        if (lane == 0) {
+          cc->q0 = q0e;
+          cc->n = ncache;
+        }
+      }
       if (w > 0) {
         // x of this wave may be y of the previous one: wait until every
         // workgroup has left that wave (each leaves once the wave has no
@@ -915,7 +947,7 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
       const uint32_t tp = bcast(st.tp);
       st.p_held = 0;
       if ((int)tp < np) {
-        set_job(job, kJobProj, a.unit_call[p0 + tp], p0 + (int)tp, 0);
+        set_job(job, kJobProj, tp == blockIdx.x && st.uc0 >= 0 ? st.uc0 : a.unit_call[p0 + tp], p0 + (int)tp, 0);
         st.last_out = 0;
         st.pf = 1;
         return;
@@ -985,7 +1017,7 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job) {
       const uint32_t tp = bcast(st.tp);
       st.p_held = 0;
       if ((int)tp < np) {
-        set_job(job, kJobProj, a.unit_call[p0 + tp], p0 + (int)tp, 0);
+        set_job(job, kJobProj, tp == blockIdx.x && st.uc0 >= 0 ? st.uc0 : a.unit_call[p0 + tp], p0 + (int)tp, 0);
         st.last_out = 0;
         st.pf = 1;
         return;
@@ -1055,12 +1087,13 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0, -1};
+  __shared__ __align__(16) CdCache cc;
   int cur = -1, cur_slow = 0;
   GSI_TRACE_ONLY(unsigned tn = 0; unsigned long long tj = wall_clock64(); if (tid == 0) trace_rec(tn, tj, tj, 9, 0, 0, 0);)
   for (;;) {
     GSI_TRACE_ONLY(const unsigned long long tq = wall_clock64();)
-    if (tid < 64) next_job(a, st, s_job);
+    if (tid < 64) next_job(a, st, s_job, &cc);
     __syncthreads();
     const int kind = s_job[0];
     const int c = __builtin_amdgcn_readfirstlane(s_job[1]);
@@ -1070,7 +1103,8 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
     GSI_TRACE_ONLY(tj = wall_clock64(); if (tid == 0) trace_rec(tn, tq, tj, 8, 0, 0, 0);)
     if (kind == kJobDone) break;
     if (tid < 64) sched_prefetch(a, st);
-    const CallDesc cd = a.table[c];
+    const int ci = c - cc.q0;
+    const CallDesc cd = ci >= 0 && ci < cc.n ? cc.cd[ci] : a.table[c];
     if (kind == kJobProj) {
       cur = -1;  // the partials overwrite staged x / g
       const int q = u - cd.a_begin;
