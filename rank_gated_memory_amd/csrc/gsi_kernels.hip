@@ -57,8 +57,11 @@ namespace gsi {
 // record per job into the workgroup's own slots (no shared counter, so
 // recording adds no contended atomics), {start, end, block << 32 | kind << 8
 // | slow, call << 32 | unit}, with times from the 100 MHz constant clock.
-// kind: 1 projection unit, 2 output unit, 7 leaving the job loop, 8 choosing
-// the next job (including any wait for a gate or a wave), 9 workgroup start;
+// kind: 1 projection unit, 2 output unit (in a wave with static output
+// tickets: from the ticket's first loads, including the wait for the gate),
+// 7 leaving the job loop, 8 choosing the next job (including any wait for a
+// gate or a wave), 9 workgroup start, 10 a static output ticket left void by
+// its gate;
 // unused slots stay zero.  A unit's end is taken after its memory operations
 // completed (s_waitcnt 0), which the product build does not wait for.  Read
 // back with gsi_trace_read, cleared with gsi_trace_reset (extern "C",
@@ -525,23 +528,33 @@ __global__ void __launch_bounds__(kBlock) proj_kernel(KArgs a) {
 // Fast unit of one 64-row tile: wavefront w takes the 16-byte column
 // vectors w, w + kWaves, ... of every row (one row per lane) and the four
 // partial sums meet in LDS (`scr`, kWaves x 64 floats), added in wavefront
-// order.  Used by latency-bound waves, where a unit must be small.
+// order.  Used by latency-bound waves, where a unit must be small.  The
+// first batch of loads is a separate step (fast_tile_load), so that a caller
+// can issue it before g is known.
 template <typename T, int UNROLL>
-__device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, const float *gs,
-                                                float *scr) {
+__device__ __forceinline__ void fast_tile_load(const CallDesc &cd, int tile, uint4 (&v)[UNROLL]) {
+  constexpr int VW = Vec<T>::VW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int kv = cd.k / VW;
+  const uint4 *m = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * kTileRows * kv + lane;
+#pragma unroll
+  for (int j = 0; j < UNROLL; ++j) {
+    const int cg = wave + j * kWaves;
+    v[j] = cg < kv ? ld_stream(m + (size_t)cg * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <typename T, int UNROLL>
+__device__ __forceinline__ void fast_tile_finish(const CallDesc &cd, int tile, uint4 (&v)[UNROLL], const float *gs,
+                                                 float *scr) {
   constexpr int VW = Vec<T>::VW;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int kv = cd.k / VW;
   const uint4 *m = reinterpret_cast<const uint4 *>(cd.M) + (size_t)tile * kTileRows * kv + lane;
   float a0 = 0.f, a1 = 0.f;
-  for (int cg0 = wave; cg0 < kv; cg0 += kWaves * UNROLL) {
-    uint4 v[UNROLL];
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      const int cg = cg0 + j * kWaves;
-      v[j] = cg < kv ? ld_stream(m + (size_t)cg * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
-    }
+  for (int cg0 = wave;;) {
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
       const int cg = cg0 + j * kWaves;
@@ -556,6 +569,13 @@ __device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, co
         }
       }
     }
+    cg0 += kWaves * UNROLL;
+    if (cg0 >= kv) break;
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int cg = cg0 + j * kWaves;
+      v[j] = cg < kv ? ld_stream(m + (size_t)cg * kTileRows) : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   scr[wave * 64 + lane] = a0 + a1;
   __syncthreads();
@@ -567,6 +587,13 @@ __device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, co
     if (o < cd.d_out) store_y<T>(cd, o, t);
   }
   __syncthreads();  // scr is free again
+}
+
+template <typename T, int UNROLL>
+__device__ __forceinline__ void fast_tile_split(const CallDesc &cd, int tile, const float *gs, float *scr) {
+  uint4 v[UNROLL];
+  fast_tile_load<T, UNROLL>(cd, tile, v);
+  fast_tile_finish<T, UNROLL>(cd, tile, v, gs, scr);
 }
 
 template <typename T, int UNROLL>
@@ -773,7 +800,19 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
 // proj_kernel; s_waitcnt 0 before a barrier orders a workgroup's stores
 // before the control word that publishes them.
 // ---------------------------------------------------------------------------
-enum { kJobDone = 0, kJobProj = 1, kJobOut = 2 };
+enum { kJobDone = 0, kJobProj = 1, kJobOut = 2, kJobOutStatic = 3 };
+
+// Latency-bound waves (at most kCdCache calls, each with one-tile fast
+// units and its own projection) number their output tickets statically, in
+// plan order: first every call's fast tiles (each ticket also the call's
+// slow unit of the same index if its gate goes slow), then the slow units
+// beyond those.  A workgroup holding such a ticket knows its call and unit
+// before the gate is decided: it issues the loads of its image tile, then
+// waits for the call's gate word (written by the finishing workgroup once
+// g has landed), then needs only g.  The open list is not used there.
+#ifndef GSI_STATIC_WAVES
+#define GSI_STATIC_WAVES 1
+#endif
 
 // Rows of V_k in flight per thread in a projection unit of the single-launch
 // kernel.
@@ -827,6 +866,7 @@ struct Sched {
   uint64_t open;  // last open word seen for wave w
   int fresh;      // first pass after entering wave w
   int uc0;        // call of the first (static) projection ticket of wave w, or -1
+  int stat;       // wave w numbers its output tickets statically (see kJobOutStatic)
 };
 
 // Descriptors of the calls of the current wave, copied to LDS when a
@@ -876,6 +916,26 @@ __device__ __forceinline__ uint64_t load_open(const FArgs &a, int w) {
   return bcast64(ow);
 }
 
+// Leave wave w.  The outputs this workgroup wrote in it have landed (each
+// output unit of a wave with a successor ends with s_waitcnt 0 and a
+// barrier).  The last workgroup of its group to leave counts the group; the
+// last group raises the ready flags of the next wave's entry.
+__device__ __forceinline__ void leave_wave(const FArgs &a, Sched &st, uint32_t *wv, int w, int lane) {
+  if (lane == 0 && w + 1 < a.n_waves) {
+    const uint32_t g = blockIdx.x % kGroups;
+    const uint32_t gsize = (gridDim.x - g + kGroups - 1) / kGroups;
+    if (ctl_add(wv + kWvLeft + 32 * g, 1u) == gsize - 1) {
+      const uint32_t ngroups = gridDim.x < (uint32_t)kGroups ? gridDim.x : (uint32_t)kGroups;
+      if (ctl_add(wv + kWvGroups, 1u) == ngroups - 1) {
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) ctl_store(wv + kWvReady + 32 * q, 1u);
+      }
+    }
+  }
+  st.w += 1;
+  st.entered = 0;
+}
+
 // Picks the next job of this workgroup (wavefront 0): job = {kind, call,
 // unit, slow} in LDS.  Within a wave a workgroup holds one output ticket
 // and at most one projection ticket.  It runs its output unit as soon as
@@ -913,6 +973,12 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
           cc->q0 = q0e;
           cc->n = ncache;
         }
+        int ok = 1;
+        if (lane < ncache) {
+          const CallDesc &dd = a.table[q0e + lane];
+          ok = dd.fast_tiles == 1 && dd.share_next == 0 && dd.a_units > 0;
+        }
+        st.stat = GSI_STATIC_WAVES && ncache > 0 && ncache == nqe && __ballot(!ok) == 0;
       }
       if (w > 0) {
         // x of this wave may be y of the previous one: wait until every
@@ -942,6 +1008,43 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
     }
     const int p0 = a.wave_tab[w];
     const int np = a.wave_tab[w + 1] - p0;
+    if (st.stat) {
+      // every projection ticket before any output ticket: an output job
+      // waits for its call's gate, which needs every projection unit
+      if (!st.p_out) {
+        if (!st.p_held) {
+          uint32_t t = 0;
+          if (lane == 0) t = take_ticket(wv + kWvProj);
+          st.tp = t;
+        }
+        const uint32_t tp = bcast(st.tp);
+        st.p_held = 0;
+        if ((int)tp < np) {
+          set_job(job, kJobProj, tp == blockIdx.x && st.uc0 >= 0 ? st.uc0 : a.unit_call[p0 + tp], p0 + (int)tp, 0);
+          st.last_out = 0;
+          st.pf = 1;
+          return;
+        }
+        st.p_out = 1;
+      }
+      // output ticket -> (call, region, unit) from the cached descriptors
+      const uint32_t to = bcast(st.to);
+      uint32_t base = 0;
+      for (int r = 0; r < 2; ++r)
+        for (int i = 0; i < cc->n; ++i) {
+          const int fu = cc->cd[i].fast_units, su = cc->cd[i].slow_units;
+          const uint32_t cnt = (uint32_t)(r == 0 ? fu : (su > fu ? su - fu : 0));
+          if (to - base < cnt) {
+            set_job(job, kJobOutStatic, cc->q0 + i, (int)(to - base), r);
+            st.last_out = 1;
+            st.pf = 2;
+            return;
+          }
+          base += cnt;
+        }
+      leave_wave(a, st, wv, w, lane);
+      continue;
+    }
     if (st.p_held && st.last_out) {
       // a projection ticket waited through one output unit: run it now
       const uint32_t tp = bcast(st.tp);
@@ -1025,23 +1128,7 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
       st.p_out = 1;
     }
     if ((uint32_t)(st.open >> 40) == ncalls) {  // every gate open and `to` beyond the last unit
-      // Leave the wave.  The outputs this workgroup wrote in it have landed
-      // (each output unit of a wave with a successor ends with s_waitcnt 0
-      // and a barrier).  The last workgroup of its group to leave counts the
-      // group; the last group raises the ready flags of the next wave's entry.
-      if (lane == 0 && w + 1 < a.n_waves) {
-        const uint32_t g = blockIdx.x % kGroups;
-        const uint32_t gsize = (gridDim.x - g + kGroups - 1) / kGroups;
-        if (ctl_add(wv + kWvLeft + 32 * g, 1u) == gsize - 1) {
-          const uint32_t ngroups = gridDim.x < (uint32_t)kGroups ? gridDim.x : (uint32_t)kGroups;
-          if (ctl_add(wv + kWvGroups, 1u) == ngroups - 1) {
-#pragma unroll
-            for (int q = 0; q < kGroups; ++q) ctl_store(wv + kWvReady + 32 * q, 1u);
-          }
-        }
-      }
-      st.w += 1;
-      st.entered = 0;
+      leave_wave(a, st, wv, w, lane);
       continue;
     }
     // nothing to do until another gate of this wave opens
@@ -1063,6 +1150,73 @@ __device__ __forceinline__ void sched_prefetch(const FArgs &a, Sched &st) {
   }
 }
 
+// x of a call staged in LDS for its slow units (agent-coherent loads when
+// an earlier wave of the launch wrote it).
+template <typename T>
+__device__ __forceinline__ void stage_x(const CallDesc &cd, uint4 *xs) {
+  constexpr int VW = Vec<T>::VW;
+  const int nv = cd.d / VW;
+  if (cd.flags & kCallXCoherent) {
+    const uint32_t *xw = static_cast<const uint32_t *>(cd.x);
+    for (int i = threadIdx.x; i < nv; i += kBlock)
+      xs[i] = make_uint4(ctl_load(xw + 4 * i), ctl_load(xw + 4 * i + 1), ctl_load(xw + 4 * i + 2),
+                         ctl_load(xw + 4 * i + 3));
+  } else {
+    const uint4 *xp = static_cast<const uint4 *>(cd.x);
+    for (int i = threadIdx.x; i < nv; i += kBlock) xs[i] = xp[i];
+  }
+}
+
+// One static output ticket (see kJobOutStatic) of call c: region 0 = fast
+// tile u or slow unit u, region 1 = slow unit fast_units + u.  Issues the
+// tile's first loads, waits (bounded) for the call's gate word, then runs
+// the unit the gate selects, if any.  Returns the path run (0 fast, 1 slow)
+// or -1 for a void ticket.  cur / cur_slow: what xs / gs hold.
+template <typename T, int UNROLL>
+__device__ __forceinline__ int static_output(const FArgs &a, const CallDesc &cd, int c, int u, int region,
+                                             int &cur, int &cur_slow, uint4 *xs, float *gs, float *scr,
+                                             int *flag) {
+  uint4 mv[UNROLL];
+  if (region == 0) fast_tile_load<T, UNROLL>(cd, u, mv);
+  if (threadIdx.x == 0) {
+    uint64_t e = ctl_load64(a.entries + c);
+    for (int s = 0; e == 0; ++s) {
+      if (s >= a.spin_limit) {
+        ctl_max(a.ctl + kCtlStatus, 5u);
+        e = 3;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      e = ctl_load64(a.entries + c);
+    }
+    *flag = (int)e;
+  }
+  __syncthreads();
+  const int gate = *flag;  // 1 fast, 2 slow, 3 the wait ran out
+  if (gate == 1 && region == 0) {
+    if (c != cur || cur_slow) {
+      for (int j = threadIdx.x; j < cd.k; j += kBlock) gs[j] = load_coherent(a.wsf + cd.g_off + j);
+      __syncthreads();
+      cur = c;
+      cur_slow = 0;
+    }
+    fast_tile_finish<T, UNROLL>(cd, u, mv, gs, scr);
+    return 0;
+  }
+  const int su = region == 0 ? u : cd.fast_units + u;
+  if (gate == 2 && su < cd.slow_units) {
+    if (c != cur || !cur_slow) {
+      stage_x<T>(cd, xs);
+      __syncthreads();
+      cur = c;
+      cur_slow = 1;
+    }
+    slow_unit<T, UNROLL>(cd, su, xs);
+    return 1;
+  }
+  return -1;
+}
+
 // Two workgroups of four wavefronts per CU (see launch_stack_mode): the
 // register budget of two wavefronts per SIMD lets the compiler keep every
 // streaming load of a unit in flight (measured 290 -> 238 us per 112-map
@@ -1074,7 +1228,6 @@ __device__ __forceinline__ void sched_prefetch(const FArgs &a, Sched &st) {
 
 template <typename T, int UNROLL, int MODE>
 __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
-  constexpr int VW = Vec<T>::VW;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float sh[kWaves];
   __shared__ int s_job[4];
@@ -1087,7 +1240,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0, -1};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0, -1, 0};
   __shared__ __align__(16) CdCache cc;
   int cur = -1, cur_slow = 0;
   GSI_TRACE_ONLY(unsigned tn = 0; unsigned long long tj = wall_clock64(); if (tid == 0) trace_rec(tn, tj, tj, 9, 0, 0, 0);)
@@ -1105,6 +1258,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
     if (tid < 64) sched_prefetch(a, st);
     const int ci = c - cc.q0;
     const CallDesc cd = ci >= 0 && ci < cc.n ? cc.cd[ci] : a.table[c];
+    GSI_TRACE_ONLY(int t_kind = kind; int t_u = u; int t_slow = slow;)
     if (kind == kJobProj) {
       cur = -1;  // the partials overwrite staged x / g
       const int q = u - cd.a_begin;
@@ -1121,7 +1275,11 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         const float3 r = finish_projection<T, true>(cd, p0, rows, a.wsf + cd.g_off, a.counters, sh, red);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // g of every thread is stored before any gate opens
-        if (tid == 0) {
+        if (tid == 0 && st.stat) {
+          // a wave with static output tickets: publish the gate in the call's word
+          const int sl = decide_gate<MODE>(cd, r, a.gate);
+          ctl_store64(a.entries + c, 1u + (uint64_t)sl);
+        } else if (tid == 0) {
           // open the gates of this call and of every call sharing its
           // projection: append each to its wave's open list
           uint32_t *wv = wave_ctl(a, cd.wave);
@@ -1137,22 +1295,23 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
           }
         }
       }
+    } else if (kind == kJobOutStatic) {
+      // A static output ticket: region `slow` of the call's tickets, 0 = fast
+      // tile u (or slow unit u), 1 = slow unit fast_units + u.  The tile's
+      // first loads go out before the wait for the gate.
+      const int sl = static_output<T, UNROLL>(a, cd, c, u, slow, cur, cur_slow, xs, gs, scr, &s_flag);
+      GSI_TRACE_ONLY(t_kind = sl >= 0 ? kJobOut : 10; t_slow = sl; t_u = slow && sl > 0 ? cd.fast_units + u : u;)
+      (void)sl;
+      if (cd.wave + 1 < a.n_waves) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
     } else {
       if (c != cur || slow != cur_slow) {
-        if (slow) {
-          const int nv = cd.d / VW;
-          const uint4 *xp = static_cast<const uint4 *>(cd.x);
-          if (cd.flags & kCallXCoherent) {
-            const uint32_t *xw = static_cast<const uint32_t *>(cd.x);
-            for (int i = tid; i < nv; i += kBlock)
-              xs[i] = make_uint4(ctl_load(xw + 4 * i), ctl_load(xw + 4 * i + 1),
-                                 ctl_load(xw + 4 * i + 2), ctl_load(xw + 4 * i + 3));
-          } else {
-            for (int i = tid; i < nv; i += kBlock) xs[i] = xp[i];
-          }
-        } else {
+        if (slow)
+          stage_x<T>(cd, xs);
+        else
           for (int j = tid; j < cd.k; j += kBlock) gs[j] = load_coherent(a.wsf + cd.g_off + j);
-        }
         __syncthreads();
         cur = c;
         cur_slow = slow;
@@ -1168,7 +1327,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
         __syncthreads();
       }
     }
-    GSI_TRACE_ONLY(__builtin_amdgcn_s_waitcnt(0); if (tid == 0) trace_rec(tn, tj, wall_clock64(), kind, c, u, slow);)
+    GSI_TRACE_ONLY(__builtin_amdgcn_s_waitcnt(0); if (tid == 0) trace_rec(tn, tj, wall_clock64(), t_kind, c, t_u, t_slow);)
   }
   GSI_TRACE_ONLY(if (tid == 0) { const unsigned long long te = wall_clock64(); trace_rec(tn, te, te, 7, 0, 0, 0); })
 
