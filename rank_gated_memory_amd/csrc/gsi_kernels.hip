@@ -813,6 +813,15 @@ enum { kJobDone = 0, kJobProj = 1, kJobOut = 2, kJobOutStatic = 3 };
 #ifndef GSI_STATIC_WAVES
 #define GSI_STATIC_WAVES 1
 #endif
+// Polls of a gate word before the image tile's loads are issued (they are
+// issued at once if the gate is decided earlier), and the sleep between
+// polls (units of 64 clocks).
+#ifndef GSI_STATIC_PREFETCH_DELAY
+#define GSI_STATIC_PREFETCH_DELAY 0
+#endif
+#ifndef GSI_STATIC_POLL_SLEEP
+#define GSI_STATIC_POLL_SLEEP 1
+#endif
 
 // Rows of V_k in flight per thread in a projection unit of the single-launch
 // kernel.
@@ -1177,22 +1186,26 @@ __device__ __forceinline__ int static_output(const FArgs &a, const CallDesc &cd,
                                              int &cur, int &cur_slow, uint4 *xs, float *gs, float *scr,
                                              int *flag) {
   uint4 mv[UNROLL];
-  if (region == 0) fast_tile_load<T, UNROLL>(cd, u, mv);
-  if (threadIdx.x == 0) {
-    uint64_t e = ctl_load64(a.entries + c);
-    for (int s = 0; e == 0; ++s) {
-      if (s >= a.spin_limit) {
+  if (region == 0 && GSI_STATIC_PREFETCH_DELAY < 0) fast_tile_load<T, UNROLL>(cd, u, mv);
+  int gate = 0;
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) {
+      uint64_t e = ctl_load64(a.entries + c);
+      if (e == 0 && it >= a.spin_limit) {
         ctl_max(a.ctl + kCtlStatus, 5u);
         e = 3;
-        break;
       }
-      __builtin_amdgcn_s_sleep(1);
-      e = ctl_load64(a.entries + c);
+      *flag = (int)e;
     }
-    *flag = (int)e;
+    __syncthreads();
+    gate = *flag;
+    __syncthreads();
+    if (GSI_STATIC_PREFETCH_DELAY >= 0 && region == 0 && (gate != 0 || it == GSI_STATIC_PREFETCH_DELAY) &&
+        it <= GSI_STATIC_PREFETCH_DELAY)
+      fast_tile_load<T, UNROLL>(cd, u, mv);
+    if (gate) break;
+    __builtin_amdgcn_s_sleep(GSI_STATIC_POLL_SLEEP);
   }
-  __syncthreads();
-  const int gate = *flag;  // 1 fast, 2 slow, 3 the wait ran out
   if (gate == 1 && region == 0) {
     if (c != cur || cur_slow) {
       for (int j = threadIdx.x; j < cd.k; j += kBlock) gs[j] = load_coherent(a.wsf + cd.g_off + j);
