@@ -16,7 +16,9 @@
 //                  levels of at most 64 rows for calls with many units),
 //                  forms ||g||^2, rho and the gate (GSI-TS §2.2) and appends
 //                  the call to the wave's open list; output units of open
-//                  calls run while other calls still project.  A wave is
+//                  calls run while other calls still project (latency-bound
+//                  waves number their output tickets statically instead and
+//                  publish each gate in a word of its own).  A wave is
 //                  entered once every workgroup has left the previous one
 //                  (per-group counters and ready flags), so a call may read
 //                  the y of an earlier wave.  Every device-side wait is
