@@ -91,9 +91,14 @@ def check_chain(outs, ref, dtype, what):
     return worst
 
 
+@pytest.mark.parametrize("chains,slow_chains", [(4, (1, 3)), (2, (1,))], ids=["8-call-waves", "4-call-waves"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
-def test_chained_stack_matches_oracle_chain(dtype):
-    st, outs, calls = build_chain(dtype)
+def test_chained_stack_matches_oracle_chain(dtype, chains, slow_chains):
+    """Waves of 8 calls hand out output units through the open list; waves of
+    at most 4 calls number their output tickets statically (each call's tiles,
+    then its further slow units) and publish each gate in a word of its own.
+    Both with fast and slow calls in every wave."""
+    st, outs, calls = build_chain(dtype, chains=chains, slow_chains=slow_chains)
     ws = st.run()
     sync()
     ref = orc.chain(calls, STORE[dtype])
@@ -106,7 +111,7 @@ def test_chained_stack_matches_oracle_chain(dtype):
     st.run(ws=ws)
     sync()
     assert all(torch.equal(o[3], a) for o, a in zip(outs, y0))
-    print(f"{STORE[dtype]}: {len(outs)} calls in {2 * 3} waves, worst rel L2 {worst:.2e}")
+    print(f"{STORE[dtype]}: {len(outs)} calls in {2 * 3} waves of {2 * chains}, worst rel L2 {worst:.2e}")
 
 
 def test_chained_stack_forced_modes():
