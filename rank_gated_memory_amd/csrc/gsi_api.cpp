@@ -658,6 +658,7 @@ gsi_status gsi_stack(const void *plan_host, const void *plan_dev, int32_t mode, 
   a.max_k = h->max_k;
   a.max_d = h->max_d;
   a.spin_limit = spin_limit();
+  a.units_a = h->units_a;
   const hipError_t e = launch_stack(h->dtype, a, mode, h->units_a + h->units_b,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSI_OK : GSI_E_HIP;

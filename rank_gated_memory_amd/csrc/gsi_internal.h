@@ -171,7 +171,7 @@ struct FArgs {
   int32_t max_k;
   int32_t max_d;
   int32_t spin_limit;        // bound of every device-side wait (polls)
-  int32_t pad_;
+  int32_t units_a;           // projection units of the plan (entries of gcounters)
 };
 
 // A call with more than kGroupUnits2 projection units sums its partials in

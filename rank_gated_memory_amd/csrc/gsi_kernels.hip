@@ -1347,7 +1347,10 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   GSI_TRACE_ONLY(if (tid == 0) { const unsigned long long te = wall_clock64(); trace_rec(tn, te, te, 7, 0, 0, 0); })
 
   // The last workgroup to leave clears the control words (all but the status
-  // word) and the projection counters for the next launch on this workspace.
+  // word) and the projection counters for the next launch on this workspace;
+  // also the group counters of two-level sums, which a completed launch has
+  // already cleared, but a launch whose wait bound ran out may have left
+  // counting a group whose units did not all run.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) s_flag = ctl_add(a.ctl + kCtlExit, 1u) == gridDim.x - 1 ? 1 : 0;
@@ -1358,6 +1361,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
     ctl_store64(a.entries + i, 0u);
     ctl_store(a.counters + i, 0u);
   }
+  for (int i = tid; i < a.units_a; i += kBlock) ctl_store(a.gcounters + i, 0u);
   if (tid == 0) {
     ctl_store(a.ctl + kCtlSeg, 0u);
     ctl_store(a.ctl + kCtlExit, 0u);

@@ -189,3 +189,40 @@ def test_exhausted_wait_bound_drains_and_recovers(monkeypatch):
     gsi.gsi_stack(st, gsi.GATED, ws, check=True)
     assert st.status(ws) == 0
     check_chain(outs, orc.chain(calls, "fp32"), torch.float32, "after recovery")
+
+
+def test_exhausted_wait_bound_recovers_two_level_sums(monkeypatch):
+    """The same with a wide basis in the second wave (16384 x 512: 256
+    projection units whose partials are summed in two levels, groups of 16):
+    a launch whose bound ran out may leave a group of partials half counted,
+    and the next runs on the same workspace still give the bits of a run that
+    never failed."""
+    bf = torch.bfloat16
+    WA = synth.gaussian_weight(16384, 512, (98, 1, 0, 0), dtype=bf)
+    vA, uA = synth.orthonormal_frame(512, 64, 16, (98, 1, 0, 1))
+    WB = synth.gaussian_weight(4096, 16384, (98, 1, 1, 0), dtype=bf)
+    vB, _ = synth.orthonormal_frame(16384, 512, 0, (98, 1, 1, 1))
+    xA, _ = synth.tokens(vA, uA, torch.tensor([False]), (98, 1, 2))
+    mA, mB = gsi.Map(WA.to(DEV), vA.to(bf).to(DEV)), gsi.Map(WB.to(DEV), vB.to(bf).to(DEV))
+    gsi.gsi_prepare(mA)
+    gsi.gsi_prepare(mB)
+    x = xA[0].to(bf).to(DEV)
+    yA = torch.empty(16384, dtype=bf, device=DEV)
+    yB = torch.empty(4096, dtype=bf, device=DEV)
+    st = gsi.Stack([(mA, x, yA, 0.05, None, None, 0), (mB, yA, yB, 0.05, None, None, 1)])
+    ws = gsi.workspace(st.ws_bytes, DEV)
+    gsi.gsi_stack(st, gsi.GATED, ws, check=True)
+    sync()
+    ref = (yA.clone(), yB.clone())
+    monkeypatch.setenv("GSI_SPIN_LIMIT", "0")
+    with pytest.raises(gsi.StackIncomplete):
+        gsi.gsi_stack(st, gsi.GATED, ws, check=True)
+    ws[st.status_offset:st.status_offset + 4] = 0
+    monkeypatch.delenv("GSI_SPIN_LIMIT")
+    for _ in range(3):
+        yA.fill_(float("nan"))
+        yB.fill_(float("nan"))
+        gsi.gsi_stack(st, gsi.GATED, ws, check=True)
+        sync()
+        assert torch.equal(yA, ref[0]) and torch.equal(yB, ref[1])
+    assert st.status(ws) == 0
