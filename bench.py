@@ -331,17 +331,21 @@ def cpu_baseline(wl, seconds):
                       f"{el:.1f}s; step time scaled by {maps_total}/{len(host)} maps"}
 
 
-def kernel_source_sha() -> str:
+STACK_SOURCES = ("gsi_kernels.hip", "gsi_internal.h", "gsi_gram.h")
+BATCHED_SOURCES = ("gsi_batched.hip", "gsi_batched.h", "gsi_gram.h")
+
+
+def kernel_source_sha(files=STACK_SOURCES) -> str:
     """sha256 of the kernel sources; counter figures are only reported for the code they measured."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gsi_kernels.hip", "gsi_internal.h", "gsi_gram.h"):
+    for f in files:
         with open(os.path.join(ROOT, "rank_gated_memory_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel: str, files=STACK_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this code."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
@@ -349,7 +353,7 @@ def measured_traffic(workload: str, kernel: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_sha():
+    if rec.get("source_sha256") != kernel_source_sha(files):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else float(k["hbm_bytes_per_launch"])
@@ -467,7 +471,11 @@ def bench_batched(args):
         # rotated call time
         "roofline": {"bound": "hbm", "kernel": "gsi_linear (bproj, bgate, bout)",
                      "achieved": head["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": head["gbps"] / PEAK_HBM_GBPS, "traffic": None},
+                     "frac": head["gbps"] / PEAK_HBM_GBPS,
+                     # bytes out of the L2s per call of the head cell (bproj + bgate + bout
+                     # counters), when the committed record matches these sources
+                     "traffic": measured_traffic("batched-t256", "gsi_linear (bproj, bgate, bout)",
+                                                 BATCHED_SOURCES)},
         "cpu_baseline": cpu,
     }), flush=True)
 
