@@ -878,6 +878,7 @@ struct Sched {
   int fresh;      // first pass after entering wave w
   int uc0;        // call of the first (static) projection ticket of wave w, or -1
   int stat;       // wave w numbers its output tickets statically (see kJobOutStatic)
+  int vg;         // group whose counter hands out this workgroup's output tickets
 };
 
 // Descriptors of the calls of the current wave, copied to LDS when a
@@ -896,11 +897,38 @@ struct CdCache {
 // Tickets of a wave: the first of each kind is the workgroup's index; the
 // later ones of group g = blockIdx % kGroups are gridDim + kGroups * j + g
 // for j = 0, 1, ... taken from group g's counter.  Every ticket from the
-// grid size on belongs to exactly one group, whose workgroups take its
-// tickets in order until they pass the wave's count.
-__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr0) {
-  const uint32_t g = blockIdx.x % kGroups;
+// grid size on belongs to exactly one group's counter, which hands it out
+// once: the group's workgroups take its tickets in order until they pass
+// the wave's count (and, at the end of a wave, workgroups of groups that
+// have run out of output tickets).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr0, uint32_t g) {
   return gridDim.x + kGroups * ctl_add(ctr0 + 32 * g, 1u) + g;
+}
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr0) { return take_ticket(ctr0, blockIdx.x % kGroups); }
+
+// The groups use up their output tickets at different times (their
+// workgroups run units of different lengths), so a workgroup whose group
+// has none left takes them from the group furthest behind before it leaves
+// the wave (a ticket belongs to one group's counter, whoever takes it).
+#ifndef GSI_STEAL_TAIL
+#define GSI_STEAL_TAIL 1
+#endif
+
+// Lanes 0..7 read the groups' counters at ctr0; returns, uniform over the
+// wavefront, (tickets below `total` left in the fullest group) << 3 | that
+// group.  (Group tickets start at the grid size.)
+__device__ __forceinline__ uint32_t fullest_group(uint32_t *ctr0, uint32_t total, int lane) {
+  uint32_t key = (uint32_t)lane;
+  if (lane < kGroups) {
+    const uint32_t nt = gridDim.x + kGroups * ctl_load(ctr0 + 32 * lane) + (uint32_t)lane;
+    key |= (nt < total ? (total - nt) : 0u) << 3;
+  }
+#pragma unroll
+  for (int o = 4; o >= 1; o >>= 1) {
+    const uint32_t other = (uint32_t)__shfl_xor((int)key, o, 64);
+    key = other > key ? other : key;
+  }
+  return bcast(key);
 }
 
 __device__ __forceinline__ uint32_t *wave_ctl(const FArgs &a, int w) {
@@ -954,8 +982,8 @@ __device__ __forceinline__ void leave_wave(const FArgs &a, Sched &st, uint32_t *
 // projection ticket fetched during a projection unit is run right after at
 // most one output unit, so no ticket that gates other work is held for
 // long.  It waits only when the wave has no projection ticket left, and
-// leaves the wave once every gate is open and its output ticket lies beyond
-// the last unit.  The first ticket of each kind in a wave is the workgroup's
+// leaves the wave once every gate is open and neither its output ticket nor
+// any group's next one lies below the last unit.  The first ticket of each kind in a wave is the workgroup's
 // own index (no atomic); the counters hand out the tickets from the grid
 // size on.
 __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
@@ -1009,6 +1037,7 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
       }
       st.to = blockIdx.x;
       st.tp = blockIdx.x;
+      st.vg = (int)(blockIdx.x % kGroups);
       st.entered = 1;
       st.p_out = 0;
       st.p_held = 1;
@@ -1139,6 +1168,22 @@ __device__ void next_job(const FArgs &a, Sched &st, int *job, CdCache *cc) {
       st.p_out = 1;
     }
     if ((uint32_t)(st.open >> 40) == ncalls) {  // every gate open and `to` beyond the last unit
+      const uint32_t total = (uint32_t)(st.open & kLow40);
+      if (GSI_STEAL_TAIL && total > gridDim.x) {
+        // take a ticket from the group with the most left.  Each attempt
+        // either gets a unit or finds that group exhausted, so the
+        // workgroup leaves after at most kGroups empty attempts.
+        const uint32_t key = fullest_group(wv + kWvOut, total, lane);
+        if (key >> 3) {
+          const uint32_t vg = key & 7u;
+          uint32_t t = 0;
+          if (lane == 0) t = take_ticket(wv + kWvOut, vg);
+          st.to = t;
+          st.vg = (int)vg;
+          st.slot = 0;  // a ticket of another group may lie before the last one held
+          continue;
+        }
+      }
       leave_wave(a, st, wv, w, lane);
       continue;
     }
@@ -1157,7 +1202,7 @@ __device__ __forceinline__ void sched_prefetch(const FArgs &a, Sched &st) {
     if (threadIdx.x == 0) st.tp = take_ticket(wave_ctl(a, st.w) + kWvProj);
     st.p_held = 1;
   } else if (st.pf == 2) {
-    if (threadIdx.x == 0) st.to = take_ticket(wave_ctl(a, st.w) + kWvOut);
+    if (threadIdx.x == 0) st.to = take_ticket(wave_ctl(a, st.w) + kWvOut, (uint32_t)st.vg);
   }
 }
 
@@ -1255,7 +1300,7 @@ __global__ void __launch_bounds__(kBlock) GSI_STACK_ATTR stack_kernel(FArgs a) {
   float *scr = gs + align_up((uint64_t)a.max_k, 4);
   float *red = reinterpret_cast<float *>(smem);
 
-  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0, -1, 0};
+  Sched st{0, 0, 0, 0, 0, 0, 0, 0u, 0u, 0, 0, -1, 0, 0};
   __shared__ __align__(16) CdCache cc;
   int cur = -1, cur_slow = 0;
   GSI_TRACE_ONLY(unsigned tn = 0; unsigned long long tj = wall_clock64(); if (tid == 0) trace_rec(tn, tj, tj, 9, 0, 0, 0);)
