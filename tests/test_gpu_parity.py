@@ -620,6 +620,54 @@ def test_many_projection_units(dtype):
     assert st1.status(ws1) == 0
 
 
+def test_stack_output_tickets_beyond_the_grid():
+    """One wave of 48 calls (4 maps d = 1024 -> 8192, k = 64, x 12 tokens,
+    every other one slow) whose output units (one 64-row image tile per fast
+    unit, 128 rows of W per slow unit: several thousand) outnumber the
+    workgroups many times over.  The eight ticket groups then run dry at
+    different times and workgroups take tickets from other groups before
+    they leave.  Every output row is written (y starts as NaN) and equals
+    the oracle, and three runs on one workspace give the same bits with the
+    status word 0."""
+    dtype = torch.bfloat16
+    d, d_out, k = 1024, 8192, 64
+    items = []
+    for i in range(4):
+        W = synth.gaussian_weight(d_out, d, (97, 0, i, 0), dtype=dtype)
+        v, u = synth.orthonormal_frame(d, k, 16, (97, 0, i, 1))
+        mask = torch.tensor([t % 2 == 1 for t in range(12)])
+        X, _ = synth.tokens(v, u, mask, (97, 0, i))
+        items.append((W, v.to(dtype), X.to(dtype)))
+    calls, outs = [], []
+    for W, V, X in items:
+        m = new_map(W, V)
+        Xd = X.to(DEV)
+        ys = torch.full((X.shape[0], d_out), float("nan"), dtype=dtype, device=DEV)
+        rs = torch.empty(X.shape[0], dtype=torch.float32, device=DEV)
+        ss = torch.empty(X.shape[0], dtype=torch.uint8, device=DEV)
+        for t in range(X.shape[0]):
+            calls.append((m, Xd[t], ys[t], 0.05, rs[t:t + 1], ss[t:t + 1]))
+        outs.append((W, V, X, ys, rs, ss))
+    st = gsi.Stack(calls)
+    ws = gsi.workspace(st.ws_bytes, DEV)
+    ref = None
+    for _ in range(3):
+        gsi.gsi_stack(st, gsi.GATED, ws)
+        sync()
+        assert st.status(ws) == 0
+        got = [tuple(t.clone() for t in o[3:]) for o in outs]
+        if ref is None:
+            ref = got
+        assert all(all(torch.equal(a, b) for a, b in zip(g, r)) for g, r in zip(got, ref))
+    n_slow = 0
+    for W, V, X, ys, rs, ss in outs:
+        assert torch.isfinite(ys.float()).all(), "an output unit was never run"
+        n_slow += int(ss.sum().item())
+        compare_tokens(f64(W), f64(V), f64(X), 0.05, f64(ys), ss.cpu().numpy(), f64(rs), dtype,
+                       rho_tol="norm", what="tickets beyond the grid")
+    assert n_slow == 24
+
+
 # ------------------------------------------------------------- maximum sizes -
 
 @pytest.mark.parametrize("dtype,d,d_out,k", [
