@@ -1,7 +1,8 @@
 """The library's host code (argument checks, workspace sizing, stack plans)
 under AddressSanitizer and UndefinedBehaviorSanitizer, built with warnings as
-errors, running the C-ABI tests of tests/test_abi.py in a child process with
-the ASan runtime preloaded.  CPU only: no kernel is launched."""
+errors, running the C-ABI tests of tests/test_abi.py and the random-plan
+properties of tests/test_plan_properties.py in a child process with the ASan
+runtime preloaded.  CPU only: no kernel is launched."""
 import os
 import subprocess
 import sys
@@ -25,7 +26,8 @@ def test_abi_tests_clean_under_host_sanitizers():
         "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1",
     })
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_abi.py")],
+                        os.path.join(ROOT, "tests", "test_abi.py"),
+                        os.path.join(ROOT, "tests", "test_plan_properties.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-4000:]
