@@ -14,7 +14,10 @@ Prints one JSON line (rank 0, N=1):
   value        decode steps (= tokens at batch 1) per second, wall clock
   roofline     stack_kernel: algorithmic bytes per launch (averaged over the
                timed steps) / its mean launch time from HIP events recorded
-               on the launch stream around the timed region, against 8 TB/s
+               on the launch stream around the timed region, against 8 TB/s;
+               traffic: HBM bytes per launch from the rocprofv3 counter
+               record in profiles/ (null unless that record was taken on the
+               same kernel sources, by sha256)
   status       the stack's device status word after the timed region and
                after the per-launch pass (0: every wait finished; the run
                exits with status 3 otherwise)
