@@ -10,7 +10,9 @@
 // are streamed with nontemporal 16-byte loads.
 //
 //   stack_kernel : gsi_stack, one persistent launch per stack.  Workgroups
-//                  take projection and output tickets wave by wave.  The
+//                  take projection and output tickets wave by wave (from
+//                  eight group counters; at the end of a wave, output
+//                  tickets from whichever group has most left).  The
 //                  workgroup that writes a call's last partial sums the
 //                  partials in a fixed order (bitwise deterministic; in two
 //                  levels of at most 64 rows for calls with many units),
@@ -768,8 +770,8 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
 // in one persistent launch.
 //
 // Waves run one after the other.  Within wave w there are projection units
-// (a fixed count, one ticket counter) and output units (a count known per
-// call once its gate is decided).  The workgroup that decides a call's gate
+// (a fixed count) and output units (a count known per call once its gate is
+// decided), both handed out as tickets (see take_ticket).  The workgroup that decides a call's gate
 // opens it by appending the call to the wave's open list: one 64-bit
 // fetch-add on the wave's open word (open calls << 40 | their output units)
 // returns both the call's slot and the output ticket of its first unit, so
@@ -779,8 +781,10 @@ __global__ void __launch_bounds__(kBlock) apply_kernel(KArgs a) {
 // cover its output ticket (finding the covering call by scanning the open
 // list 64 slots at a time with the lanes of wavefront 0), otherwise a
 // projection unit, and fetches the next ticket of the kind it used while the
-// unit runs.  No workgroup walks calls or polls a single call's word, which
-// keeps the control traffic off any one memory channel.
+// unit runs; once its group's output tickets are used up it takes them from
+// the group with the most left before it leaves the wave.  No workgroup
+// walks calls or polls a single call's word, which keeps the control traffic
+// off any one memory channel.
 //
 // A workgroup waits only (a) when its wave has no projection ticket left and
 // its output ticket is not covered yet: every gate it can wait for belongs
